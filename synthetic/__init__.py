@@ -1,0 +1,32 @@
+"""Seeded synthetic inputs for the BitDelta path.
+
+This module only draws inputs (base weights, fine-tuned weights, activations,
+variant ids).  It holds none of the method's arithmetic: no delta, sign,
+packing, scale or product is computed here.  Both the oracle-side tests and
+the GPU path take their inputs from it.
+
+Recipe (the page models a fine-tuning delta as Laplace(0, b); section
+"Matematiksel temel"):
+
+* W_base ~ N(0, sigma) drawn in float32, rounded to bf16 (RNE);
+* Delta ~ Laplace(0, b) by inverse CDF, -b*sgn(u)*ln(1-2|u|) with
+  u ~ U(-1/2, 1/2), in float32;
+* W_ft = bf16(float32(W_base) + Delta);
+* x ~ N(0, 1), rounded to bf16;
+* variant ids: truncated Zipf(1.1) over the variants, P(v) ~ (v+1)^-1.1,
+  drawn with numpy's Generator.choice.
+"""
+
+from .workloads import (  # noqa: F401
+    LAYER_70B,
+    WORKLOADS,
+    Workload,
+    bf16_bits,
+    draw_activations,
+    draw_base,
+    draw_finetuned,
+    generator,
+    laplace_scales,
+    small_pair,
+    zipf_ids,
+)

@@ -1,0 +1,125 @@
+"""Seeded generators and the five synthetic workloads.
+
+Shapes follow a 70B-class decoder layer (grouped-query QKV 8192->10240, O
+8192->8192, gate/up 8192->28672, down 28672->8192), the scale the page talks
+about (a 70B bf16 model of 140 GB with 14 fine-tuned variants; section
+"Matematiksel temel" and the figure in "Sunum mimarisi").
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+# (name, d_out, d_in) of the five linears of one 70B-shaped decoder layer.
+LAYER_70B = (
+    ("qkv", 10240, 8192),
+    ("o", 8192, 8192),
+    ("gate", 28672, 8192),
+    ("up", 28672, 8192),
+    ("down", 8192, 28672),
+)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    seed: int
+    matrices: tuple            # ((name, d_out, d_in), ...)
+    sigma: float               # std of W_base
+    b: float | None            # Laplace scale of the deltas (None: per variant)
+    alpha_mode: int            # 0 per matrix, 1 per row
+    tokens: tuple              # token counts M exercised
+    n_variants: int = 1
+    layers: int = 1
+    note: str = ""
+    extra: dict = field(default_factory=dict)
+
+
+WORKLOADS = {
+    "single_256x512": Workload(
+        "single_256x512", 0, (("w", 256, 512),), 0.02, 1e-3, 0, (4,),
+        note="one small linear, scalar alpha, M=4"),
+    "proj_4096": Workload(
+        "proj_4096", 2, (("w", 4096, 4096),), 0.02, 5e-4, 1, (1, 4, 16),
+        note="Llama-style 4096x4096 projection, per-row alpha, decode M=1,4,16"),
+    "layer70b_multi": Workload(
+        "layer70b_multi", 3, LAYER_70B, 0.015, None, 1, (32,), n_variants=14,
+        note="one 70B-shaped layer, 14 variants, b_v log-uniform [2e-4, 2e-3], "
+             "M=32 Zipf(1.1) variant mix"),
+    "layer70b_prefill": Workload(
+        "layer70b_prefill", 4, LAYER_70B, 0.015, 1e-3, 0, (2048,),
+        note="one 70B-shaped layer, one variant, per-matrix alpha, prefill M=2048"),
+    "stack70b_multi": Workload(
+        "stack70b_multi", 5, LAYER_70B, 0.015, 5e-4, 1, (64,), n_variants=14,
+        layers=80,
+        note="80 70B-shaped layers resident, 14 variants, M=64 Zipf(1.1) mix"),
+}
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """uint16 bit patterns of a bf16 tensor, as a host numpy array."""
+    if t.dtype != torch.bfloat16:
+        raise TypeError("expected a bfloat16 tensor")
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def draw_base(d_out: int, d_in: int, sigma: float, gen: torch.Generator,
+              device="cpu") -> torch.Tensor:
+    """W_base ~ N(0, sigma), bf16."""
+    w = torch.randn(d_out, d_in, generator=gen, device=device, dtype=torch.float32)
+    w.mul_(sigma)
+    return w.to(torch.bfloat16)
+
+
+def draw_finetuned(w_base: torch.Tensor, b: float, gen: torch.Generator) -> torch.Tensor:
+    """W_ft = bf16(float32(W_base) + Laplace(0, b)) with the Laplace draw taken
+    by inverse CDF from u ~ U(-1/2, 1/2)."""
+    u = torch.rand(w_base.shape, generator=gen, device=w_base.device,
+                   dtype=torch.float32)
+    u.sub_(0.5)
+    lap = torch.log1p(u.abs().mul_(-2.0)).mul_(-b).mul_(torch.sign(u))
+    del u
+    lap.add_(w_base.to(torch.float32))
+    return lap.to(torch.bfloat16)
+
+
+def draw_activations(m: int, d_in: int, gen: torch.Generator, device="cpu") -> torch.Tensor:
+    """x ~ N(0, 1), bf16, shape [m, d_in]."""
+    return torch.randn(m, d_in, generator=gen, device=device,
+                       dtype=torch.float32).to(torch.bfloat16)
+
+
+def laplace_scales(n_variants: int, seed: int, lo=2e-4, hi=2e-3) -> list:
+    """Per-variant Laplace scales b_v, log-uniform in [lo, hi]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return [float(v) for v in np.exp(rng.uniform(np.log(lo), np.log(hi), n_variants))]
+
+
+def zipf_ids(m: int, n_variants: int, seed: int, s: float = 1.1) -> np.ndarray:
+    """m variant ids from a Zipf(s) law truncated to n_variants ranks;
+    id 0 is the most popular."""
+    ranks = np.arange(1, n_variants + 1, dtype=np.float64)
+    p = ranks ** -s
+    p /= p.sum()
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.choice(n_variants, size=m, p=p).astype(np.int32)
+
+
+def small_pair(d_out: int, d_in: int, sigma: float, b: float, seed: int, device="cpu"):
+    """(W_base, W_ft) for one matrix from one seed, drawn in that order."""
+    g = _gen(seed, device)
+    w = draw_base(d_out, d_in, sigma, g, device)
+    return w, draw_finetuned(w, b, g)
+
+
+def generator(seed: int, device="cpu") -> torch.Generator:
+    return _gen(seed, device)
