@@ -1,0 +1,339 @@
+"""Benchmark of the BitDelta hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload proj_4096]
+
+A step is one pass of the whole path over one batch of synthetic input on the
+workload's matrices: compression of a fine-tuned matrix (delta, packed signs,
+alpha), the decode-shaped fused linear at each decode token count, a
+mixed-variant decode batch (Zipf(1.1) over 14 variants), and the prefill GEMM
+(M = 2048).  Inputs are resident in HBM before timing starts.  Weight copies
+rotate so that the working set of consecutive calls exceeds the 256 MB
+last-level cache several times: every call streams its weights from HBM.
+
+Each kernel range inside the timed steps is bracketed by HIP events on the
+stream the kernels run on, which gives per-kernel average durations; the
+whole K steps are bracketed by synchronisations for ms_per_step.  The line
+printed reports decode effective HBM GB/s (algorithmic bytes / kernel time)
+as `value`, the prefill TFLOP/s beside it, a roofline entry per kernel, and
+the CPU oracle timed on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synthetic as S  # noqa: E402
+import tenant_linear_layers_amd as T  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+MALL_BYTES = 256 * 2**20
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def sources_digest(names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "tenant_linear_layers_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "decode": ("decode.hip", "common.h", "internal.h"),
+    "multi": ("decode.hip", "common.h", "internal.h"),
+    "compress": ("compress.hip", "common.h", "scale_round.h"),
+    "prefill": ("prefill.hip", "common.h", "internal.h"),
+}
+
+
+def counter_traffic(kernel: str, workload: str):
+    """HBM bytes per launch measured by rocprofv3 counters, from the committed
+    summary for this kernel and workload, or None when there is none or the
+    kernel's sources changed since it was taken."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except (OSError, ValueError):
+        return None
+    if rec.get("sources_digest") != sources_digest(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+class Ranges:
+    """Per-name HIP-event timing of kernel ranges on the current stream."""
+
+    def __init__(self):
+        self.pending = []
+        self.total_ms = {}
+        self.count = {}
+
+    def run(self, name, fn):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pending.append((name, s, e))
+
+    def collect(self):
+        torch.cuda.synchronize()
+        for name, s, e in self.pending:
+            self.total_ms[name] = self.total_ms.get(name, 0.0) + s.elapsed_time(e)
+            self.count[name] = self.count.get(name, 0) + 1
+        self.pending = []
+
+    def avg_us(self, name):
+        return 1e3 * self.total_ms[name] / self.count[name]
+
+
+# ------------------------------------------------------------------ workload
+class ProjWorkload:
+    """The 4096x4096 projection: per-row alpha, decode M = 1, 4, 16, a
+    14-variant mixed decode batch of 16 tokens, prefill M = 2048."""
+
+    name = "proj_4096"
+    multi_m = 16
+    prefill_m = 2048
+    n_variants = 14
+
+    def __init__(self, dev):
+        wl = S.WORKLOADS["proj_4096"]
+        self.wl = wl
+        self.dev = dev
+        self.d_out = self.d_in = 4096
+        self.mode = wl.alpha_mode
+        self.decode_ms = wl.tokens
+        g = S.generator(wl.seed)
+        wb = S.draw_base(4096, 4096, wl.sigma, g)
+        wf = S.draw_finetuned(wb, wl.b, g)
+        xs = {m: S.draw_activations(m, 4096, g) for m in wl.tokens}
+        # 13 more variants of the same base for the mixed batch (b as the workload's)
+        more = [S.draw_finetuned(wb, wl.b, g) for _ in range(self.n_variants - 1)]
+        x_multi = S.draw_activations(self.multi_m, 4096, g)
+        x_prefill = S.draw_activations(self.prefill_m, 4096, g)
+        ids = S.zipf_ids(self.multi_m, self.n_variants, wl.seed)
+
+        per_copy = 4096 * 4096 * 2 + 4096 * 4096 // 8
+        self.R = max(4, math.ceil(4 * MALL_BYTES / per_copy))
+        wb_d, wf_d = wb.to(dev), wf.to(dev)
+        packed, alpha = T.compress(wf_d, wb_d, self.mode)
+        variants = [(packed, alpha)] + [T.compress(w.to(dev), wb_d, self.mode) for w in more]
+        self.bases = [wb_d] + [wb_d.clone() for _ in range(self.R - 1)]
+        self.fts = [wf_d] + [wf_d.clone() for _ in range(min(self.R, 16) - 1)]
+        self.vsets = [variants] + [[(p.clone(), a.clone()) for p, a in variants]
+                                   for _ in range(self.R - 1)]
+        self.xs = {m: x.to(dev) for m, x in xs.items()}
+        self.x_multi = x_multi.to(dev)
+        self.x_prefill = x_prefill.to(dev)
+        self.ids = torch.from_numpy(ids).to(dev)
+        self.distinct = int(len(set(ids.tolist())))
+        self.ys = {m: torch.empty(m, 4096, dtype=torch.bfloat16, device=dev) for m in wl.tokens}
+        self.y_multi = torch.empty(self.multi_m, 4096, dtype=torch.bfloat16, device=dev)
+        self.y_prefill = torch.empty(self.prefill_m, 4096, dtype=torch.bfloat16, device=dev)
+        self.c_out = [(torch.empty_like(packed), torch.empty_like(alpha)) for _ in range(2)]
+        self.host = dict(wb=wb, wf=wf, xs=xs, more=more, x_multi=x_multi, ids=ids)
+        self.k = 0
+
+    # algorithmic bytes / flops per launch
+    def decode_bytes(self, m):
+        n = self.d_out * self.d_in
+        alpha = 4 * (self.d_out if self.mode == 1 else 1)
+        return 2 * n + n // 8 + alpha + 2 * m * self.d_in + 2 * m * self.d_out
+
+    def multi_bytes(self):
+        n = self.d_out * self.d_in
+        alpha = 4 * (self.d_out if self.mode == 1 else 1)
+        return (2 * n + self.distinct * (n // 8 + alpha) + 2 * self.multi_m * self.d_in
+                + 2 * self.multi_m * self.d_out + 4 * self.multi_m)
+
+    def compress_bytes(self):
+        n = self.d_out * self.d_in
+        alpha = 4 * (self.d_out if self.mode == 1 else 1)
+        return 4 * n + n // 8 + alpha
+
+    def prefill_flops(self):
+        return 2 * self.prefill_m * self.d_out * self.d_in
+
+    def step(self, rg: Ranges):
+        R = self.R
+        k = self.k
+        self.k += 1
+        wb = self.bases[k % R]
+        wf = self.fts[k % len(self.fts)]
+        cp, ca = self.c_out[k % 2]
+        rg.run("compress", lambda: T.compress(wf, wb, self.mode, packed=cp, alpha=ca))
+        for j, m in enumerate(self.decode_ms):
+            r = (k + 1 + j) % R
+            p, a = self.vsets[r][0]
+            rg.run(f"decode_m{m}", lambda m=m, r=r, p=p, a=a:
+                   T.linear(self.xs[m], self.bases[r], p, a, self.mode, y=self.ys[m]))
+        r = (k + 5) % R
+        vs = self.vsets[r]
+        rg.run("multi", lambda: T.linear_multi(self.x_multi, self.ids, self.bases[r],
+                                               [p for p, _ in vs], [a for _, a in vs],
+                                               self.mode, y=self.y_multi))
+        r2 = (k + 7) % R
+        p, a = self.vsets[r2][0]
+        rg.run("prefill", lambda: T.linear(self.x_prefill, self.bases[r2], p, a, self.mode,
+                                           y=self.y_prefill))
+
+
+# ------------------------------------------------------------------ CPU oracle
+def cpu_baseline(w: ProjWorkload, budget_s: float):
+    """The oracle, as it stands, on a bounded sample of the same workload:
+    compression of the projection and the three decode products (all 4096 rows),
+    repeated while the time budget lasts.  Reported in the metric's unit."""
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        threads = 1
+    wb = S.bf16_bits(w.host["wb"])
+    wf = S.bf16_bits(w.host["wf"])
+    xs = {m: S.bf16_bits(x) for m, x in w.host["xs"].items()}
+    t0 = time.perf_counter()
+    packed, alpha = O.compress(wf, wb, w.mode)
+    t_comp = time.perf_counter() - t0
+    passes, t_dec, nbytes = 0, 0.0, 0
+    while True:
+        t0 = time.perf_counter()
+        for m in w.decode_ms:
+            O.linear(xs[m], wb, packed, alpha, w.mode)
+            nbytes += w.decode_bytes(m)
+        t_dec += time.perf_counter() - t0
+        passes += 1
+        if t_dec + t_comp > budget_s or passes >= 20:
+            break
+    return {
+        "value": round(nbytes / t_dec / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"oracle decode products M={list(w.decode_ms)} on the full 4096x4096 "
+                   f"projection, {passes} pass(es), {t_dec:.1f} s; oracle compression of the "
+                   f"same matrix {t_comp:.1f} s ({w.compress_bytes() / t_comp / 1e9:.3f} GB/s)"),
+        "host_cores_available": len(os.sched_getaffinity(0)),
+    }
+
+
+def roofline_entry(bound, achieved, peak, unit, traffic=None):
+    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="proj_4096", choices=["proj_4096"])
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the kernels shard by output rows, see DESIGN.md); run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T.lib()
+    print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
+    w = ProjWorkload(dev)
+    torch.cuda.synchronize()
+    print(f"[bench] rotation copies R={w.R}, distinct variants in the mixed batch "
+          f"D={w.distinct}", file=sys.stderr, flush=True)
+
+    warm = Ranges()
+    for _ in range(args.warmup):
+        w.step(warm)
+    warm.collect()
+
+    rg = Ranges()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        w.step(rg)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    rg.collect()
+    print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+
+    dec_bytes = sum(w.decode_bytes(m) for m in w.decode_ms)
+    dec_us = sum(rg.avg_us(f"decode_m{m}") for m in w.decode_ms)
+    dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
+    pre_us = rg.avg_us("prefill")
+    pre_tflops = w.prefill_flops() / (pre_us * 1e-6) / 1e12
+    comp_us = rg.avg_us("compress")
+    multi_us = rg.avg_us("multi")
+
+    rooflines = {
+        "decode": roofline_entry("hbm", dec_gbs, HBM_PEAK_GBS, "GB/s",
+                                 counter_traffic("decode", w.name)),
+        "compress": roofline_entry("hbm", w.compress_bytes() / (comp_us * 1e-6) / 1e9,
+                                   HBM_PEAK_GBS, "GB/s", counter_traffic("compress", w.name)),
+        "multi": roofline_entry("hbm", w.multi_bytes() / (multi_us * 1e-6) / 1e9,
+                                HBM_PEAK_GBS, "GB/s", counter_traffic("multi", w.name)),
+        "prefill": roofline_entry("mfma", pre_tflops, BF16_PEAK_TFLOPS, "TFLOP/s",
+                                  counter_traffic("prefill", w.name)),
+    }
+    kernel_us = {name: round(rg.avg_us(name), 3) for name in rg.total_ms}
+
+    cpu = None
+    if args.cpu_budget > 0:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, args.cpu_budget)
+
+    out = {
+        "metric": "bitdelta_linear effective HBM GB/s (decode) + bf16 TFLOP/s (prefill), 1 GPU",
+        "value": round(dec_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1e3 * wall / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "proj_4096: Llama-style 4096x4096 projection, bf16 W_base~N(0,0.02), "
+                        "Laplace(0,5e-4) delta, per-row alpha; step = compress W_ft + decode "
+                        "M=1,4,16 + 14-variant Zipf(1.1) decode M=16 + prefill M=2048",
+            "d_out": 4096, "d_in": 4096, "decode_tokens": list(w.decode_ms),
+            "multi_tokens": w.multi_m, "multi_variants": w.n_variants,
+            "multi_distinct_variants": w.distinct, "prefill_tokens": w.prefill_m,
+            "alpha_mode": "per_row", "rotation_copies": w.R,
+        },
+        "prefill_tflops": round(pre_tflops, 2),
+        "roofline": rooflines["decode"],
+        "roofline_by_kernel": rooflines,
+        "kernel_avg_us": kernel_us,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,176 @@
+/*
+ * bitdelta.h - C ABI of libbitdelta, the MI355X (gfx950) BitDelta path.
+ *
+ * Method: the page "BitDelta: Tek bir GPU kümesinden 14 Zen modeli sunmak"
+ * (hanzo.blog, 2026-02-28; Spanish translation on hanzo-blog.hanzo.app).
+ * A fine-tuned weight W_ft is served as the shared base W_base plus a one-bit
+ * code of its task vector: W_ft ~ W_base + alpha * sign(W_ft - W_base), with
+ * alpha = mean|W_ft - W_base| (section "Matematiksel temel"), and the linear
+ * layer y = x * (W_base + alpha * sign(Delta))^T is computed in one kernel
+ * pass without writing the effective weight to memory (section "Sunum
+ * mimarisi", the conceptual fused kernel).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers marked "device" are HIP device pointers; the caller allocates
+ *   and owns every buffer.  The library allocates no memory and keeps no
+ *   state between calls beyond cached device attributes; calls on different
+ *   streams may run concurrently.
+ * - bf16 values are passed as uint16_t bit patterns (the top half of an IEEE
+ *   float32).
+ * - Matrices are row-major: W [d_out, d_in], x [M, d_in], y [M, d_out].
+ *   The page's activations [batch, seq, d_in] are passed flattened to
+ *   [batch*seq, d_in].
+ * - Packed signs: uint64 [d_out, d_in/64].  Element c of row r is bit
+ *   (c mod 64) of word (c div 64) of row r, least significant bit first; bit
+ *   value 1 means sign +1; sign(0) = +1.  On a little-endian machine the same
+ *   bytes read as uint8/int8 [d_out, d_in/8], 8 signs per byte along the
+ *   input dimension (section "Altyapı ayrıntıları": a 4096x4096 weight packs
+ *   to 4096x512 bytes).  Exactly d_out*d_in/8 bytes.
+ * - alpha: float32, one value (BITDELTA_ALPHA_PER_MATRIX) or d_out values
+ *   (BITDELTA_ALPHA_PER_ROW, one per output dimension as the page stores it).
+ * - stream: a hipStream_t passed as void*; NULL means the null stream.  All
+ *   GPU work is enqueued on it asynchronously.  The returned status reports
+ *   argument checks (done on the host before anything is enqueued) and
+ *   launch errors only.
+ * - Shapes: d_out >= 1, d_in >= 64 and d_in % 64 == 0, M >= 1.  d_out,
+ *   d_in and M must each fit in a signed 32-bit int, and d_out*d_in below
+ *   2^40.
+ * - Alignment: x, w_ft, w_base, packed and y must be 16-byte aligned.
+ * - Outputs must not overlap inputs (checked: BITDELTA_ERR_OVERLAP).
+ * - Data errors are encoded in values, never reported by status: a scope
+ *   (row or matrix) whose delta is non-finite or has |delta| >= 2^15 gets
+ *   alpha = NaN (bits 0x7FC00000); NaN alpha propagates to the outputs.
+ */
+#ifndef BITDELTA_H
+#define BITDELTA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define BITDELTA_OK 0
+#define BITDELTA_ERR_NULL 1      /* a required pointer is NULL */
+#define BITDELTA_ERR_SHAPE 2     /* M, d_out or d_in out of range, d_in % 64 != 0 */
+#define BITDELTA_ERR_ALIGN 3     /* a buffer is not 16-byte aligned */
+#define BITDELTA_ERR_MODE 4      /* alpha_mode is not 0 or 1 */
+#define BITDELTA_ERR_VARIANTS 5  /* n_variants outside [1, BITDELTA_MAX_VARIANTS] */
+#define BITDELTA_ERR_WORKSPACE 6 /* workspace missing or smaller than required */
+#define BITDELTA_ERR_HIP 7       /* the HIP runtime reported an error at launch */
+#define BITDELTA_ERR_DEVICE 8    /* the current device is not a gfx950 GPU */
+#define BITDELTA_ERR_OVERLAP 9   /* an output buffer overlaps an input buffer */
+
+/* alpha_mode values. */
+#define BITDELTA_ALPHA_PER_MATRIX 0
+#define BITDELTA_ALPHA_PER_ROW 1
+
+/* Most variants one bitdelta_linear_multi call can address (their pointers
+ * travel in the kernel arguments). */
+#define BITDELTA_MAX_VARIANTS 64
+
+/*
+ * bitdelta_compress_workspace_size
+ * Bytes of device workspace bitdelta_compress needs for this shape and mode:
+ * 16 bytes per row in per-matrix mode (exact integer partial sums of the
+ * scale, one per row), 0 in per-row mode.  Returns 0 for invalid arguments.
+ */
+size_t bitdelta_compress_workspace_size(int64_t d_out, int64_t d_in, int alpha_mode);
+
+/*
+ * bitdelta_compress - compress one fine-tuned weight matrix against its base.
+ *
+ * Computes Delta = W_ft - W_base (section "Matematiksel temel", Delta
+ * equation) per element as one float32 subtraction of the widened bf16
+ * values (round to nearest even, subnormals kept), writes sign(Delta) packed
+ * as described above (section "Altyapı ayrıntıları"), and writes
+ * alpha = mean|Delta| over each scope (section "Matematiksel temel", alpha
+ * equation).  The mean is defined exactly: S = sum of floor(|d| * 2^48) as an
+ * integer, alpha = S / (n * 2^48) rounded once to float32 (nearest, ties to
+ * even), n the scope's element count.  The result does not depend on the
+ * order of summation, so it is bit-reproducible.
+ *
+ *   w_ft, w_base  device, bf16 [d_out, d_in], read only
+ *   packed        device, uint64 [d_out, d_in/64], written
+ *   alpha         device, float32 [1] (per matrix) or [d_out] (per row), written
+ *   workspace     device, >= bitdelta_compress_workspace_size(...) bytes, or
+ *                 NULL when that size is 0; contents are scratch
+ *   stream        hipStream_t or NULL
+ * Returns BITDELTA_OK or an error status; nothing is enqueued on error.
+ */
+int bitdelta_compress(const uint16_t* w_ft, const uint16_t* w_base, int64_t d_out,
+                      int64_t d_in, int alpha_mode, uint64_t* packed, float* alpha,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * bitdelta_linear - fused BitDelta linear for one variant:
+ *   y[m, o] = sum_i x[m, i] * (W_base[o, i] + alpha_o * s[o, i]),   no bias
+ * (section "Sunum mimarisi", the conceptual fused kernel; s from the packed
+ * signs, alpha_o = alpha[o] per row or alpha[0] per matrix).  The effective
+ * weight is never written to memory.  Accumulation is in float32, y is
+ * rounded to bf16 (nearest even).  M <= 64 runs the decode-shaped kernel
+ * (base and sign products on the matrix cores, one pass over W_base and the
+ * packed signs); larger M runs the prefill GEMM, which rebuilds bf16 tiles of
+ * W_eff in LDS.
+ *
+ *   x       device, bf16 [M, d_in]
+ *   w_base  device, bf16 [d_out, d_in]
+ *   packed  device, uint64 [d_out, d_in/64]
+ *   alpha   device, float32 [1] or [d_out]
+ *   y       device, bf16 [M, d_out], written
+ * Returns BITDELTA_OK or an error status; nothing is enqueued on error.
+ */
+int bitdelta_linear(const uint16_t* x, int64_t M, const uint16_t* w_base,
+                    const uint64_t* packed, const float* alpha, int alpha_mode,
+                    int64_t d_out, int64_t d_in, uint16_t* y, void* stream);
+
+/*
+ * bitdelta_linear_multi - one token batch that mixes variants of one base
+ * (section "Sunum mimarisi": many variants' deltas served over one shared,
+ * read-only base; section "Altyapı ayrıntıları": per-variant routing).
+ * Token m uses variant v = variant_ids[m]:
+ *   y[m] = x[m] * W_base^T + alpha_v (.) (x[m] * S_v^T)
+ * and v = -1 selects the base model alone.  W_base is streamed once for all
+ * tokens and each distinct variant's packed signs once.  An id outside
+ * [-1, n_variants) makes that token's output row NaN (nothing out of bounds
+ * is read).  Tokens are processed in groups of 64 (one pass over the weights
+ * per group).
+ *
+ *   x            device, bf16 [M, d_in]
+ *   variant_ids  device, int32 [M]
+ *   w_base       device, bf16 [d_out, d_in]
+ *   n_variants   1 .. BITDELTA_MAX_VARIANTS
+ *   packed       HOST array of n_variants device pointers, each uint64
+ *                [d_out, d_in/64], none NULL
+ *   alpha        HOST array of n_variants device pointers, float32 [1] or
+ *                [d_out] each according to alpha_mode, none NULL
+ *   y            device, bf16 [M, d_out], written
+ * The host arrays are read during the call only.
+ * Returns BITDELTA_OK or an error status; nothing is enqueued on error.
+ */
+int bitdelta_linear_multi(const uint16_t* x, int64_t M, const int32_t* variant_ids,
+                          const uint16_t* w_base, int32_t n_variants,
+                          const uint64_t* const* packed, const float* const* alpha,
+                          int alpha_mode, int64_t d_out, int64_t d_in, uint16_t* y,
+                          void* stream);
+
+/* Human-readable text of a status code (static storage, never NULL). */
+const char* bitdelta_status_string(int status);
+
+/*
+ * bitdelta_ratio_to_f32_bits - host copy of the scale's final rounding step:
+ * float32 bits of S / (n * 2^48) rounded to nearest, ties to even, where
+ * S = s_hi * 2^64 + s_lo.  The device kernels use the same routine; it is
+ * exported so the rounding can be checked without a GPU.  Returns 0 for
+ * S = 0 and 0x7FC00000 for n = 0.
+ */
+uint32_t bitdelta_ratio_to_f32_bits(uint64_t s_hi, uint64_t s_lo, uint64_t n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BITDELTA_H */

@@ -25,8 +25,12 @@ from .workloads import (  # noqa: F401
     draw_activations,
     draw_base,
     draw_finetuned,
+    draw_layer_bases,
+    draw_layer_inputs,
+    iter_finetuned,
     generator,
     laplace_scales,
     small_pair,
+    variant_scales,
     zipf_ids,
 )

@@ -123,3 +123,37 @@ def small_pair(d_out: int, d_in: int, sigma: float, b: float, seed: int, device=
 
 def generator(seed: int, device="cpu") -> torch.Generator:
     return _gen(seed, device)
+
+
+# ----------------------------------------------------------------- layers
+def variant_scales(wl: Workload) -> list:
+    """Laplace scale of each variant: the workload's fixed b, or per-variant
+    log-uniform draws in [2e-4, 2e-3] seeded by the workload seed."""
+    if wl.b is not None:
+        return [wl.b] * wl.n_variants
+    return laplace_scales(wl.n_variants, wl.seed)
+
+
+def draw_layer_bases(wl: Workload, gen: torch.Generator, device) -> list:
+    """W_base of each matrix of one layer, in matrix order."""
+    return [draw_base(d_out, d_in, wl.sigma, gen, device) for _, d_out, d_in in wl.matrices]
+
+
+def iter_finetuned(bases: list, scales: list, gen: torch.Generator):
+    """Yield (variant, matrix index, W_ft), variant-major, one temporary at a
+    time, so the caller can compress and drop each before the next."""
+    for v, b in enumerate(scales):
+        for i, w in enumerate(bases):
+            yield v, i, draw_finetuned(w, b, gen)
+
+
+def draw_layer_inputs(wl: Workload, m: int, gen: torch.Generator, device) -> list:
+    """One activation tensor per matrix of the layer.  QKV, gate and up read
+    the same [m, 8192] input, O its own [m, 8192], down a [m, 28672] one."""
+    names = [name for name, _, _ in wl.matrices]
+    if names == [n for n, _, _ in LAYER_70B]:
+        x_in = draw_activations(m, 8192, gen, device)
+        x_o = draw_activations(m, 8192, gen, device)
+        x_down = draw_activations(m, 28672, gen, device)
+        return [x_in, x_o, x_in, x_in, x_down]
+    return [draw_activations(m, d_in, gen, device) for _, _, d_in in wl.matrices]

@@ -1,0 +1,22 @@
+"""BitDelta multi-tenant linear layer for MI355X (gfx950).
+
+The path lives in libbitdelta.so (HIP kernels behind the C ABI of
+include/bitdelta.h); this package is the build script and a thin ctypes
+binding with the same names.
+"""
+
+from .bitdelta import (  # noqa: F401
+    ALPHA_PER_MATRIX,
+    ALPHA_PER_ROW,
+    EXPORTS,
+    LIB_PATH,
+    MAX_VARIANTS,
+    BitDeltaError,
+    compress,
+    compress_workspace_size,
+    lib,
+    linear,
+    linear_multi,
+    ratio_to_f32_bits,
+    status_string,
+)

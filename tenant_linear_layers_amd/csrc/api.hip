@@ -1,0 +1,206 @@
+// C ABI of libbitdelta: argument checks, device check and kernel dispatch.
+// Every check runs on the host before anything is enqueued; see
+// include/bitdelta.h for the contract of each entry point.
+#include <atomic>
+#include <cstring>
+
+#include "bitdelta.h"
+#include "common.h"
+#include "internal.h"
+#include "scale_round.h"
+
+#define BD_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int64_t kInt32Max = 2147483647;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+bool shape_ok(int64_t d_out, int64_t d_in) {
+  return d_out >= 1 && d_in >= 64 && d_in % 64 == 0 && d_out <= kInt32Max && d_in <= kInt32Max &&
+         d_out * d_in < kMaxElems;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+// 0 unknown, 1 gfx950, 2 other.  Cached per device index.
+std::atomic<int> g_arch_state[64];
+
+int check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return BITDELTA_ERR_HIP;
+  if (dev < 0 || dev >= 64) return BITDELTA_ERR_DEVICE;
+  int st = g_arch_state[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return BITDELTA_ERR_HIP;
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_state[dev].store(st, std::memory_order_relaxed);
+  }
+  return st == 1 ? BITDELTA_OK : BITDELTA_ERR_DEVICE;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? BITDELTA_OK : BITDELTA_ERR_HIP; }
+
+}  // namespace
+
+BD_EXPORT const char* bitdelta_status_string(int status) {
+  switch (status) {
+    case BITDELTA_OK: return "ok";
+    case BITDELTA_ERR_NULL: return "a required pointer is NULL";
+    case BITDELTA_ERR_SHAPE:
+      return "shape out of range (need M >= 1, d_out >= 1, d_in >= 64, d_in % 64 == 0, "
+             "each below 2^31, d_out*d_in below 2^40)";
+    case BITDELTA_ERR_ALIGN: return "a buffer is not 16-byte aligned";
+    case BITDELTA_ERR_MODE: return "alpha_mode must be 0 (per matrix) or 1 (per row)";
+    case BITDELTA_ERR_VARIANTS: return "n_variants must be in [1, 64]";
+    case BITDELTA_ERR_WORKSPACE: return "workspace missing or too small";
+    case BITDELTA_ERR_HIP: return "HIP runtime error";
+    case BITDELTA_ERR_DEVICE: return "current device is not a gfx950 GPU";
+    case BITDELTA_ERR_OVERLAP: return "an output buffer overlaps an input buffer";
+    default: return "unknown status";
+  }
+}
+
+BD_EXPORT uint32_t bitdelta_ratio_to_f32_bits(uint64_t s_hi, uint64_t s_lo, uint64_t n) {
+  return bd::ratio_to_f32_bits(s_hi, s_lo, n);
+}
+
+BD_EXPORT size_t bitdelta_compress_workspace_size(int64_t d_out, int64_t d_in, int alpha_mode) {
+  if (!shape_ok(d_out, d_in)) return 0;
+  if (alpha_mode == BITDELTA_ALPHA_PER_MATRIX) return (size_t)d_out * 16u;
+  return 0;
+}
+
+BD_EXPORT int bitdelta_compress(const uint16_t* w_ft, const uint16_t* w_base, int64_t d_out,
+                                int64_t d_in, int alpha_mode, uint64_t* packed, float* alpha,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!w_ft || !w_base || !packed || !alpha) return BITDELTA_ERR_NULL;
+  if (!shape_ok(d_out, d_in)) return BITDELTA_ERR_SHAPE;
+  if (alpha_mode != BITDELTA_ALPHA_PER_MATRIX && alpha_mode != BITDELTA_ALPHA_PER_ROW)
+    return BITDELTA_ERR_MODE;
+  if (!aligned16(w_ft) || !aligned16(w_base) || !aligned16(packed) || !aligned16(alpha))
+    return BITDELTA_ERR_ALIGN;
+  const size_t need = bitdelta_compress_workspace_size(d_out, d_in, alpha_mode);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return BITDELTA_ERR_WORKSPACE;
+  if (need > 0 && !aligned16(workspace)) return BITDELTA_ERR_ALIGN;
+  const size_t wbytes = (size_t)d_out * (size_t)d_in * 2u;
+  const size_t pbytes = wbytes / 16u;
+  const size_t abytes = alpha_mode == BITDELTA_ALPHA_PER_ROW ? (size_t)d_out * 4u : 4u;
+  if (overlap(packed, pbytes, w_ft, wbytes) || overlap(packed, pbytes, w_base, wbytes) ||
+      overlap(alpha, abytes, w_ft, wbytes) || overlap(alpha, abytes, w_base, wbytes) ||
+      overlap(alpha, abytes, packed, pbytes) ||
+      (need > 0 && (overlap(workspace, need, w_ft, wbytes) ||
+                    overlap(workspace, need, w_base, wbytes) ||
+                    overlap(workspace, need, packed, pbytes) ||
+                    overlap(workspace, need, alpha, abytes))))
+    return BITDELTA_ERR_OVERLAP;
+  const int dev = check_device();
+  if (dev != BITDELTA_OK) return dev;
+  return status_of(bd::launch_compress(w_ft, w_base, (int)d_out, (int)d_in,
+                                       alpha_mode == BITDELTA_ALPHA_PER_ROW, packed, alpha,
+                                       static_cast<uint64_t*>(workspace),
+                                       static_cast<hipStream_t>(stream)));
+}
+
+BD_EXPORT int bitdelta_linear(const uint16_t* x, int64_t M, const uint16_t* w_base,
+                              const uint64_t* packed, const float* alpha, int alpha_mode,
+                              int64_t d_out, int64_t d_in, uint16_t* y, void* stream) {
+  if (!x || !w_base || !packed || !alpha || !y) return BITDELTA_ERR_NULL;
+  if (!shape_ok(d_out, d_in) || M < 1 || M > kInt32Max || M * d_in >= kMaxElems ||
+      M * d_out >= kMaxElems)
+    return BITDELTA_ERR_SHAPE;
+  if (alpha_mode != BITDELTA_ALPHA_PER_MATRIX && alpha_mode != BITDELTA_ALPHA_PER_ROW)
+    return BITDELTA_ERR_MODE;
+  if (!aligned16(x) || !aligned16(w_base) || !aligned16(packed) || !aligned16(y))
+    return BITDELTA_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(alpha) & 3u) return BITDELTA_ERR_ALIGN;
+  const size_t ybytes = (size_t)M * (size_t)d_out * 2u;
+  const size_t wbytes = (size_t)d_out * (size_t)d_in * 2u;
+  const size_t abytes = alpha_mode == BITDELTA_ALPHA_PER_ROW ? (size_t)d_out * 4u : 4u;
+  if (overlap(y, ybytes, x, (size_t)M * (size_t)d_in * 2u) || overlap(y, ybytes, w_base, wbytes) ||
+      overlap(y, ybytes, packed, wbytes / 16u) || overlap(y, ybytes, alpha, abytes))
+    return BITDELTA_ERR_OVERLAP;
+  const int dev = check_device();
+  if (dev != BITDELTA_OK) return dev;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M <= bd::kMaxSkinnyTokens) {
+    bd::SkinnyArgs a;
+    std::memset(&a, 0, sizeof(a));
+    a.x = x;
+    a.ids = nullptr;
+    a.w = w_base;
+    a.y = y;
+    a.M = (int)M;
+    a.d_out = (int)d_out;
+    a.d_in = (int)d_in;
+    a.per_row = alpha_mode == BITDELTA_ALPHA_PER_ROW;
+    a.n_variants = 1;
+    a.packed[0] = reinterpret_cast<const uint32_t*>(packed);
+    a.alpha[0] = alpha;
+    return status_of(bd::launch_linear_skinny(a, s));
+  }
+  return status_of(bd::launch_linear_prefill(
+      x, (int)M, w_base, reinterpret_cast<const uint8_t*>(packed), alpha,
+      alpha_mode == BITDELTA_ALPHA_PER_ROW, (int)d_out, (int)d_in, y, s));
+}
+
+BD_EXPORT int bitdelta_linear_multi(const uint16_t* x, int64_t M, const int32_t* variant_ids,
+                                    const uint16_t* w_base, int32_t n_variants,
+                                    const uint64_t* const* packed, const float* const* alpha,
+                                    int alpha_mode, int64_t d_out, int64_t d_in, uint16_t* y,
+                                    void* stream) {
+  if (!x || !variant_ids || !w_base || !packed || !alpha || !y) return BITDELTA_ERR_NULL;
+  if (!shape_ok(d_out, d_in) || M < 1 || M > kInt32Max || M * d_in >= kMaxElems ||
+      M * d_out >= kMaxElems)
+    return BITDELTA_ERR_SHAPE;
+  if (alpha_mode != BITDELTA_ALPHA_PER_MATRIX && alpha_mode != BITDELTA_ALPHA_PER_ROW)
+    return BITDELTA_ERR_MODE;
+  if (n_variants < 1 || n_variants > BITDELTA_MAX_VARIANTS) return BITDELTA_ERR_VARIANTS;
+  for (int v = 0; v < n_variants; ++v)
+    if (!packed[v] || !alpha[v]) return BITDELTA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w_base) || !aligned16(y) ||
+      (reinterpret_cast<uintptr_t>(variant_ids) & 3u))
+    return BITDELTA_ERR_ALIGN;
+  for (int v = 0; v < n_variants; ++v)
+    if (!aligned16(packed[v]) || (reinterpret_cast<uintptr_t>(alpha[v]) & 3u))
+      return BITDELTA_ERR_ALIGN;
+  const size_t ybytes = (size_t)M * (size_t)d_out * 2u;
+  const size_t wbytes = (size_t)d_out * (size_t)d_in * 2u;
+  const size_t abytes = alpha_mode == BITDELTA_ALPHA_PER_ROW ? (size_t)d_out * 4u : 4u;
+  if (overlap(y, ybytes, x, (size_t)M * (size_t)d_in * 2u) || overlap(y, ybytes, w_base, wbytes) ||
+      overlap(y, ybytes, variant_ids, (size_t)M * 4u))
+    return BITDELTA_ERR_OVERLAP;
+  for (int v = 0; v < n_variants; ++v)
+    if (overlap(y, ybytes, packed[v], wbytes / 16u) || overlap(y, ybytes, alpha[v], abytes))
+      return BITDELTA_ERR_OVERLAP;
+  const int dev = check_device();
+  if (dev != BITDELTA_OK) return dev;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  bd::SkinnyArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.w = w_base;
+  a.d_out = (int)d_out;
+  a.d_in = (int)d_in;
+  a.per_row = alpha_mode == BITDELTA_ALPHA_PER_ROW;
+  a.n_variants = n_variants;
+  for (int v = 0; v < n_variants; ++v) {
+    a.packed[v] = reinterpret_cast<const uint32_t*>(packed[v]);
+    a.alpha[v] = alpha[v];
+  }
+  for (int64_t m0 = 0; m0 < M; m0 += bd::kMaxSkinnyTokens) {
+    const int mc = (int)((M - m0) < bd::kMaxSkinnyTokens ? (M - m0) : bd::kMaxSkinnyTokens);
+    a.x = x + m0 * d_in;
+    a.ids = variant_ids + m0;
+    a.y = y + m0 * d_out;
+    a.M = mc;
+    const int st = status_of(bd::launch_linear_multi(a, s));
+    if (st != BITDELTA_OK) return st;
+  }
+  return BITDELTA_OK;
+}

@@ -1,0 +1,48 @@
+// Shared device helpers of libbitdelta (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bd {
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
+typedef uint32_t u32x4 __attribute__((__vector_size__(4 * sizeof(uint32_t))));
+
+constexpr int kWave = 64;
+
+// Four dwords reinterpreted as eight bf16 MFMA operands.
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// bf16 bit pattern of a float, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Two floats to packed bf16 (lo in bits 0..15), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+// Global loads that bypass nothing special but keep the 128-bit width explicit.
+__device__ __forceinline__ u32x4 ld128(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+__device__ __forceinline__ uint32_t ld32(const void* p) {
+  return *reinterpret_cast<const uint32_t*>(p);
+}
+
+}  // namespace bd

@@ -1,0 +1,185 @@
+// BitDelta compression on gfx950: Delta = W_ft - W_base, packed sign(Delta)
+// and alpha = mean|Delta|, in one HBM-streaming pass.
+//
+// Page "BitDelta: Tek bir GPU kümesinden 14 Zen modeli sunmak": section
+// "Matematiksel temel" (Delta, the sign code and the alpha equation) and
+// section "Altyapı ayrıntıları" (signs stored 8 per byte along the input
+// dimension, alpha as float32).
+//
+// One wave per row.  Lane k of a wave reads 16 bytes of each input per
+// 512-element chunk (elements 8k..8k+7), so every wave-wide load is a
+// contiguous 1 KiB.  The sign of element 8k+j is taken with one wave64
+// ballot per j; the eight 64-bit ballots are turned into the eight packed
+// words of the chunk by lanes 0..7, each doing one 8x8 bit transpose.
+// The scale is summed exactly in integers (floor(|d| * 2^48) split into two
+// 32-bit limbs), so the result does not depend on the order of summation.
+#include "common.h"
+#include "internal.h"
+#include "scale_round.h"
+
+#pragma clang fp contract(off)
+
+namespace bd {
+namespace {
+
+constexpr int kRowsPerBlock = 4;  // one wave per row, 256 threads
+
+// Transpose an 8x8 bit matrix held as eight bytes (byte r = row r, bit c =
+// column c): the result holds bit r of byte c = input bit c of byte r.
+__device__ __forceinline__ uint64_t transpose8x8(uint64_t x) {
+  uint64_t t;
+  t = (x ^ (x >> 7)) & 0x00AA00AA00AA00AAull;
+  x = x ^ t ^ (t << 7);
+  t = (x ^ (x >> 14)) & 0x0000CCCC0000CCCCull;
+  x = x ^ t ^ (t << 14);
+  t = (x ^ (x >> 28)) & 0x00000000F0F0F0F0ull;
+  x = x ^ t ^ (t << 28);
+  return x;
+}
+
+__device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// Per-row pass.  kPerRow: write alpha[row] directly; otherwise write the
+// row's two integer limbs to partial[2*row .. 2*row+1] (limb hi = sum of
+// floor(|d|*2^16), limb lo = sum of the next 32 fraction bits; a row with a
+// bad delta gets hi = ~0).
+template <bool kPerRow>
+__global__ __launch_bounds__(kRowsPerBlock * kWave) void compress_rows_kernel(
+    const uint16_t* __restrict__ w_ft, const uint16_t* __restrict__ w_base, int d_out, int d_in,
+    uint64_t* __restrict__ packed, float* __restrict__ alpha, uint64_t* __restrict__ partial) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= d_out) return;  // whole wave leaves together
+
+  const uint16_t* a_row = w_ft + (size_t)row * d_in;
+  const uint16_t* b_row = w_base + (size_t)row * d_in;
+  const int n_words = d_in >> 6;
+  uint64_t* p_row = packed + (size_t)row * n_words;
+
+  uint64_t acc_hi = 0, acc_lo = 0;
+  uint32_t bad = 0;
+  const int n_chunks = (d_in + 511) >> 9;
+
+  for (int c = 0; c < n_chunks; ++c) {
+    const int e0 = (c << 9) + (lane << 3);
+    // d_in is a multiple of 64, so the active lanes of the last chunk cover
+    // whole 64-element words.
+    const bool active = e0 < d_in;
+    u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
+    if (active) {
+      va = ld128(a_row + e0);
+      vb = ld128(b_row + e0);
+    }
+    uint64_t ball[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t ua = (j & 1) ? (va[j >> 1] & 0xFFFF0000u) : (va[j >> 1] << 16);
+      const uint32_t ub = (j & 1) ? (vb[j >> 1] & 0xFFFF0000u) : (vb[j >> 1] << 16);
+      const float d = __uint_as_float(ua) - __uint_as_float(ub);
+      // sign bit 1 <=> +1 <=> not (d < 0): +0, -0 and NaN give +1.
+      ball[j] = __builtin_amdgcn_ballot_w64(!(d < 0.0f));
+      // q = floor(|d| * 2^48) = hi * 2^32 + lo with hi = floor(|d| * 2^16)
+      // and lo = floor(frac(|d| * 2^16) * 2^32); every step is exact.
+      float ad = __builtin_fabsf(d) * 65536.0f;
+      const bool ok = ad < 2147483648.0f;  // false for NaN, inf, |d| >= 2^15
+      bad |= ok ? 0u : 1u;
+      ad = ok ? ad : 0.0f;
+      const uint32_t hi = (uint32_t)ad;
+      const float fr = ad - (float)hi;
+      const uint32_t lo = (uint32_t)(fr * 4294967296.0f);
+      acc_hi += active ? hi : 0u;
+      acc_lo += active ? lo : 0u;
+    }
+    if (lane < 8) {
+      // word `lane` of this chunk: bit 8i+j comes from ballot j, bit 8*lane+i.
+      uint64_t x = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x |= ((ball[j] >> (lane << 3)) & 0xFFull) << (j << 3);
+      const int w = (c << 3) + lane;
+      if (w < n_words) p_row[w] = transpose8x8(x);
+    }
+  }
+
+  acc_hi = wave_sum_u64(acc_hi);
+  acc_lo = wave_sum_u64(acc_lo);
+  const bool row_bad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
+  if (lane == 0) {
+    if (kPerRow) {
+      // S = acc_hi * 2^32 + acc_lo as a 128-bit value.
+      const uint64_t lo = (acc_hi << 32) + acc_lo;
+      const uint64_t hi = (acc_hi >> 32) + (lo < acc_lo ? 1u : 0u);
+      const uint32_t bits = row_bad ? 0x7FC00000u : ratio_to_f32_bits(hi, lo, (uint64_t)d_in);
+      alpha[row] = __uint_as_float(bits);
+    } else {
+      partial[2 * (size_t)row] = row_bad ? ~0ull : acc_hi;
+      partial[2 * (size_t)row + 1] = acc_lo;
+    }
+  }
+}
+
+// Per-matrix scale: sum the per-row limbs with 128-bit integers (exact and
+// order independent) and round once.
+constexpr int kFinalizeThreads = 256;
+
+__global__ __launch_bounds__(kFinalizeThreads) void compress_finalize_kernel(
+    const uint64_t* __restrict__ partial, int d_out, uint64_t n, float* __restrict__ alpha) {
+  __shared__ unsigned __int128 s_hi[kFinalizeThreads];
+  __shared__ unsigned __int128 s_lo[kFinalizeThreads];
+  __shared__ uint32_t s_bad[kFinalizeThreads];
+  unsigned __int128 hi = 0, lo = 0;
+  uint32_t bad = 0;
+  for (int r = threadIdx.x; r < d_out; r += kFinalizeThreads) {
+    const uint64_t h = partial[2 * (size_t)r];
+    if (h == ~0ull) {
+      bad = 1;
+    } else {
+      hi += h;
+    }
+    lo += partial[2 * (size_t)r + 1];
+  }
+  s_hi[threadIdx.x] = hi;
+  s_lo[threadIdx.x] = lo;
+  s_bad[threadIdx.x] = bad;
+  __syncthreads();
+  for (int step = kFinalizeThreads / 2; step > 0; step >>= 1) {
+    if ((int)threadIdx.x < step) {
+      s_hi[threadIdx.x] += s_hi[threadIdx.x + step];
+      s_lo[threadIdx.x] += s_lo[threadIdx.x + step];
+      s_bad[threadIdx.x] |= s_bad[threadIdx.x + step];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const unsigned __int128 s = (s_hi[0] << 32) + s_lo[0];
+    const uint32_t bits =
+        s_bad[0] ? 0x7FC00000u : ratio_to_f32_bits((uint64_t)(s >> 64), (uint64_t)s, n);
+    alpha[0] = __uint_as_float(bits);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_compress(const uint16_t* w_ft, const uint16_t* w_base, int d_out, int d_in,
+                           int per_row, uint64_t* packed, float* alpha, uint64_t* partial,
+                           hipStream_t stream) {
+  const dim3 grid((d_out + kRowsPerBlock - 1) / kRowsPerBlock);
+  const dim3 block(kRowsPerBlock * kWave);
+  if (per_row) {
+    hipLaunchKernelGGL(compress_rows_kernel<true>, grid, block, 0, stream, w_ft, w_base, d_out,
+                       d_in, packed, alpha, nullptr);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(compress_rows_kernel<false>, grid, block, 0, stream, w_ft, w_base, d_out,
+                     d_in, packed, nullptr, partial);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(compress_finalize_kernel, dim3(1), dim3(kFinalizeThreads), 0, stream,
+                     partial, d_out, (uint64_t)d_out * (uint64_t)d_in, alpha);
+  return hipGetLastError();
+}
+
+}  // namespace bd

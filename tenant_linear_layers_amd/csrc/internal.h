@@ -1,0 +1,39 @@
+// Launchers shared between the C ABI layer and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bd {
+
+constexpr int kMaxVariants = 64;   // equals BITDELTA_MAX_VARIANTS
+constexpr int kMaxSkinnyTokens = 64;
+
+// Compression of one matrix.  per_row != 0: alpha[d_out]; otherwise alpha[1]
+// and `partial` holds 2*d_out uint64 of scratch.
+hipError_t launch_compress(const uint16_t* w_ft, const uint16_t* w_base, int d_out, int d_in,
+                           int per_row, uint64_t* packed, float* alpha, uint64_t* partial,
+                           hipStream_t stream);
+
+// Kernel arguments of the decode-shaped linear (single variant or mixed).
+struct SkinnyArgs {
+  const uint16_t* x;         // [M, d_in]
+  const int32_t* ids;        // [M] variant ids (mixed batches only)
+  const uint16_t* w;         // [d_out, d_in]
+  uint16_t* y;               // [M, d_out]
+  int M, d_out, d_in, per_row;
+  int n_variants;
+  const uint32_t* packed[kMaxVariants];  // packed signs viewed as uint32 words
+  const float* alpha[kMaxVariants];
+};
+
+// 1 <= M <= 64, one variant (packed[0], alpha[0]).
+hipError_t launch_linear_skinny(const SkinnyArgs& a, hipStream_t stream);
+// 1 <= M <= 64, token m uses variant ids[m].
+hipError_t launch_linear_multi(const SkinnyArgs& a, hipStream_t stream);
+// Any M >= 1, one variant; the LDS-staged MFMA GEMM.
+hipError_t launch_linear_prefill(const uint16_t* x, int M, const uint16_t* w,
+                                 const uint8_t* packed_bytes, const float* alpha, int per_row,
+                                 int d_out, int d_in, uint16_t* y, hipStream_t stream);
+
+}  // namespace bd

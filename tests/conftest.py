@@ -8,3 +8,15 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+import pytest  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    """Name each test on the real stderr before it runs, so a run that ends
+    abruptly still shows which case was on the GPU."""
+    sys.__stderr__.write(f"[case] {request.node.nodeid}\n")
+    sys.__stderr__.flush()
+    yield

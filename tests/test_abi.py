@@ -1,0 +1,117 @@
+"""C ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call.
+
+Every call below fails argument validation by construction, so no fake
+pointer is ever handed to the runtime or a kernel, on any machine.
+"""
+
+import ctypes
+import os
+import re
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+import tenant_linear_layers_amd as T
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "bitdelta.h")
+A = 0x100000      # 16-byte-aligned addresses that are never dereferenced
+B = 0x200000
+C = 0x300000
+D = 0x400000
+E = 0x500000
+
+
+def test_header_functions_are_exported():
+    text = open(HEADER).read()
+    names = set(re.findall(r"^\w[\w\s\*]*?\b(bitdelta_\w+)\s*\(", text, flags=re.M))
+    assert names == set(T.EXPORTS), names
+    L = T.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    for s in range(10):
+        txt = T.status_string(s)
+        assert txt and txt != "unknown status"
+    assert T.status_string(123) == "unknown status"
+
+
+def test_workspace_size():
+    assert T.compress_workspace_size(4096, 4096, 0) == 4096 * 16
+    assert T.compress_workspace_size(4096, 4096, 1) == 0
+    assert T.compress_workspace_size(4096, 100, 0) == 0     # invalid shape
+    assert T.compress_workspace_size(0, 64, 0) == 0
+
+
+def test_host_rounding_matches_oracle():
+    """The library's rounding routine (the one its kernels use) against the
+    oracle's independent long division, on random sums and counts."""
+    rng = np.random.default_rng(7)
+    for _ in range(4000):
+        n = int(rng.integers(1, 1 << 34))
+        s = int(rng.integers(0, 1 << 62)) << int(rng.integers(0, 30))
+        s += int(rng.integers(0, 1 << 20))
+        want = O.rne_ratio_to_f32_bits(s, n << 48) if s else 0
+        assert T.ratio_to_f32_bits(s, n) == want, (s, n)
+    # exact halfway cases, both parities
+    for q in (1 << 23, (1 << 23) + 1, (1 << 24) - 1):
+        for n in (1, 3, 4096):
+            s = ((2 * q + 1) * n) << 23               # S/(n 2^48) = (q+1/2) 2^-24
+            assert T.ratio_to_f32_bits(s, n) == O.rne_ratio_to_f32_bits(s, n << 48)
+    assert T.ratio_to_f32_bits(0, 5) == 0
+    assert T.ratio_to_f32_bits(5, 0) == 0x7FC00000
+    # the mean of |d| for constant |d| = 2^-12 over 4096 elements
+    s = 4096 * (1 << 36)
+    assert T.ratio_to_f32_bits(s, 4096) == int(np.float32(2.0 ** -12).view(np.uint32))
+    assert float(Fraction(s, 4096 << 48)) == 2.0 ** -12
+
+
+def _c(status):
+    return int(status)
+
+
+def test_compress_argument_errors():
+    L = T.lib()
+    f = L.bitdelta_compress
+    assert _c(f(None, B, 4, 64, 1, C, D, None, 0, None)) == 1
+    assert _c(f(A, B, 4, 100, 1, C, D, None, 0, None)) == 2      # d_in % 64
+    assert _c(f(A, B, 0, 64, 1, C, D, None, 0, None)) == 2       # d_out
+    assert _c(f(A, B, 4, 0, 1, C, D, None, 0, None)) == 2
+    assert _c(f(A, B, 1 << 31, 64, 1, C, D, None, 0, None)) == 2
+    assert _c(f(A, B, 4, 64, 2, C, D, None, 0, None)) == 4       # mode
+    assert _c(f(A + 2, B, 4, 64, 1, C, D, None, 0, None)) == 3   # alignment
+    assert _c(f(A, B, 4, 64, 0, C, D, None, 0, None)) == 6       # no workspace
+    assert _c(f(A, B, 4, 64, 0, C, D, E, 63, None)) == 6         # too small
+    assert _c(f(A, B, 4, 64, 1, A + 64, D, None, 0, None)) == 9  # packed overlaps w_ft
+
+
+def test_linear_argument_errors():
+    f = T.lib().bitdelta_linear
+    assert _c(f(A, 4, B, C, D, 1, 8, 64, None, None)) == 1
+    assert _c(f(A, 0, B, C, D, 1, 8, 64, E, None)) == 2          # M = 0
+    assert _c(f(A, 4, B, C, D, 1, 8, 96, E, None)) == 2          # d_in % 64
+    assert _c(f(A, 4, B, C, D, 7, 8, 64, E, None)) == 4
+    assert _c(f(A, 4, B, C + 8, D, 1, 8, 64, E, None)) == 3
+    assert _c(f(A, 4, B, C, D + 2, 1, 8, 64, E, None)) == 3      # alpha needs 4 bytes
+    assert _c(f(A, 4, B, C, D, 1, 8, 64, A, None)) == 9          # y overlaps x
+
+
+def test_multi_argument_errors():
+    f = T.lib().bitdelta_linear_multi
+    vp = ctypes.c_void_p
+    arr = (vp * 2)(C, C + 4096)
+    al = (vp * 2)(D, D + 4096)
+    nul = (vp * 2)(C, None)
+    pa, aa, na = (ctypes.cast(a, vp) for a in (arr, al, nul))
+    assert _c(f(A, 4, B, E, 2, pa, aa, 1, 8, 64, None, None)) == 1
+    assert _c(f(A, 4, B, E, 0, pa, aa, 1, 8, 64, E + 65536, None)) == 5
+    assert _c(f(A, 4, B, E, 65, pa, aa, 1, 8, 64, E + 65536, None)) == 5
+    assert _c(f(A, 4, B, E, 2, na, aa, 1, 8, 64, E + 65536, None)) == 1   # NULL entry
+    assert _c(f(A, 4, B + 2, E, 2, pa, aa, 1, 8, 64, E + 65536, None)) == 3
+    assert _c(f(A, 4, B, E, 2, pa, aa, 3, 8, 64, E + 65536, None)) == 4
+    assert _c(f(A, 4, B, E, 2, pa, aa, 1, 8, 32, E + 65536, None)) == 2
+    assert _c(f(A, 4, B, E, 2, pa, aa, 1, 8, 64, A, None)) == 9

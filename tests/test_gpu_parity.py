@@ -1,0 +1,319 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Packing and alpha are compared bit for bit; outputs within the tolerance in
+tests/helpers.py.  Small cases compare every output; the full-size workloads
+compare sampled output rows (each output row depends on one weight row only)
+and sampled compressed rows (per-row alpha), or stream the whole matrix
+through the oracle (per-matrix alpha).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import synthetic as S
+import tenant_linear_layers_amd as T
+from helpers import alpha_bits, assert_y_close, bits16, packed_u64
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    T.lib()  # fail loudly if the library is missing
+
+
+def to_dev(*ts):
+    return [t.to(DEV) for t in ts]
+
+
+def check_compress(wf, wb, mode, rows=None):
+    """GPU compress vs oracle, bit-exact.  rows: sampled rows (per-row mode)."""
+    packed, alpha = T.compress(wf, wb, mode)
+    torch.cuda.synchronize()
+    if rows is None:
+        p_ref, a_ref = O.compress(bits16(wf), bits16(wb), mode)
+        np.testing.assert_array_equal(packed_u64(packed), p_ref)
+        np.testing.assert_array_equal(alpha_bits(alpha), a_ref.view(np.uint32))
+    else:
+        assert mode == 1
+        ridx = torch.as_tensor(rows, device=DEV)
+        p_ref, a_ref = O.compress(bits16(wf[ridx]), bits16(wb[ridx]), 1)
+        np.testing.assert_array_equal(packed_u64(packed[ridx]), p_ref)
+        np.testing.assert_array_equal(alpha_bits(alpha[ridx]), a_ref.view(np.uint32))
+    return packed, alpha
+
+
+def oracle_y(x, wb, packed, alpha, mode, rows=None):
+    if rows is None:
+        return O.linear(bits16(x), bits16(wb), packed_u64(packed), alpha.cpu().numpy(), mode)
+    ridx = torch.as_tensor(rows, device=DEV)
+    a = alpha[ridx] if mode == 1 else alpha
+    return O.linear(bits16(x), bits16(wb[ridx]), packed_u64(packed[ridx]), a.cpu().numpy(), mode)
+
+
+# ---------------------------------------------------------------- workload 1
+def test_single_256x512_compress_and_linear():
+    wl = S.WORKLOADS["single_256x512"]
+    g = S.generator(wl.seed)
+    (_, d_out, d_in), = wl.matrices
+    wb = S.draw_base(d_out, d_in, wl.sigma, g)
+    wf = S.draw_finetuned(wb, wl.b, g)
+    x = S.draw_activations(4, d_in, g)
+    wb, wf, x = to_dev(wb, wf, x)
+    packed, alpha = check_compress(wf, wb, 0)
+    assert packed.numel() * 8 == 16384
+    y = T.linear(x, wb, packed, alpha, 0)
+    assert_y_close(y, oracle_y(x, wb, packed, alpha, 0), "single_256x512 M=4")
+
+
+# ---------------------------------------------------------------- workload 2
+@pytest.fixture(scope="module")
+def proj4096():
+    wl = S.WORKLOADS["proj_4096"]
+    g = S.generator(wl.seed)
+    wb = S.draw_base(4096, 4096, wl.sigma, g)
+    wf = S.draw_finetuned(wb, wl.b, g)
+    xs = {m: S.draw_activations(m, 4096, g) for m in wl.tokens}
+    wb, wf = to_dev(wb, wf)
+    return wb, wf, {m: x.to(DEV) for m, x in xs.items()}
+
+
+def test_proj4096_compress_per_row(proj4096):
+    wb, wf, _ = proj4096
+    check_compress(wf, wb, 1)
+
+
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_proj4096_linear(proj4096, m):
+    wb, wf, xs = proj4096
+    packed, alpha = T.compress(wf, wb, 1)
+    y = T.linear(xs[m], wb, packed, alpha, 1)
+    assert_y_close(y, oracle_y(xs[m], wb, packed, alpha, 1), f"proj_4096 M={m}")
+
+
+# ---------------------------------------------------------------- edge cases
+@pytest.mark.parametrize("shape", [(1, 64), (3, 128), (17, 192), (33, 576), (5, 1088), (70, 4160)])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_compress_ragged_shapes(shape, mode):
+    wb, wf = S.small_pair(*shape, 0.02, 1e-3, seed=shape[0] * 7 + shape[1])
+    wb, wf = to_dev(wb, wf)
+    check_compress(wf, wb, mode)
+
+
+def _bf16(a):
+    return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).to(DEV)
+
+
+def test_compress_special_values():
+    rng = np.random.default_rng(5)
+    d_out, d_in = 8, 256
+    base = rng.normal(0, 0.02, (d_out, d_in)).astype(np.float32)
+    wb = _bf16(base)
+    # row 0: zero delta (+0 and -0); row 1: constant magnitude 2^-12
+    ft = wb.float().cpu().numpy().copy()          # row 0 equal to the base
+    j = np.clip(np.round(base[1] * 4096), -200, 200)
+    ft[1] = (j + rng.choice([-1, 1], d_in)) / 4096
+    wb = wb.clone()
+    wb[1] = _bf16(j / 4096)
+    wf = _bf16(ft)
+    wf[0, ::2] = _bf16(np.zeros(d_in // 2)) * -1.0     # -0 against +/-0 bases
+    wb[0, ::2] = 0
+    # row 2: +inf, row 3: NaN, row 4: |d| >= 2^15, row 5: |d| just below 2^15
+    wf[2, 3] = float("inf")
+    wf[3, 9] = float("nan")
+    wf[4, 0] = 65536.0
+    wb[4, 0] = 0.0
+    wf[5, 0] = 16384.0
+    wb[5, 0] = -16000.0
+    packed, alpha = check_compress(wf, wb, 1)
+    a = alpha_bits(alpha)
+    assert a[0] == 0 and np.all(packed_u64(packed)[0] == np.uint64(0xFFFFFFFFFFFFFFFF))
+    assert alpha.cpu()[1].item() == 2.0 ** -12
+    assert a[2] == a[3] == a[4] == 0x7FC00000 and a[5] != 0x7FC00000
+    check_compress(wf, wb, 0)
+
+
+def test_compress_is_deterministic():
+    wb, wf = S.small_pair(300, 2048, 0.02, 1e-3, seed=77)
+    wb, wf = to_dev(wb, wf)
+    for mode in (0, 1):
+        p1, a1 = T.compress(wf, wb, mode)
+        p2, a2 = T.compress(wf, wb, mode)
+        assert torch.equal(p1, p2) and torch.equal(a1.view(torch.int32), a2.view(torch.int32))
+
+
+@pytest.mark.parametrize("shape", [(17, 192), (100, 320), (64, 1024), (1, 64)])
+@pytest.mark.parametrize("m", [1, 2, 15, 16, 17, 31, 33, 48, 63, 64])
+def test_linear_decode_ragged(shape, m):
+    mode = (shape[0] + m) % 2
+    wb, wf = S.small_pair(*shape, 0.02, 1e-3, seed=shape[0] + m)
+    x = S.draw_activations(m, shape[1], S.generator(m))
+    wb, wf, x = to_dev(wb, wf, x)
+    packed, alpha = T.compress(wf, wb, mode)
+    y = T.linear(x, wb, packed, alpha, mode)
+    assert_y_close(y, oracle_y(x, wb, packed, alpha, mode), f"decode {shape} M={m}")
+
+
+@pytest.mark.parametrize("shape", [(130, 192), (257, 640), (128, 64)])
+@pytest.mark.parametrize("m", [65, 100, 256, 300, 513])
+def test_linear_prefill_ragged(shape, m):
+    mode = (shape[0] + m) % 2
+    wb, wf = S.small_pair(*shape, 0.02, 1e-3, seed=shape[1] + m)
+    x = S.draw_activations(m, shape[1], S.generator(m + 1))
+    wb, wf, x = to_dev(wb, wf, x)
+    packed, alpha = T.compress(wf, wb, mode)
+    y = T.linear(x, wb, packed, alpha, mode)
+    assert_y_close(y, oracle_y(x, wb, packed, alpha, mode), f"prefill {shape} M={m}")
+
+
+@pytest.mark.parametrize("m", [3, 300])
+def test_linear_one_hot_extracts_columns(m):
+    """x = e_c picks column c of W_eff: any bit-order, axis or layout slip in
+    either kernel shows up here."""
+    d_out, d_in = 48, 256
+    wb, wf = S.small_pair(d_out, d_in, 0.02, 1e-3, seed=91)
+    cols = [(7 * i + 3) % d_in for i in range(m)]
+    x = np.zeros((m, d_in), np.float32)
+    x[np.arange(m), cols] = 1.0
+    wb, wf = to_dev(wb, wf)
+    xd = _bf16(x)
+    packed, alpha = T.compress(wf, wb, 1)
+    y = T.linear(xd, wb, packed, alpha, 1).float().cpu().numpy()
+    d = O.delta_f32(bits16(wf), bits16(wb))
+    w = O.bf16_bits_to_f32(bits16(wb)).astype(np.float64)
+    a = alpha.cpu().numpy().astype(np.float64)
+    for i, c in enumerate(cols):
+        ref = w[:, c] + a * np.where(d[:, c] < 0, -1.0, 1.0)
+        assert np.allclose(y[i], ref, rtol=2 ** -8, atol=1e-7), (i, c)
+
+
+# ---------------------------------------------------------------- multi
+def _variants(d_out, d_in, n_var, seed, mode):
+    g = S.generator(seed)
+    wb = S.draw_base(d_out, d_in, 0.02, g)
+    wfs = [S.draw_finetuned(wb, 2e-4 * (v + 1), g) for v in range(n_var)]
+    wb = wb.to(DEV)
+    packs, alphas = [], []
+    for wf in wfs:
+        p, a = T.compress(wf.to(DEV), wb, mode)
+        packs.append(p)
+        alphas.append(a)
+    return wb, packs, alphas
+
+
+def _multi_ref(x, ids, wb, packs, alphas, mode):
+    return O.linear_multi(bits16(x), ids.cpu().numpy(), bits16(wb),
+                          [packed_u64(p) for p in packs], [a.cpu().numpy() for a in alphas], mode)
+
+
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 32, 50, 64, 100, 130])
+@pytest.mark.parametrize("shape", [(40, 192), (130, 512)])
+def test_multi_mixed_ids(m, shape):
+    mode = m % 2
+    wb, packs, alphas = _variants(*shape, 5, seed=m + shape[0], mode=mode)
+    rng = np.random.default_rng(m)
+    ids = rng.integers(-1, 5, size=m).astype(np.int32)
+    if m > 3:
+        ids[2] = 7           # invalid id -> NaN row
+        ids[3] = -5
+    x = S.draw_activations(m, shape[1], S.generator(m + 2)).to(DEV)
+    idt = torch.from_numpy(ids).to(DEV)
+    y = T.linear_multi(x, idt, wb, packs, alphas, mode)
+    assert_y_close(y, _multi_ref(x, idt, wb, packs, alphas, mode), f"multi {shape} M={m}")
+
+
+def test_multi_single_variant_matches_linear():
+    wb, packs, alphas = _variants(96, 384, 3, seed=5, mode=1)
+    x = S.draw_activations(40, 384, S.generator(6)).to(DEV)
+    ids = torch.full((40,), 1, dtype=torch.int32, device=DEV)
+    y_multi = T.linear_multi(x, ids, wb, packs, alphas, 1)
+    y_single = T.linear(x, wb, packs[1], alphas[1], 1)
+    assert torch.equal(y_multi.view(torch.int16), y_single.view(torch.int16))
+
+
+def test_multi_zipf_mix_many_variants():
+    wb, packs, alphas = _variants(200, 1024, 14, seed=9, mode=1)
+    ids = torch.from_numpy(S.zipf_ids(64, 14, seed=10)).to(DEV)
+    x = S.draw_activations(64, 1024, S.generator(11)).to(DEV)
+    y = T.linear_multi(x, ids, wb, packs, alphas, 1)
+    assert_y_close(y, _multi_ref(x, ids, wb, packs, alphas, 1), "multi zipf 14 variants")
+
+
+# ---------------------------------------------------------------- workloads 3, 4
+def _sample_rows(d_out, k, seed):
+    rng = np.random.default_rng(seed)
+    rows = rng.choice(d_out, size=min(k, d_out), replace=False)
+    rows[:2] = [0, d_out - 1]
+    return np.sort(rows)
+
+
+def test_layer70b_multi_full_size():
+    """14 variants of one 70B-shaped layer, M=32 Zipf(1.1) mix: every one of
+    the 70 compressions checked bit-exact on sampled rows, every linear on
+    sampled output rows."""
+    wl = S.WORKLOADS["layer70b_multi"]
+    g = S.generator(wl.seed, DEV)
+    bases = S.draw_layer_bases(wl, g, DEV)
+    scales = S.variant_scales(wl)
+    packs = [[None] * len(bases) for _ in scales]
+    alphas = [[None] * len(bases) for _ in scales]
+    for v, i, wf in S.iter_finetuned(bases, scales, g):
+        rows = _sample_rows(wf.shape[0], 6, 1000 * v + i)
+        packs[v][i], alphas[v][i] = check_compress(wf, bases[i], 1, rows=rows)
+        del wf
+    xs = S.draw_layer_inputs(wl, 32, g, DEV)
+    ids = torch.from_numpy(S.zipf_ids(32, wl.n_variants, wl.seed)).to(DEV)
+    ids_np = ids.cpu().numpy()
+    for i, (name, d_out, d_in) in enumerate(wl.matrices):
+        y = T.linear_multi(xs[i], ids, bases[i], [packs[v][i] for v in range(len(scales))],
+                           [alphas[v][i] for v in range(len(scales))], 1)
+        rows = _sample_rows(d_out, 48, 7 + i)
+        ridx = torch.as_tensor(rows, device=DEV)
+        ref = O.linear_multi(bits16(xs[i]), ids_np, bits16(bases[i][ridx]),
+                             [packed_u64(packs[v][i][ridx]) for v in range(len(scales))],
+                             [alphas[v][i][ridx].cpu().numpy() for v in range(len(scales))], 1)
+        assert_y_close(y[:, ridx], ref, f"layer70b_multi {name}")
+
+
+def _oracle_alpha_streamed(wf, wb, chunk=2048):
+    """Per-matrix alpha through the oracle, rows streamed in chunks: the
+    matrix sum is the sum of the row sums."""
+    total, bad = 0, False
+    for r0 in range(0, wf.shape[0], chunk):
+        d = O.delta_f32(bits16(wf[r0:r0 + chunk]), bits16(wb[r0:r0 + chunk]))
+        sums, _, flags = O.fixed_point_scope_sums(d, 1)
+        total += sum(sums)
+        bad = bad or any(flags)
+    n = wf.shape[0] * wf.shape[1]
+    return O.F32_NAN_BITS if bad else O.rne_ratio_to_f32_bits(total, n << O.Q_FRACTION_BITS)
+
+
+def test_layer70b_prefill_full_size():
+    """One variant of one 70B-shaped layer, per-matrix alpha, M=2048 through
+    the prefill GEMM: alpha bit-exact over each whole matrix, packing on
+    sampled rows, outputs on sampled rows."""
+    wl = S.WORKLOADS["layer70b_prefill"]
+    g = S.generator(wl.seed, DEV)
+    bases = S.draw_layer_bases(wl, g, DEV)
+    packs, alphas = [None] * 5, [None] * 5
+    for v, i, wf in S.iter_finetuned(bases, S.variant_scales(wl), g):
+        packs[i], alphas[i] = T.compress(wf, bases[i], 0)
+        assert alpha_bits(alphas[i])[0] == _oracle_alpha_streamed(wf, bases[i])
+        rows = _sample_rows(wf.shape[0], 6, 3 + i)
+        ridx = torch.as_tensor(rows, device=DEV)
+        p_ref, _ = O.compress(bits16(wf[ridx]), bits16(bases[i][ridx]), 1)
+        np.testing.assert_array_equal(packed_u64(packs[i][ridx]), p_ref)
+        del wf
+    xs = S.draw_layer_inputs(wl, 2048, g, DEV)
+    for i, (name, d_out, d_in) in enumerate(wl.matrices):
+        y = T.linear(xs[i], bases[i], packs[i], alphas[i], 0)
+        rows = _sample_rows(d_out, 32, 11 + i)
+        assert_y_close(y[:, torch.as_tensor(rows, device=DEV)],
+                       oracle_y(xs[i], bases[i], packs[i], alphas[i], 0, rows=rows),
+                       f"layer70b_prefill {name}")
