@@ -10,9 +10,13 @@ mixed-variant decode batch (Zipf(1.1) over 14 variants), and the prefill GEMM
 rotate so that the working set of consecutive calls exceeds the 256 MB
 last-level cache several times: every call streams its weights from HBM.
 
-Each kernel range inside the timed steps is bracketed by HIP events on the
-stream the kernels run on, which gives per-kernel average durations; the
-whole K steps are bracketed by synchronisations for ms_per_step.  The line
+Launches are captured in HIP graphs so that the GPU runs them back to back
+(a Python launch costs more host time than a decode kernel takes).  Timed
+region 1 replays K one-pass graphs (the steps), each bracketed by HIP events,
+between synchronisations: ms_per_step.  Timed region 2 replays, per kernel,
+a graph of back-to-back launches over the rotation copies with HIP events
+around each replay, on the stream the kernels run on: the average launch
+duration of each kernel, which is what value and the rooflines use.  The line
 printed reports decode effective HBM GB/s (algorithmic bytes / kernel time)
 as `value`, the prefill TFLOP/s beside it, a roofline entry per kernel, and
 the CPU oracle timed on a bounded sample of the same workload.
@@ -75,31 +79,33 @@ def counter_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-class Ranges:
-    """Per-name HIP-event timing of kernel ranges on the current stream."""
-
-    def __init__(self):
-        self.pending = []
-        self.total_ms = {}
-        self.count = {}
-
-    def run(self, name, fn):
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record()
+def capture(fn) -> torch.cuda.CUDAGraph:
+    """HIP graph of the launches fn makes (run once eagerly first, on a side
+    stream, as torch's capture rules ask)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
         fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_replays(graph, reps: int) -> float:
+    """Mean milliseconds per replay, from HIP events recorded on the stream
+    the graph runs on, around each replay."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps)]
+    for s, e in evs:
+        s.record()
+        graph.replay()
         e.record()
-        self.pending.append((name, s, e))
-
-    def collect(self):
-        torch.cuda.synchronize()
-        for name, s, e in self.pending:
-            self.total_ms[name] = self.total_ms.get(name, 0.0) + s.elapsed_time(e)
-            self.count[name] = self.count.get(name, 0) + 1
-        self.pending = []
-
-    def avg_us(self, name):
-        return 1e3 * self.total_ms[name] / self.count[name]
+    torch.cuda.synchronize()
+    return sum(s.elapsed_time(e) for s, e in evs) / reps
 
 
 # ------------------------------------------------------------------ workload
@@ -170,28 +176,44 @@ class ProjWorkload:
     def prefill_flops(self):
         return 2 * self.prefill_m * self.d_out * self.d_in
 
-    def step(self, rg: Ranges):
-        R = self.R
-        k = self.k
-        self.k += 1
-        wb = self.bases[k % R]
-        wf = self.fts[k % len(self.fts)]
-        cp, ca = self.c_out[k % 2]
-        rg.run("compress", lambda: T.compress(wf, wb, self.mode, packed=cp, alpha=ca))
-        for j, m in enumerate(self.decode_ms):
-            r = (k + 1 + j) % R
-            p, a = self.vsets[r][0]
-            rg.run(f"decode_m{m}", lambda m=m, r=r, p=p, a=a:
-                   T.linear(self.xs[m], self.bases[r], p, a, self.mode, y=self.ys[m]))
-        r = (k + 5) % R
-        vs = self.vsets[r]
-        rg.run("multi", lambda: T.linear_multi(self.x_multi, self.ids, self.bases[r],
-                                               [p for p, _ in vs], [a for _, a in vs],
-                                               self.mode, y=self.y_multi))
-        r2 = (k + 7) % R
-        p, a = self.vsets[r2][0]
-        rg.run("prefill", lambda: T.linear(self.x_prefill, self.bases[r2], p, a, self.mode,
-                                           y=self.y_prefill))
+    # one launch of each kernel range on rotation copy r
+    def run_compress(self, r):
+        cp, ca = self.c_out[r % 2]
+        T.compress(self.fts[r % len(self.fts)], self.bases[r % self.R], self.mode,
+                   packed=cp, alpha=ca)
+
+    def run_decode(self, m, r):
+        p, a = self.vsets[r % self.R][0]
+        T.linear(self.xs[m], self.bases[r % self.R], p, a, self.mode, y=self.ys[m])
+
+    def run_multi(self, r):
+        vs = self.vsets[r % self.R]
+        T.linear_multi(self.x_multi, self.ids, self.bases[r % self.R], [p for p, _ in vs],
+                       [a for _, a in vs], self.mode, y=self.y_multi)
+
+    def run_prefill(self, r):
+        p, a = self.vsets[r % self.R][0]
+        T.linear(self.x_prefill, self.bases[r % self.R], p, a, self.mode, y=self.y_prefill)
+
+    def one_pass(self, j):
+        """One pass of the whole path (a step), on copies 6j .. 6j+5."""
+        r = 6 * j
+        self.run_compress(r)
+        for i, m in enumerate(self.decode_ms):
+            self.run_decode(m, r + 1 + i)
+        self.run_multi(r + 4)
+        self.run_prefill(r + 5)
+
+    def ranges(self):
+        """name -> (launches per graph, function making them back to back)."""
+        out = {"compress": (len(self.fts), lambda: [self.run_compress(r)
+                                                    for r in range(len(self.fts))])}
+        for m in self.decode_ms:
+            out[f"decode_m{m}"] = (self.R, lambda m=m: [self.run_decode(m, r)
+                                                        for r in range(self.R)])
+        out["multi"] = (self.R, lambda: [self.run_multi(r) for r in range(self.R)])
+        out["prefill"] = (8, lambda: [self.run_prefill(r) for r in range(8)])
+        return out
 
 
 # ------------------------------------------------------------------ CPU oracle
@@ -264,28 +286,53 @@ def main():
     print(f"[bench] rotation copies R={w.R}, distinct variants in the mixed batch "
           f"D={w.distinct}", file=sys.stderr, flush=True)
 
-    warm = Ranges()
+    # Graphs: one per pass over distinct rotation copies (the steps), and
+    # one per kernel range holding back-to-back launches over the copies.
+    n_pass = max(1, w.R // 6)
+    passes = [capture(lambda j=j: w.one_pass(j)) for j in range(n_pass)]
+    range_graphs = {name: (n, capture(fn)) for name, (n, fn) in w.ranges().items()}
+    # the graphs must reproduce eager results
+    w.run_decode(16, 0)
+    y_eager = w.ys[16].clone()
+    range_graphs["decode_m16"][1].replay()
+    torch.cuda.synchronize()
+    w.run_decode(16, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(w.ys[16], y_eager), "graph replay differs from eager launch"
     for _ in range(args.warmup):
-        w.step(warm)
-    warm.collect()
+        passes[_ % n_pass].replay()
+    torch.cuda.synchronize()
+    print(f"[bench] graphs captured ({n_pass} passes, {len(range_graphs)} ranges)",
+          file=sys.stderr, flush=True)
 
-    rg = Ranges()
+    # Timed region 1: K steps, each one pass of the path.
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        w.step(rg)
+        step_ev[i][0].record()
+        passes[i % n_pass].replay()
+        step_ev[i][1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    rg.collect()
-    print(f"[bench] timed {args.steps} steps in {wall:.3f} s", file=sys.stderr, flush=True)
+    step_ms = sum(s.elapsed_time(e) for s, e in step_ev) / args.steps
+    # Timed region 2: each kernel range, back-to-back launches, HIP events
+    # around each replay -> average launch duration per kernel.
+    avg_us = {}
+    for name, (n, g) in range_graphs.items():
+        g.replay()
+        avg_us[name] = 1e3 * time_replays(g, max(3, args.steps // 4)) / n
+    print(f"[bench] timed {args.steps} steps in {wall:.3f} s "
+          f"(GPU {step_ms:.3f} ms per step)", file=sys.stderr, flush=True)
 
     dec_bytes = sum(w.decode_bytes(m) for m in w.decode_ms)
-    dec_us = sum(rg.avg_us(f"decode_m{m}") for m in w.decode_ms)
+    dec_us = sum(avg_us[f"decode_m{m}"] for m in w.decode_ms)
     dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
-    pre_us = rg.avg_us("prefill")
+    pre_us = avg_us["prefill"]
     pre_tflops = w.prefill_flops() / (pre_us * 1e-6) / 1e12
-    comp_us = rg.avg_us("compress")
-    multi_us = rg.avg_us("multi")
+    comp_us = avg_us["compress"]
+    multi_us = avg_us["multi"]
 
     rooflines = {
         "decode": roofline_entry("hbm", dec_gbs, HBM_PEAK_GBS, "GB/s",
@@ -297,7 +344,7 @@ def main():
         "prefill": roofline_entry("mfma", pre_tflops, BF16_PEAK_TFLOPS, "TFLOP/s",
                                   counter_traffic("prefill", w.name)),
     }
-    kernel_us = {name: round(rg.avg_us(name), 3) for name in rg.total_ms}
+    kernel_us = {name: round(v, 3) for name, v in avg_us.items()}
 
     cpu = None
     if args.cpu_budget > 0:
@@ -311,7 +358,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(1e3 * wall / args.steps, 4),
+        "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -8,6 +8,7 @@ an exception is raised.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -95,6 +96,13 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(handle)
 
 
+def _on(dev: torch.device):
+    """Make dev the current HIP device for the call (a no-op when it is)."""
+    if dev.index is None or dev.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(dev)
+
+
 def _ptr(t) -> ctypes.c_void_p:
     return ctypes.c_void_p(None if t is None else t.data_ptr())
 
@@ -140,7 +148,7 @@ def compress(w_ft: torch.Tensor, w_base: torch.Tensor, alpha_mode: int, packed=N
     if workspace is None and need:
         workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib().bitdelta_compress(_ptr(w_ft), _ptr(w_base), d_out, d_in, alpha_mode,
                                      _ptr(packed), _ptr(alpha), _ptr(workspace), ws_bytes,
                                      _stream(stream))
@@ -164,7 +172,7 @@ def linear(x: torch.Tensor, w_base: torch.Tensor, packed: torch.Tensor, alpha: t
     if y is None:
         y = torch.empty((*lead, d_out), dtype=torch.bfloat16, device=dev)
     _need(y, "y", torch.bfloat16, dev)
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib().bitdelta_linear(_ptr(x), m, _ptr(w_base), _ptr(packed), _ptr(alpha),
                                    alpha_mode, d_out, d_in, _ptr(y), _stream(stream))
     _check(st, "bitdelta_linear")
@@ -194,7 +202,7 @@ def linear_multi(x: torch.Tensor, variant_ids: torch.Tensor, w_base: torch.Tenso
     _need(y, "y", torch.bfloat16, dev)
     parr = (ctypes.c_void_p * max(nv, 1))(*[p.data_ptr() for p in packed_list])
     aarr = (ctypes.c_void_p * max(nv, 1))(*[a.data_ptr() for a in alpha_list])
-    with torch.cuda.device(dev):
+    with _on(dev):
         st = lib().bitdelta_linear_multi(_ptr(x), m, _ptr(variant_ids), _ptr(w_base), nv,
                                          ctypes.cast(parr, ctypes.c_void_p),
                                          ctypes.cast(aarr, ctypes.c_void_p), alpha_mode, d_out,

@@ -64,43 +64,59 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void compress_rows_kernel(
   uint32_t bad = 0;
   const int n_chunks = (d_in + 511) >> 9;
 
-  for (int c = 0; c < n_chunks; ++c) {
-    const int e0 = (c << 9) + (lane << 3);
-    // d_in is a multiple of 64, so the active lanes of the last chunk cover
-    // whole 64-element words.
-    const bool active = e0 < d_in;
-    u32x4 va = {0u, 0u, 0u, 0u}, vb = {0u, 0u, 0u, 0u};
-    if (active) {
-      va = ld128(a_row + e0);
-      vb = ld128(b_row + e0);
-    }
-    uint64_t ball[8];
+  // Four chunks per group: all eight 16-byte loads of a group are issued
+  // before any is used, so each wave keeps 8 KiB in flight.
+  constexpr int kGroup = 4;
+  for (int c0 = 0; c0 < n_chunks; c0 += kGroup) {
+    // Loads are never predicated (see the decode kernel): lanes past the end
+    // of the row re-read its last 16 bytes and are zeroed afterwards, which
+    // only happens in a final partial chunk (d_in % 512 != 0).
+    u32x4 va[kGroup], vb[kGroup];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t ua = (j & 1) ? (va[j >> 1] & 0xFFFF0000u) : (va[j >> 1] << 16);
-      const uint32_t ub = (j & 1) ? (vb[j >> 1] & 0xFFFF0000u) : (vb[j >> 1] << 16);
-      const float d = __uint_as_float(ua) - __uint_as_float(ub);
-      // sign bit 1 <=> +1 <=> not (d < 0): +0, -0 and NaN give +1.
-      ball[j] = __builtin_amdgcn_ballot_w64(!(d < 0.0f));
-      // q = floor(|d| * 2^48) = hi * 2^32 + lo with hi = floor(|d| * 2^16)
-      // and lo = floor(frac(|d| * 2^16) * 2^32); every step is exact.
-      float ad = __builtin_fabsf(d) * 65536.0f;
-      const bool ok = ad < 2147483648.0f;  // false for NaN, inf, |d| >= 2^15
-      bad |= ok ? 0u : 1u;
-      ad = ok ? ad : 0.0f;
-      const uint32_t hi = (uint32_t)ad;
-      const float fr = ad - (float)hi;
-      const uint32_t lo = (uint32_t)(fr * 4294967296.0f);
-      acc_hi += active ? hi : 0u;
-      acc_lo += active ? lo : 0u;
+    for (int u = 0; u < kGroup; ++u) {
+      const int e0 = min(((c0 + u) << 9) + (lane << 3), d_in - 8);
+      va[u] = ld128(a_row + e0);
+      vb[u] = ld128(b_row + e0);
     }
-    if (lane < 8) {
-      // word `lane` of this chunk: bit 8i+j comes from ballot j, bit 8*lane+i.
-      uint64_t x = 0;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x |= ((ball[j] >> (lane << 3)) & 0xFFull) << (j << 3);
-      const int w = (c << 3) + lane;
-      if (w < n_words) p_row[w] = transpose8x8(x);
+    for (int u = 0; u < kGroup; ++u) {
+      const int c = c0 + u;
+      if (c >= n_chunks) break;  // uniform
+      if ((c << 9) + 512 > d_in && (c << 9) + (lane << 3) >= d_in) {
+        // d_in is a multiple of 64, so the active lanes of a partial chunk
+        // cover whole 64-element words; the rest contribute +1 signs (never
+        // stored) and zero magnitudes.
+        va[u] = u32x4{0u, 0u, 0u, 0u};
+        vb[u] = u32x4{0u, 0u, 0u, 0u};
+      }
+      uint64_t ball[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t ua = (j & 1) ? (va[u][j >> 1] & 0xFFFF0000u) : (va[u][j >> 1] << 16);
+        const uint32_t ub = (j & 1) ? (vb[u][j >> 1] & 0xFFFF0000u) : (vb[u][j >> 1] << 16);
+        const float d = __uint_as_float(ua) - __uint_as_float(ub);
+        // sign bit 1 <=> +1 <=> not (d < 0): +0, -0 and NaN give +1.
+        ball[j] = __builtin_amdgcn_ballot_w64(!(d < 0.0f));
+        // q = floor(|d| * 2^48) = hi * 2^32 + lo with hi = floor(|d| * 2^16)
+        // and lo = floor(frac(|d| * 2^16) * 2^32); every step is exact.
+        float ad = __builtin_fabsf(d) * 65536.0f;
+        const bool ok = ad < 2147483648.0f;  // false for NaN, inf, |d| >= 2^15
+        bad |= ok ? 0u : 1u;
+        ad = ok ? ad : 0.0f;
+        const uint32_t hi = (uint32_t)ad;
+        const float fr = ad - (float)hi;
+        const uint32_t lo = (uint32_t)(fr * 4294967296.0f);
+        acc_hi += hi;  // inactive lanes hold zeros, so add zero
+        acc_lo += lo;
+      }
+      if (lane < 8) {
+        // word `lane` of this chunk: bit 8i+j comes from ballot j, bit 8*lane+i.
+        uint64_t x = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x |= ((ball[j] >> (lane << 3)) & 0xFFull) << (j << 3);
+        const int w = (c << 3) + lane;
+        if (w < n_words) p_row[w] = transpose8x8(x);
+      }
     }
   }
 

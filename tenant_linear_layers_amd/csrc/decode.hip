@@ -65,7 +65,11 @@ struct Groups {
   int plo[kMaxSkinnyTokens];
   int phi[kMaxSkinnyTokens];
   int key[kMaxSkinnyTokens];
+  int dv[kMaxSkinnyTokens];   // distinct variants present, ascending
+  int dp0[kMaxSkinnyTokens];  // first pair of each distinct variant
+  int dp1[kMaxSkinnyTokens];  // one past its last pair
   int np;
+  int nd;
 };
 
 __device__ void build_groups(Groups& G, const int32_t* ids, int M, int n_variants) {
@@ -104,18 +108,29 @@ __device__ void build_groups(Groups& G, const int32_t* ids, int M, int n_variant
       G.phi[idx] = end - (t / 16) * 16;
     }
   }
+  __syncthreads();
   if (t == 0) {
-    int np = 0;
+    int np = 0, nd = 0;
     for (int u = 0; u < M; ++u) {
       const int vu = G.slotv[u];
-      np += (vu >= 0 && (u % 16 == 0 || G.slotv[u - 1] != vu)) ? 1 : 0;
+      if (vu >= 0 && (u % 16 == 0 || G.slotv[u - 1] != vu)) {
+        if (nd == 0 || G.dv[nd - 1] != vu) {
+          if (nd > 0) G.dp1[nd - 1] = np;
+          G.dv[nd] = vu;
+          G.dp0[nd] = np;
+          ++nd;
+        }
+        ++np;
+      }
     }
+    if (nd > 0) G.dp1[nd - 1] = np;
     G.np = np;
+    G.nd = nd;
   }
   __syncthreads();
 }
 
-template <int MT, int NW, bool kMulti>
+template <int MT, int NW, int U, bool kMulti>
 __global__ __launch_bounds__(NW * kWave) void linear_skinny_kernel(const SkinnyArgs a) {
   __shared__ float red[NW * MT * 2 * 4 * kWave];
   __shared__ Groups G;
@@ -151,57 +166,102 @@ __global__ __launch_bounds__(NW * kWave) void linear_skinny_kernel(const SkinnyA
   const int nblk = (d_in + 127) >> 7;
   const int b0 = (wv * nblk) / NW;
   const int b1 = ((wv + 1) * nblk) / NW;
-  const int np = kMulti ? G.np : 0;
+  const int nd = kMulti ? G.nd : 0;
 
-  for (int b = b0; b < b1; ++b) {
-    const int k = (b << 7) + (g << 5);
-    const bool kv = k < d_in;  // false only for g >= 2 in a final 64-wide block
-    u32x4 xf[MT][4];
-    u32x4 wf[4];
+  // Groups of U blocks: every load of a group is issued before the first
+  // MFMA that needs it, so each wave keeps U blocks of weights in flight.
+  // Loads are never predicated (a lane-dependent load would force a wait on
+  // the register it shares with the zero fill): a block past the wave's
+  // range re-reads the last valid block and is skipped, and the lanes of a
+  // final 64-wide block that fall past d_in re-read valid data whose x is
+  // then zeroed.
+  const bool half_tail = (d_in & 127) != 0;
+  for (int b = b0; b < b1; b += U) {
+    u32x4 wf[U][4];
+    u32x4 xf[U][MT][4];
+    uint32_t bits[U];
+    size_t boff[U];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      wf[q] = kv ? ld128(wrow + k + 8 * q) : u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-        xf[t][q] = kv ? ld128(xrow[t] + k + 8 * q) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (!kMulti) {
-      const uint32_t bits = kv ? ld32(a.packed[0] + brow + (k >> 5)) : 0xFFFFFFFFu;
-      uint32_t s[16];
-      sign_pairs(bits, s);
+    for (int u = 0; u < U; ++u) {
+      const int bu = min(b + u, b1 - 1);
+      const int kc = min((bu << 7) + (g << 5), d_in - 32);
+      boff[u] = brow + (kc >> 5);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        wf[u][q] = ld128(wrow + kc + 8 * q);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          accw[t] = mfma16(xf[t][q], wf[q], accw[t]);
-          accs[t] = mfma16(xf[t][q], quad(s, q), accs[t]);
+        for (int t = 0; t < MT; ++t) xf[u][t][q] = ld128(xrow[t] + kc + 8 * q);
+      }
+      if (!kMulti) bits[u] = ld32(a.packed[0] + boff[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (half_tail && b + u == nblk - 1 && ((b + u) << 7) + (g << 5) >= d_in) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xf[u][t][q] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if (!kMulti) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (b + u >= b1) continue;  // uniform
+        uint32_t s[16];
+        sign_pairs(bits[u], s);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            accw[t] = mfma16(xf[u][t][q], wf[u][q], accw[t]);
+            accs[t] = mfma16(xf[u][t][q], quad(s, q), accs[t]);
+          }
         }
       }
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int u = 0; u < U; ++u) {
+        if (b + u >= b1) continue;  // uniform
 #pragma unroll
-        for (int t = 0; t < MT; ++t) accw[t] = mfma16(xf[t][q], wf[q], accw[t]);
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int t = 0; t < MT; ++t) accw[t] = mfma16(xf[u][t][q], wf[u][q], accw[t]);
       }
-      int vprev = -1;
-      uint32_t s[16];
-      for (int p = 0; p < np; ++p) {
-        const int v = __builtin_amdgcn_readfirstlane(G.pv[p]);
-        const int tp = __builtin_amdgcn_readfirstlane(G.pt[p]);
-        const int lo = G.plo[p];
-        const int hi = G.phi[p];
-        if (v != vprev) {
-          const uint32_t bits = kv ? ld32(a.packed[v] + brow + (k >> 5)) : 0xFFFFFFFFu;
-          sign_pairs(bits, s);
-          vprev = v;
+      // One distinct variant at a time; its sign words for the U blocks are
+      // fetched while the previous variant's MFMAs run.
+      uint32_t nxt[U];
+      if (nd > 0) {
+        const int v0 = __builtin_amdgcn_readfirstlane(G.dv[0]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) nxt[u] = ld32(a.packed[v0] + boff[u]);
+      }
+      for (int d = 0; d < nd; ++d) {
+        uint32_t cur[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+        if (d + 1 < nd) {
+          const int vn = __builtin_amdgcn_readfirstlane(G.dv[d + 1]);
+#pragma unroll
+          for (int u = 0; u < U; ++u) nxt[u] = ld32(a.packed[vn] + boff[u]);
         }
-        const bool keep = n >= lo && n < hi;
+        const int p0 = __builtin_amdgcn_readfirstlane(G.dp0[d]);
+        const int p1 = __builtin_amdgcn_readfirstlane(G.dp1[d]);
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-          if (t == tp) {
+        for (int u = 0; u < U; ++u) {
+          if (b + u >= b1) continue;  // uniform
+          uint32_t s[16];
+          sign_pairs(cur[u], s);
+          for (int p = p0; p < p1; ++p) {
+            const int tp = __builtin_amdgcn_readfirstlane(G.pt[p]);
+            const bool keep = n >= G.plo[p] && n < G.phi[p];
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              accs[t] = mfma16(masked(xf[t][q], keep), quad(s, q), accs[t]);
+            for (int t = 0; t < MT; ++t) {
+              if (t == tp) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                  accs[t] = mfma16(masked(xf[u][t][q], keep), quad(s, q), accs[t]);
+              }
+            }
           }
         }
       }
@@ -260,8 +320,10 @@ __global__ __launch_bounds__(NW * kWave) void linear_skinny_kernel(const SkinnyA
 template <int MT, bool kMulti>
 hipError_t launch_mt(const SkinnyArgs& a, hipStream_t stream) {
   constexpr int NW = 8;
+  constexpr int U = MT >= 4 ? 1 : (kMulti ? 4 / (2 * MT) : 4 / MT);
   const dim3 grid((a.d_out + 15) / 16);
-  hipLaunchKernelGGL((linear_skinny_kernel<MT, NW, kMulti>), grid, dim3(NW * kWave), 0, stream, a);
+  hipLaunchKernelGGL((linear_skinny_kernel<MT, NW, U, kMulti>), grid, dim3(NW * kWave), 0, stream,
+                     a);
   return hipGetLastError();
 }
 

@@ -317,3 +317,48 @@ def test_layer70b_prefill_full_size():
         assert_y_close(y[:, torch.as_tensor(rows, device=DEV)],
                        oracle_y(xs[i], bases[i], packs[i], alphas[i], 0, rows=rows),
                        f"layer70b_prefill {name}")
+
+
+# ---------------------------------------------------------------- graph capture
+def test_graph_replays_match_eager():
+    """Every entry point captured in one HIP graph: each replay, with eager
+    work and synchronisations in between, equals the eager results bit for
+    bit (the kernels use no memset and no host-side state)."""
+    wb, packs, alphas = _variants(96, 512, 3, seed=41, mode=0)
+    wf = S.draw_finetuned(wb.cpu(), 1e-3, S.generator(42)).to(DEV)
+    x4 = S.draw_activations(4, 512, S.generator(43)).to(DEV)
+    x100 = S.draw_activations(100, 512, S.generator(44)).to(DEV)
+    ids = torch.tensor([0, 2, -1, 1], dtype=torch.int32, device=DEV)
+    outs = dict(p=torch.empty_like(packs[0]), a=torch.empty_like(alphas[0]),
+                y4=torch.empty(4, 96, dtype=torch.bfloat16, device=DEV),
+                y100=torch.empty(100, 96, dtype=torch.bfloat16, device=DEV),
+                ym=torch.empty(4, 96, dtype=torch.bfloat16, device=DEV))
+    ws = torch.empty(T.compress_workspace_size(96, 512, 0), dtype=torch.uint8, device=DEV)
+
+    def run():
+        T.compress(wf, wb, 0, packed=outs["p"], alpha=outs["a"], workspace=ws)
+        T.linear(x4, wb, packs[1], alphas[1], 0, y=outs["y4"])
+        T.linear(x100, wb, packs[2], alphas[2], 0, y=outs["y100"])
+        T.linear_multi(x4, ids, wb, packs, alphas, 0, y=outs["ym"])
+
+    run()
+    torch.cuda.synchronize()
+    eager = {k: v.clone() for k, v in outs.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(4):
+        for v in outs.values():
+            v.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for k in outs:
+            assert torch.equal(outs[k].view(torch.uint8), eager[k].view(torch.uint8)), (rep, k)
+        _ = (x100.float() @ x100.float().T).sum().item()   # eager work between replays
