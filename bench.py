@@ -44,6 +44,7 @@ import tenant_linear_layers_amd as T  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 MALL_BYTES = 256 * 2**20
+METRIC = "bitdelta_linear effective HBM GB/s (decode) + bf16 TFLOP/s (prefill), 1 GPU"
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -216,6 +217,86 @@ class ProjWorkload:
         return out
 
 
+class LayerWorkload:
+    """One 70B-shaped decoder layer (QKV, O, gate, up, down).  mode "prefill":
+    one variant, per-matrix alpha, M = 2048 through the prefill GEMM, reported
+    in TFLOP/s.  mode "multi": 14 variants, per-row alpha, M = 32 tokens with
+    Zipf(1.1) ids through the mixed-variant kernel, reported in GB/s.  The
+    layer's weights (1.7 GB) exceed the last-level cache, so no rotation."""
+
+    def __init__(self, name, dev):
+        wl = S.WORKLOADS[name]
+        self.name, self.wl, self.dev = name, wl, dev
+        self.mode = wl.alpha_mode
+        self.kind = "prefill" if name == "layer70b_prefill" else "multi"
+        self.m = wl.tokens[0]
+        g = S.generator(wl.seed, dev)
+        self.bases = S.draw_layer_bases(wl, g, dev)
+        scales = S.variant_scales(wl)
+        self.packs = [[None] * len(self.bases) for _ in scales]
+        self.alphas = [[None] * len(self.bases) for _ in scales]
+        for v, i, wf in S.iter_finetuned(self.bases, scales, g):
+            self.packs[v][i], self.alphas[v][i] = T.compress(wf, self.bases[i], self.mode)
+            del wf
+        self.xs = S.draw_layer_inputs(wl, self.m, g, dev)
+        ids = S.zipf_ids(self.m, wl.n_variants, wl.seed)
+        self.ids = torch.from_numpy(ids).to(dev)
+        self.distinct = int(len(set(ids.tolist())))
+        self.ys = [torch.empty(self.m, d_out, dtype=torch.bfloat16, device=dev)
+                   for _, d_out, _ in wl.matrices]
+        self.R = 1
+
+    def run(self, i):
+        if self.kind == "prefill":
+            T.linear(self.xs[i], self.bases[i], self.packs[0][i], self.alphas[0][i], self.mode,
+                     y=self.ys[i])
+        else:
+            T.linear_multi(self.xs[i], self.ids, self.bases[i], [p[i] for p in self.packs],
+                           [a[i] for a in self.alphas], self.mode, y=self.ys[i])
+
+    def one_pass(self, j):
+        for i in range(len(self.bases)):
+            self.run(i)
+
+    def ranges(self):
+        return {f"{self.kind}_{nm}": (2, lambda i=i: [self.run(i), self.run(i)])
+                for i, (nm, _, _) in enumerate(self.wl.matrices)}
+
+    def work(self, i):
+        _, d_out, d_in = self.wl.matrices[i]
+        n = d_out * d_in
+        if self.kind == "prefill":
+            return 2.0 * self.m * n
+        alpha = 4 * (d_out if self.mode == 1 else 1)
+        return (2 * n + self.distinct * (n // 8 + alpha) + 2 * self.m * d_in
+                + 2 * self.m * d_out + 4 * self.m)
+
+    def report(self, avg_us, args):
+        names = [nm for nm, _, _ in self.wl.matrices]
+        total_us = sum(avg_us[f"{self.kind}_{nm}"] for nm in names)
+        total_work = sum(self.work(i) for i in range(len(names)))
+        per = {nm: round(self.work(i) / (avg_us[f"{self.kind}_{nm}"] * 1e-6)
+                         / (1e12 if self.kind == "prefill" else 1e9), 2)
+               for i, nm in enumerate(names)}
+        if self.kind == "prefill":
+            val = total_work / (total_us * 1e-6) / 1e12
+            roof = roofline_entry("mfma", val, BF16_PEAK_TFLOPS, "TFLOP/s",
+                                  counter_traffic("prefill", self.name))
+            unit = "TFLOP/s"
+        else:
+            val = total_work / (total_us * 1e-6) / 1e9
+            roof = roofline_entry("hbm", val, HBM_PEAK_GBS, "GB/s",
+                                  counter_traffic("multi", self.name))
+            unit = "GB/s"
+        cfg = {"workload": f"{self.name}: {self.wl.note}", "tokens": self.m,
+               "alpha_mode": "per_row" if self.mode == 1 else "per_matrix",
+               "matrices": [list(mm) for mm in self.wl.matrices]}
+        if self.kind == "multi":
+            cfg["distinct_variants"] = self.distinct
+        return {"value": round(val, 2), "unit": unit, "config": cfg, "per_matrix": per,
+                "roofline": roof, "layer_us": round(total_us, 2)}
+
+
 # ------------------------------------------------------------------ CPU oracle
 def cpu_baseline(w: ProjWorkload, budget_s: float):
     """The oracle, as it stands, on a bounded sample of the same workload:
@@ -265,7 +346,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="proj_4096", choices=["proj_4096"])
+    ap.add_argument("--workload", default="proj_4096",
+                    choices=["proj_4096", "layer70b_prefill", "layer70b_multi"])
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
     args = ap.parse_args()
@@ -281,7 +363,7 @@ def main():
     torch.cuda.set_device(dev)
     T.lib()
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
-    w = ProjWorkload(dev)
+    w = ProjWorkload(dev) if args.workload == "proj_4096" else LayerWorkload(args.workload, dev)
     torch.cuda.synchronize()
     print(f"[bench] rotation copies R={w.R}, distinct variants in the mixed batch "
           f"D={w.distinct}", file=sys.stderr, flush=True)
@@ -291,14 +373,15 @@ def main():
     n_pass = max(1, w.R // 6)
     passes = [capture(lambda j=j: w.one_pass(j)) for j in range(n_pass)]
     range_graphs = {name: (n, capture(fn)) for name, (n, fn) in w.ranges().items()}
-    # the graphs must reproduce eager results
-    w.run_decode(16, 0)
-    y_eager = w.ys[16].clone()
-    range_graphs["decode_m16"][1].replay()
-    torch.cuda.synchronize()
-    w.run_decode(16, 0)
-    torch.cuda.synchronize()
-    assert torch.equal(w.ys[16], y_eager), "graph replay differs from eager launch"
+    if isinstance(w, ProjWorkload):
+        # the graphs must reproduce eager results
+        w.run_decode(16, 0)
+        y_eager = w.ys[16].clone()
+        range_graphs["decode_m16"][1].replay()
+        torch.cuda.synchronize()
+        w.run_decode(16, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(w.ys[16], y_eager), "graph replay differs from eager launch"
     for _ in range(args.warmup):
         passes[_ % n_pass].replay()
     torch.cuda.synchronize()
@@ -326,6 +409,19 @@ def main():
     print(f"[bench] timed {args.steps} steps in {wall:.3f} s "
           f"(GPU {step_ms:.3f} ms per step)", file=sys.stderr, flush=True)
 
+    if not isinstance(w, ProjWorkload):
+        rep = w.report(avg_us, args)
+        out = {"metric": METRIC, "value": rep["value"], "unit": rep["unit"], "n_gpus": 1,
+               "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
+               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+               "dtype": "bf16", "data": "synthetic", "config": rep["config"],
+               "per_matrix": rep["per_matrix"], "layer_us": rep["layer_us"],
+               "roofline": rep["roofline"],
+               "kernel_avg_us": {k: round(v, 3) for k, v in avg_us.items()},
+               "cpu_baseline": None}
+        print(json.dumps(out), flush=True)
+        return
+
     dec_bytes = sum(w.decode_bytes(m) for m in w.decode_ms)
     dec_us = sum(avg_us[f"decode_m{m}"] for m in w.decode_ms)
     dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
@@ -352,7 +448,7 @@ def main():
         cpu = cpu_baseline(w, args.cpu_budget)
 
     out = {
-        "metric": "bitdelta_linear effective HBM GB/s (decode) + bf16 TFLOP/s (prefill), 1 GPU",
+        "metric": METRIC,
         "value": round(dec_gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,

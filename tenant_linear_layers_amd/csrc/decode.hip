@@ -13,13 +13,22 @@
 // W_eff happens and the only roundings are the float32 accumulation and the
 // final bf16 store.
 //
-// Work split: a workgroup owns 16 output rows; its NW waves split d_in into
-// contiguous ranges of 128-element blocks and their partial accumulators are
-// summed in LDS in a fixed order (deterministic).  Within a block, lane
-// (n = lane%16, g = lane/16) holds 32 consecutive elements of row n (four
-// 16-byte loads) and the 32 matching sign bits (one 4-byte load); the same
-// lane holds the same 32 elements of token n of each 16-token tile.  MFMA
-// 16x16x32 step q (0..3) uses the lane's elements 8q..8q+7 for both operands.
+// Work split: a workgroup owns 16 output rows; its NW waves take the
+// 128-element blocks of d_in round-robin (block b -> wave b % NW), so at any
+// time they work on NW consecutive blocks of the same rows and together
+// consume whole cache lines of weights and of sign words.  Their partial
+// accumulators are summed in LDS in a fixed order (deterministic).  Within a
+// block, lane (n = lane%16, g = lane/16) holds 32 consecutive elements of row
+// n (four 16-byte loads) and the 32 matching sign bits (one 4-byte load); the
+// same lane holds the same 32 elements of token n of each 16-token tile.
+// MFMA 16x16x32 step q (0..3) uses the lane's elements 8q..8q+7 for both
+// operands.
+//
+// Loads are never predicated: a lane-dependent load compiles to a masked
+// branch whose fill of the same register forces a wait on every load.  A
+// block past a wave's range re-reads the wave's last block and is skipped;
+// lanes of a final 64-wide block that fall past d_in re-read valid data whose
+// x is then zeroed.
 #include "common.h"
 #include "internal.h"
 
@@ -28,18 +37,20 @@ namespace {
 
 // +-1.0 bf16 pairs for the lane's 32 elements from their sign bits
 // (bit e = element e, 1 meaning +1).  Dword i pairs elements 2i (low half)
-// and 2i+1 (high half), the same pairing as the bf16 data dwords.
-// The negated bits are first spread so that the bits of elements 2i and
-// 2i+1 sit 16 places apart (zl for i < 8, zh for i >= 8); one shift then
-// puts both onto the two bf16 sign positions 15 and 31.
+// and 2i+1 (high half), the same pairing as the bf16 data dwords.  The
+// negated bits are first spread so that the bits of elements 2i and 2i+1 sit
+// 16 places apart (zl for i < 8, zh for i >= 8); one shift then puts both
+// onto the two bf16 sign positions 15 and 31, and one bitop3 keeps them and
+// adds the exponent and mantissa of 1.0.
 __device__ __forceinline__ void sign_pairs(uint32_t bits, uint32_t (&s)[16]) {
-  const uint32_t nb = ~bits;
-  const uint32_t zl = (nb & 0x00005555u) | ((nb << 15) & 0xFFFFAAAAu);
-  const uint32_t zh = ((nb >> 16) & 0x00005555u) | ((nb >> 1) & 0xFFFFAAAAu);
+  // bitop3 table 0x1B: (~a & c) | (~b & ~c), a bit-select of the negated
+  // inputs; table 0xEA: (a & b) | c.
+  const uint32_t zl = __builtin_amdgcn_bitop3_b32(bits, bits << 15, 0x00005555u, 0x1B);
+  const uint32_t zh = __builtin_amdgcn_bitop3_b32(bits >> 16, bits >> 1, 0x00005555u, 0x1B);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    s[i] = ((zl << (15 - 2 * i)) & 0x80008000u) | 0x3F803F80u;
-    s[i + 8] = ((zh << (15 - 2 * i)) & 0x80008000u) | 0x3F803F80u;
+    s[i] = __builtin_amdgcn_bitop3_b32(zl << (15 - 2 * i), 0x80008000u, 0x3F803F80u, 0xEA);
+    s[i + 8] = __builtin_amdgcn_bitop3_b32(zh << (15 - 2 * i), 0x80008000u, 0x3F803F80u, 0xEA);
   }
 }
 
@@ -48,26 +59,145 @@ __device__ __forceinline__ u32x4 quad(const uint32_t (&s)[16], int q) {
   return v;
 }
 
-__device__ __forceinline__ u32x4 masked(u32x4 v, bool keep) {
-  u32x4 z = {0u, 0u, 0u, 0u};
-  return keep ? v : z;
+// Number of a wave's blocks when NW waves take nblk blocks round-robin.
+__device__ __forceinline__ int blocks_of_wave(int wv, int nblk, int NW) {
+  return wv < nblk ? (nblk - 1 - wv) / NW + 1 : 0;
 }
 
+// Sum the NW waves' partial accumulators (LDS, fixed order) and store y.
+// out(slot, o, sw, ss, m) returns the output value and sets its token m.
+template <int MT, int NW, class Out>
+__device__ __forceinline__ void reduce_and_store(float* red, const f32x4 (&accw)[MT],
+                                                 const f32x4 (&accs)[MT], int row0, int M,
+                                                 int d_out, uint16_t* y, Out out) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      red[(((wv * MT + t) * 2 + 0) * 4 + v) * kWave + lane] = accw[t][v];
+      red[(((wv * MT + t) * 2 + 1) * 4 + v) * kWave + lane] = accs[t][v];
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < MT * 4 * kWave; idx += NW * kWave) {
+    const int l = idx & (kWave - 1);
+    const int v = (idx >> 6) & 3;
+    const int t = idx >> 8;
+    float sw = 0.f, ss = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      sw += red[(((w * MT + t) * 2 + 0) * 4 + v) * kWave + l];
+      ss += red[(((w * MT + t) * 2 + 1) * 4 + v) * kWave + l];
+    }
+    // MFMA 16x16 output layout: lane l holds rows 4*(l/16)+v of column l%16.
+    const int slot = 16 * t + 4 * (l >> 4) + v;
+    const int o = row0 + (l & 15);
+    if (slot < M && o < d_out) {
+      int m;
+      const float yv = out(slot, o, sw, ss, m);
+      y[(size_t)m * d_out + o] = f32_to_bf16_bits(yv);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- one variant
+template <int MT, int NW, int U>
+__global__ __launch_bounds__(NW * kWave) void linear_decode_kernel(const SkinnyArgs a) {
+  __shared__ float red[NW * MT * 2 * 4 * kWave];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int row0 = blockIdx.x * 16;
+  const int d_in = a.d_in;
+  const int M = a.M;
+  const int row = min(row0 + n, a.d_out - 1);
+
+  const uint16_t* xrow[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) xrow[t] = a.x + (size_t)min(16 * t + n, M - 1) * d_in;
+  const uint16_t* wrow = a.w + (size_t)row * d_in;
+  const uint32_t* brow = a.packed[0] + (size_t)row * (d_in >> 5);
+
+  f32x4 accw[MT], accs[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    accw[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accs[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int nblk = (d_in + 127) >> 7;
+  const int nmine = blocks_of_wave(wv, nblk, NW);
+  const bool half_tail = (d_in & 127) != 0;
+  // Groups of U blocks: every load of a group is issued before the first
+  // MFMA that needs it, so each wave keeps U blocks of weights in flight.
+  for (int i = 0; i < nmine; i += U) {
+    u32x4 wf[U][4];
+    u32x4 xf[U][MT][4];
+    uint32_t bits[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int bu = wv + NW * min(i + u, nmine - 1);
+      const int kc = min((bu << 7) + (g << 5), d_in - 32);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        wf[u][q] = ld128(wrow + kc + 8 * q);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) xf[u][t][q] = ld128(xrow[t] + kc + 8 * q);
+      }
+      bits[u] = ld32(brow + (kc >> 5));
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (i + u >= nmine) continue;  // uniform
+      const int bu = wv + NW * (i + u);
+      if (half_tail && bu == nblk - 1 && (bu << 7) + (g << 5) >= d_in) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xf[u][t][q] = u32x4{0u, 0u, 0u, 0u};
+      }
+      uint32_t s[16];
+      sign_pairs(bits[u], s);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          accw[t] = mfma16(xf[u][t][q], wf[u][q], accw[t]);
+          accs[t] = mfma16(xf[u][t][q], quad(s, q), accs[t]);
+        }
+      }
+    }
+  }
+
+  const float* alpha = a.alpha[0];
+  const int per_row = a.per_row;
+  reduce_and_store<MT, NW>(red, accw, accs, row0, M, a.d_out, a.y,
+                           [&](int slot, int o, float sw, float ss, int& m) {
+                             m = slot;
+                             return sw + (per_row ? alpha[o] : alpha[0]) * ss;
+                           });
+}
+
+// ---------------------------------------------------------------- mixed batch
 // Grouping of a mixed batch by variant, built once per workgroup in LDS.
 // Tokens are ordered by variant id (stable); slot s of the sorted order holds
 // token perm[s] of variant slotv[s] (-1 base only, -2 invalid id).  A "pair"
-// is a maximal run of slots of one variant inside one 16-token tile.
+// is a maximal run of slots of one variant inside one 16-token tile; dv[]
+// lists the distinct variants present and [dp0, dp1) their pairs.
 struct Groups {
   int perm[kMaxSkinnyTokens];
   int slotv[kMaxSkinnyTokens];
-  int pv[kMaxSkinnyTokens];
   int pt[kMaxSkinnyTokens];
   int plo[kMaxSkinnyTokens];
   int phi[kMaxSkinnyTokens];
   int key[kMaxSkinnyTokens];
-  int dv[kMaxSkinnyTokens];   // distinct variants present, ascending
-  int dp0[kMaxSkinnyTokens];  // first pair of each distinct variant
-  int dp1[kMaxSkinnyTokens];  // one past its last pair
+  int dv[kMaxSkinnyTokens];
+  int dp0[kMaxSkinnyTokens];
+  int dp1[kMaxSkinnyTokens];
   int np;
   int nd;
 };
@@ -102,7 +232,6 @@ __device__ void build_groups(Groups& G, const int32_t* ids, int M, int n_variant
       }
       int end = t + 1;
       while (end < M && end % 16 != 0 && G.slotv[end] == v) ++end;
-      G.pv[idx] = v;
       G.pt[idx] = t / 16;
       G.plo[idx] = t % 16;
       G.phi[idx] = end - (t / 16) * 16;
@@ -130,29 +259,48 @@ __device__ void build_groups(Groups& G, const int32_t* ids, int M, int n_variant
   __syncthreads();
 }
 
-template <int MT, int NW, int U, bool kMulti>
-__global__ __launch_bounds__(NW * kWave) void linear_skinny_kernel(const SkinnyArgs a) {
-  __shared__ float red[NW * MT * 2 * 4 * kWave];
+// The base product runs once for all tokens; the sign product once per
+// distinct variant present, with the x tile masked to that variant's tokens.
+// Each wave stages its x block in LDS next to a zero row: a variant's masked
+// tile is read by choosing, per lane, its token row or the zero row (one
+// address select instead of a select per register).  The distinct variants
+// are taken one at a time, the next one's sign words already requested.
+//
+// RT row tiles share a workgroup: its NW waves are RT row tiles x NW/RT
+// K-lanes, and the RT waves of one K-lane work on the same block at the same
+// time, so their x loads are the same addresses and all but one hit in L1.
+// With M = 32 the x bytes of a block are twice its weight bytes, so this
+// cuts the L2 traffic of the kernel by about a third for RT = 2.
+template <int MT, int NW, int RT>
+__global__ __launch_bounds__(NW * kWave) void linear_multi_kernel(const SkinnyArgs a) {
+  constexpr int KL = NW / RT;                  // K-lanes (waves per row tile)
+  constexpr int kRedBytes = NW * MT * 2 * 4 * kWave * 4;
+  constexpr int kXRow = 128 + 8;               // bf16 per staged row (padded)
+  constexpr int kXRows = MT * 16 + 1;          // token rows + zero row
+  constexpr int kXWave = kXRows * kXRow;       // bf16 per wave
+  constexpr int kXBytes = NW * kXWave * 2;
+  __shared__ __attribute__((aligned(16))) char smem[kRedBytes > kXBytes ? kRedBytes : kXBytes];
   __shared__ Groups G;
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x >> 6;
+  const int rt = wv % RT;
+  const int kl = wv / RT;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int row0 = blockIdx.x * 16;
+  const int row0 = (blockIdx.x * RT + rt) * 16;
   const int d_in = a.d_in;
   const int M = a.M;
   const int row = min(row0 + n, a.d_out - 1);
+  uint16_t* xst = reinterpret_cast<uint16_t*>(smem) + wv * kXWave;
 
-  if (kMulti) build_groups(G, a.ids, M, a.n_variants);
+  build_groups(G, a.ids, M, a.n_variants);
+  for (int e = lane; e < kXRow / 2; e += kWave)
+    reinterpret_cast<uint32_t*>(xst + MT * 16 * kXRow)[e] = 0u;
 
   const uint16_t* xrow[MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int slot = min(16 * t + n, M - 1);
-    const int tok = kMulti ? G.perm[slot] : slot;
-    xrow[t] = a.x + (size_t)tok * d_in;
-  }
+  for (int t = 0; t < MT; ++t) xrow[t] = a.x + (size_t)G.perm[min(16 * t + n, M - 1)] * d_in;
   const uint16_t* wrow = a.w + (size_t)row * d_in;
   const size_t brow = (size_t)row * (d_in >> 5);
 
@@ -164,111 +312,77 @@ __global__ __launch_bounds__(NW * kWave) void linear_skinny_kernel(const SkinnyA
   }
 
   const int nblk = (d_in + 127) >> 7;
-  const int b0 = (wv * nblk) / NW;
-  const int b1 = ((wv + 1) * nblk) / NW;
-  const int nd = kMulti ? G.nd : 0;
-
-  // Groups of U blocks: every load of a group is issued before the first
-  // MFMA that needs it, so each wave keeps U blocks of weights in flight.
-  // Loads are never predicated (a lane-dependent load would force a wait on
-  // the register it shares with the zero fill): a block past the wave's
-  // range re-reads the last valid block and is skipped, and the lanes of a
-  // final 64-wide block that fall past d_in re-read valid data whose x is
-  // then zeroed.
+  const int nmine = blocks_of_wave(kl, nblk, KL);
   const bool half_tail = (d_in & 127) != 0;
-  for (int b = b0; b < b1; b += U) {
-    u32x4 wf[U][4];
-    u32x4 xf[U][MT][4];
-    uint32_t bits[U];
-    size_t boff[U];
+  const int nd = G.nd;
+
+  for (int i = 0; i < nmine; ++i) {
+    const int bu = kl + KL * i;
+    const int kc = min((bu << 7) + (g << 5), d_in - 32);
+    u32x4 wf[4];
+    u32x4 xf[MT][4];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int bu = min(b + u, b1 - 1);
-      const int kc = min((bu << 7) + (g << 5), d_in - 32);
-      boff[u] = brow + (kc >> 5);
+    for (int q = 0; q < 4; ++q) {
+      wf[q] = ld128(wrow + kc + 8 * q);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        wf[u][q] = ld128(wrow + kc + 8 * q);
+      for (int t = 0; t < MT; ++t) xf[t][q] = ld128(xrow[t] + kc + 8 * q);
+    }
+    // first variant's sign words go out with the block's weights
+    uint32_t nxt = 0u;
+    if (nd > 0) {
+      const int v0 = __builtin_amdgcn_readfirstlane(G.dv[0]);
+      nxt = ld32(a.packed[v0] + brow + (kc >> 5));
+    }
+    if (half_tail && bu == nblk - 1 && (bu << 7) + (g << 5) >= d_in) {
 #pragma unroll
-        for (int t = 0; t < MT; ++t) xf[u][t][q] = ld128(xrow[t] + kc + 8 * q);
-      }
-      if (!kMulti) bits[u] = ld32(a.packed[0] + boff[u]);
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xf[t][q] = u32x4{0u, 0u, 0u, 0u};
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      if (half_tail && b + u == nblk - 1 && ((b + u) << 7) + (g << 5) >= d_in) {
+    for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<u32x4*>(xst + (16 * t + n) * kXRow + 32 * g + 8 * q) = xf[t][q];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) xf[u][t][q] = u32x4{0u, 0u, 0u, 0u};
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) accw[t] = mfma16(xf[t][q], wf[q], accw[t]);
+
+    for (int d = 0; d < nd; ++d) {
+      const uint32_t cur = nxt;
+      if (d + 1 < nd) {
+        const int vn = __builtin_amdgcn_readfirstlane(G.dv[d + 1]);
+        nxt = ld32(a.packed[vn] + brow + (kc >> 5));
       }
-    }
-    if (!kMulti) {
+      const int p0 = __builtin_amdgcn_readfirstlane(G.dp0[d]);
+      const int p1 = __builtin_amdgcn_readfirstlane(G.dp1[d]);
+      uint32_t s[16];
+      sign_pairs(cur, s);
+      for (int p = p0; p < p1; ++p) {
+        const int tp = __builtin_amdgcn_readfirstlane(G.pt[p]);
+        const int lo = __builtin_amdgcn_readfirstlane(G.plo[p]);
+        const int hi = __builtin_amdgcn_readfirstlane(G.phi[p]);
+        const bool keep = (unsigned)(n - lo) < (unsigned)(hi - lo);
+        const uint16_t* src = xst + (keep ? 16 * tp + n : MT * 16) * kXRow + 32 * g;
+        u32x4 xm[4];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (b + u >= b1) continue;  // uniform
-        uint32_t s[16];
-        sign_pairs(bits[u], s);
+        for (int q = 0; q < 4; ++q) xm[q] = *reinterpret_cast<const u32x4*>(src + 8 * q);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int t = 0; t < MT; ++t) {
+          if (t == tp) {
 #pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            accw[t] = mfma16(xf[u][t][q], wf[u][q], accw[t]);
-            accs[t] = mfma16(xf[u][t][q], quad(s, q), accs[t]);
-          }
-        }
-      }
-    } else {
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        if (b + u >= b1) continue;  // uniform
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int t = 0; t < MT; ++t) accw[t] = mfma16(xf[u][t][q], wf[u][q], accw[t]);
-      }
-      // One distinct variant at a time; its sign words for the U blocks are
-      // fetched while the previous variant's MFMAs run.
-      uint32_t nxt[U];
-      if (nd > 0) {
-        const int v0 = __builtin_amdgcn_readfirstlane(G.dv[0]);
-#pragma unroll
-        for (int u = 0; u < U; ++u) nxt[u] = ld32(a.packed[v0] + boff[u]);
-      }
-      for (int d = 0; d < nd; ++d) {
-        uint32_t cur[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-        if (d + 1 < nd) {
-          const int vn = __builtin_amdgcn_readfirstlane(G.dv[d + 1]);
-#pragma unroll
-          for (int u = 0; u < U; ++u) nxt[u] = ld32(a.packed[vn] + boff[u]);
-        }
-        const int p0 = __builtin_amdgcn_readfirstlane(G.dp0[d]);
-        const int p1 = __builtin_amdgcn_readfirstlane(G.dp1[d]);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          if (b + u >= b1) continue;  // uniform
-          uint32_t s[16];
-          sign_pairs(cur[u], s);
-          for (int p = p0; p < p1; ++p) {
-            const int tp = __builtin_amdgcn_readfirstlane(G.pt[p]);
-            const bool keep = n >= G.plo[p] && n < G.phi[p];
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-              if (t == tp) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                  accs[t] = mfma16(masked(xf[u][t][q], keep), quad(s, q), accs[t]);
-              }
-            }
+            for (int q = 0; q < 4; ++q) accs[t] = mfma16(xm[q], quad(s, q), accs[t]);
           }
         }
       }
     }
   }
 
-  // Partial sums of the NW waves -> LDS, then a fixed-order sum per output.
+  // The LDS region may still hold other waves' staged x: barrier first.
+  __syncthreads();
+  // Partial sums: wave (rt, kl) -> its row tile's K-lane kl.
+  float* red = reinterpret_cast<float*>(smem);
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
 #pragma unroll
@@ -278,70 +392,74 @@ __global__ __launch_bounds__(NW * kWave) void linear_skinny_kernel(const SkinnyA
     }
   }
   __syncthreads();
-
-  for (int idx = threadIdx.x; idx < MT * 4 * kWave; idx += NW * kWave) {
+  const int per_row = a.per_row;
+  for (int idx = threadIdx.x; idx < RT * MT * 4 * kWave; idx += NW * kWave) {
     const int l = idx & (kWave - 1);
     const int v = (idx >> 6) & 3;
-    const int t = idx >> 8;
+    const int t = (idx >> 8) % MT;
+    const int r = (idx >> 8) / MT;
     float sw = 0.f, ss = 0.f;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
+    for (int k = 0; k < KL; ++k) {
+      const int w = k * RT + r;
       sw += red[(((w * MT + t) * 2 + 0) * 4 + v) * kWave + l];
       ss += red[(((w * MT + t) * 2 + 1) * 4 + v) * kWave + l];
     }
     // MFMA 16x16 output layout: lane l holds rows 4*(l/16)+v of column l%16.
     const int slot = 16 * t + 4 * (l >> 4) + v;
-    const int o = row0 + (l & 15);
+    const int o = (blockIdx.x * RT + r) * 16 + (l & 15);
     if (slot < M && o < a.d_out) {
+      const int m = G.perm[slot];
+      const int vv = G.slotv[slot];
       float yv;
-      int m;
-      if (!kMulti) {
-        m = slot;
-        const float al = a.per_row ? a.alpha[0][o] : a.alpha[0][0];
-        yv = sw + al * ss;
+      if (vv >= 0) {
+        const float* ap = a.alpha[vv];
+        yv = sw + (per_row ? ap[o] : ap[0]) * ss;
       } else {
-        m = G.perm[slot];
-        const int vv = G.slotv[slot];
-        if (vv >= 0) {
-          const float* ap = a.alpha[vv];
-          const float al = a.per_row ? ap[o] : ap[0];
-          yv = sw + al * ss;
-        } else if (vv == -1) {
-          yv = sw;
-        } else {
-          yv = __builtin_nanf("");
-        }
+        yv = vv == -1 ? sw : __builtin_nanf("");
       }
       a.y[(size_t)m * a.d_out + o] = f32_to_bf16_bits(yv);
     }
   }
 }
 
-template <int MT, bool kMulti>
-hipError_t launch_mt(const SkinnyArgs& a, hipStream_t stream) {
-  constexpr int NW = 8;
-  constexpr int U = MT >= 4 ? 1 : (kMulti ? 4 / (2 * MT) : 4 / MT);
-  const dim3 grid((a.d_out + 15) / 16);
-  hipLaunchKernelGGL((linear_skinny_kernel<MT, NW, U, kMulti>), grid, dim3(NW * kWave), 0, stream,
-                     a);
+// ---------------------------------------------------------------- launchers
+constexpr int kNW = 8;
+
+template <int MT>
+hipError_t launch_decode(const SkinnyArgs& a, hipStream_t stream) {
+  constexpr int U = MT >= 4 ? 1 : 4 / MT;
+  hipLaunchKernelGGL((linear_decode_kernel<MT, kNW, U>), dim3((a.d_out + 15) / 16),
+                     dim3(kNW * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
-template <bool kMulti>
-hipError_t launch_any(const SkinnyArgs& a, hipStream_t stream) {
-  if (a.M <= 16) return launch_mt<1, kMulti>(a, stream);
-  if (a.M <= 32) return launch_mt<2, kMulti>(a, stream);
-  return launch_mt<4, kMulti>(a, stream);
+template <int MT, int RT>
+hipError_t launch_multi_rt(const SkinnyArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((linear_multi_kernel<MT, kNW, RT>), dim3((a.d_out + 16 * RT - 1) / (16 * RT)),
+                     dim3(kNW * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int MT>
+hipError_t launch_multi(const SkinnyArgs& a, hipStream_t stream) {
+  // One row tile per workgroup: measured on the 70B-shaped gate matrix
+  // (M = 32, 14 variants), two row tiles sharing x through L1 were 6% slower.
+  return launch_multi_rt<MT, 1>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_linear_skinny(const SkinnyArgs& a, hipStream_t stream) {
-  return launch_any<false>(a, stream);
+  if (a.M <= 16) return launch_decode<1>(a, stream);
+  if (a.M <= 32) return launch_decode<2>(a, stream);
+  return launch_decode<4>(a, stream);
 }
 
 hipError_t launch_linear_multi(const SkinnyArgs& a, hipStream_t stream) {
-  return launch_any<true>(a, stream);
+  if (a.M <= 16) return launch_multi<1>(a, stream);
+  if (a.M <= 32) return launch_multi<2>(a, stream);
+  return launch_multi<4>(a, stream);
 }
 
 }  // namespace bd
