@@ -114,7 +114,8 @@ int bitdelta_compress(const uint16_t* w_ft, const uint16_t* w_base, int64_t d_ou
  * rounded to bf16 (nearest even).  M <= 64 runs the decode-shaped kernel
  * (base and sign products on the matrix cores, one pass over W_base and the
  * packed signs); larger M runs the prefill GEMM, which rebuilds bf16 tiles of
- * W_eff in LDS.
+ * W_eff in LDS; its 32-bit buffer offsets limit it to d_in <= 4194240
+ * (BITDELTA_ERR_SHAPE beyond that when M > 64).
  *
  *   x       device, bf16 [M, d_in]
  *   w_base  device, bf16 [d_out, d_in]

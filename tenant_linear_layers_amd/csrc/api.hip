@@ -113,7 +113,7 @@ BD_EXPORT int bitdelta_linear(const uint16_t* x, int64_t M, const uint16_t* w_ba
                               int64_t d_out, int64_t d_in, uint16_t* y, void* stream) {
   if (!x || !w_base || !packed || !alpha || !y) return BITDELTA_ERR_NULL;
   if (!shape_ok(d_out, d_in) || M < 1 || M > kInt32Max || M * d_in >= kMaxElems ||
-      M * d_out >= kMaxElems)
+      M * d_out >= kMaxElems || (M > bd::kMaxSkinnyTokens && d_in > bd::kPrefillMaxDin))
     return BITDELTA_ERR_SHAPE;
   if (alpha_mode != BITDELTA_ALPHA_PER_MATRIX && alpha_mode != BITDELTA_ALPHA_PER_ROW)
     return BITDELTA_ERR_MODE;

@@ -8,6 +8,10 @@ namespace bd {
 
 constexpr int kMaxVariants = 64;   // equals BITDELTA_MAX_VARIANTS
 constexpr int kMaxSkinnyTokens = 64;
+// The prefill GEMM addresses one tile's rows of W_base (up to 256 rows) with
+// 32-bit buffer offsets: 256 * d_in * 2 bytes must stay below 2^31.
+constexpr int64_t kPrefillMaxTileBytes = 2147483647;
+constexpr int64_t kPrefillMaxDin = kPrefillMaxTileBytes / (256 * 2) / 64 * 64;
 
 // Compression of one matrix.  per_row != 0: alpha[d_out]; otherwise alpha[1]
 // and `partial` holds 2*d_out uint64 of scratch.

@@ -6,12 +6,18 @@
 // is formed in fast on-chip memory (here LDS) inside the matmul kernel and
 // never written to HBM.
 //
-// Tile: 256 tokens x BN output rows x 64 of d_in per step, WM x WN waves,
-// each owning (256/WM) x (BN/WN) outputs in MFMA 32x32x16 tiles (float32
-// accumulators in the accumulation registers).  Per step every thread loads
-// its share of 16-byte pieces of x and of W_base plus the sign byte of each
-// W piece, rebuilds those weights as bf16(W_base + alpha*s) and stores both
-// tiles into the second of two LDS buffers while the MFMAs read the first.
+// Tile: 256 tokens x BN output rows x 64 of d_in per step, 8 waves as 4 x 2,
+// each owning 64 x (BN/2) outputs in MFMA 32x32x16 tiles (float32
+// accumulators).  Two LDS stages: while the MFMAs read one, the other is
+// filled for the next step.
+//  * x goes from global memory straight into LDS (global_load_lds, 16 bytes
+//    per lane, no registers): each wave instruction writes one 8-row block of
+//    1 KB; chunk c of row r sits at position c ^ (r % 8) of its 128-byte row
+//    and consecutive blocks are 1152 bytes apart, so the MFMA operand reads
+//    (32 rows at one chunk) hit distinct banks.
+//  * W_base and the sign bytes are buffer loads into registers; each thread
+//    rebuilds its 4 x 8 weights as bf16(W_base + alpha*s) and stores them to
+//    the weight stage (rows padded to 144 bytes).
 // W_eff is rounded to bf16 once per element, the MFMA accumulates in float32
 // and y is rounded to bf16.
 #include "common.h"
@@ -22,10 +28,23 @@ namespace {
 
 constexpr int BM = 256;
 constexpr int BK = 64;
-constexpr int LDK = BK + 8;  // LDS row pitch in bf16 (144 bytes) against bank conflicts
+constexpr int ABLK = 1152;          // bytes per 8-row block of the x stage (1 KB + 128 B skew)
+constexpr int A_STAGE = 32 * ABLK;  // 256 rows
+constexpr int LDK = BK + 8;         // weight stage row pitch in bf16 (144 bytes)
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (lo in bits 0..15), round to nearest even, one
+// instruction.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
 
 // Eight weights of one row: bf16(W_base + alpha*s), s from the sign byte
-// (bit j = element j, 1 = +1).  The sign of alpha is flipped by xor for -1.
+// (bit j = element j, 1 = +1).  The sign of alpha is flipped by xor for -1:
+// bitop3 table 0x78 is a ^ (b & c).
 __device__ __forceinline__ u32x4 rebuild8(u32x4 w, uint32_t byte, uint32_t ab) {
   const uint32_t nb = ~byte;
   u32x4 out;
@@ -33,11 +52,33 @@ __device__ __forceinline__ u32x4 rebuild8(u32x4 w, uint32_t byte, uint32_t ab) {
   for (int d = 0; d < 4; ++d) {
     const float lo = __uint_as_float(w[d] << 16);
     const float hi = __uint_as_float(w[d] & 0xFFFF0000u);
-    const float slo = __uint_as_float(ab ^ ((nb << (31 - 2 * d)) & 0x80000000u));
-    const float shi = __uint_as_float(ab ^ ((nb << (30 - 2 * d)) & 0x80000000u));
-    out[d] = pack_bf16x2(lo + slo, hi + shi);
+    const float slo =
+        __uint_as_float(__builtin_amdgcn_bitop3_b32(ab, nb << (31 - 2 * d), 0x80000000u, 0x78));
+    const float shi =
+        __uint_as_float(__builtin_amdgcn_bitop3_b32(ab, nb << (30 - 2 * d), 0x80000000u, 0x78));
+    out[d] = cvt_pk_bf16(lo + slo, hi + shi);
   }
   return out;
+}
+
+// Buffer loads through a resource spanning [base, base + nbytes): offsets
+// past the end read as zero.
+__device__ __forceinline__ u32x4 bload128(const void* base, int nbytes, int voff, int soff) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+__device__ __forceinline__ uint32_t bload8(const void* base, int nbytes, int voff, int soff) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
+// at lds + 16*i (lds must be the same for the whole wave).
+__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
 }
 
 template <int BN, int WM, int WN>
@@ -45,15 +86,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
     const uint16_t* __restrict__ x, int M, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ bits8, const float* __restrict__ alpha, int per_row, int d_out,
     int d_in, uint16_t* __restrict__ y, int ntm, int ntn, int chunk) {
-  constexpr int NT = 64 * WM * WN;     // threads
-  constexpr int RS = NT / 8;           // rows covered by one pass of 16-byte loads
-  constexpr int NA = BM / RS;          // x pieces per thread per step
-  constexpr int NB = BN / RS;          // W pieces per thread per step
-  constexpr int TMW = BM / WM / 32;    // 32-row MFMA tiles per wave
-  constexpr int TNW = BN / WN / 32;    // 32-column MFMA tiles per wave
-  static_assert(NA >= 1 && NB >= 1 && TMW >= 1 && TNW >= 1, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDK];
+  constexpr int NT = 64 * WM * WN;   // threads
+  constexpr int RS = NT / 8;         // weight rows covered by one pass of 16-byte loads
+  constexpr int NB = BN / RS;        // weight pieces per thread per step
+  constexpr int AI = 32 / (WM * WN); // 8-row x blocks per wave per step
+  constexpr int TMW = BM / WM / 32;  // 32-row MFMA tiles per wave
+  constexpr int TNW = BN / WN / 32;  // 32-column MFMA tiles per wave
+  static_assert(NB >= 1 && AI >= 1 && TMW >= 1 && TNW >= 1, "tile shape");
+  // Separate arrays per stage, so that the compiler sees that reads of one
+  // stage do not depend on the LDS loads into the other.
+  __shared__ __attribute__((aligned(16))) unsigned char As0[A_STAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char As1[A_STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs0[BN][LDK];
+  __shared__ __attribute__((aligned(16))) uint16_t Bs1[BN][LDK];
 
   // Workgroups are dealt round-robin to the 8 XCDs; give each XCD a
   // contiguous range of tiles, token tile fastest, so tiles that share the
@@ -70,42 +115,63 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
   const int wv = T >> 6;
   const int wm = wv % WM;
   const int wn = wv / WM;
-  const int lr = T >> 3;   // row within an RS-row slab
-  const int lc = T & 7;    // 16-byte chunk within the 64-wide step
+  const int lr = T >> 3;  // weight row within an RS-row slab
+  const int lc = T & 7;   // 16-byte chunk within the 64-wide step
+  const int r8 = lane >> 3;
+  const int pos = lane & 7;
 
-  const uint16_t* ap[NA];
+  // x: wave wv fills 8-row blocks wv*AI + b; lane (r8, pos) fetches chunk
+  // pos ^ r8 of row r8 of the block (rows past M re-read row M-1).
+  const uint16_t* xa[AI];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) ap[i] = x + (size_t)min(m0 + lr + RS * i, M - 1) * d_in + lc * 8;
-  const uint16_t* bp[NB];
-  const uint8_t* sp[NB];
+  for (int b = 0; b < AI; ++b) {
+    const int row = (wv * AI + b) * 8 + r8;
+    xa[b] = x + (size_t)min(m0 + row, M - 1) * d_in + 8 * (pos ^ r8);
+  }
+  // W_base and sign bytes of this tile's rows (rows past d_out read zero).
+  const int nrows = min(BN, d_out - n0);
+  const uint16_t* wbase = w + (size_t)n0 * d_in;
+  const int wbytes = nrows * d_in * 2;
+  const uint8_t* sbase = bits8 + (size_t)n0 * (d_in >> 3);
+  const int sbytes = nrows * (d_in >> 3);
+  int vw[NB], vs[NB];
   uint32_t ab[NB];
-  const size_t bytes_per_row = (size_t)(d_in >> 3);
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
-    const int r = min(n0 + lr + RS * i, d_out - 1);
-    bp[i] = w + (size_t)r * d_in + lc * 8;
-    sp[i] = bits8 + (size_t)r * bytes_per_row + lc;
-    ab[i] = __float_as_uint(per_row ? alpha[r] : alpha[0]);
+    const int r = lr + RS * i;
+    vw[i] = (r * d_in + lc * 8) * 2;
+    vs[i] = r * (d_in >> 3) + lc;
+    ab[i] = __float_as_uint(per_row ? alpha[min(n0 + r, d_out - 1)] : alpha[0]);
+  }
+  // LDS byte offsets of the x operand for tile i, 16-wide sub-step ks.
+  int aoff[TMW][4];
+#pragma unroll
+  for (int i = 0; i < TMW; ++i) {
+    const int r = wm * (BM / WM) + i * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int c = 2 * ks + (lane >> 5);
+      aoff[i][ks] = (r >> 3) * ABLK + (r & 7) * 128 + ((c ^ (r & 7)) << 4);
+    }
   }
 
-  u32x4 ra[NA], rb[NB];
+  u32x4 rb[NB];
   uint32_t rs[NB];
-  auto gload = [&](int kt) {
-    const int k = kt * BK;
+  auto xload = [&](int kt, unsigned char* as) {
 #pragma unroll
-    for (int i = 0; i < NA; ++i) ra[i] = ld128(ap[i] + k);
+    for (int b = 0; b < AI; ++b) lds_load16(xa[b] + kt * BK, as + (wv * AI + b) * ABLK);
+  };
+  auto wload = [&](int kt) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      rb[i] = ld128(bp[i] + k);
-      rs[i] = sp[i][k >> 3];
+      rb[i] = bload128(wbase, wbytes, vw[i], kt * BK * 2);
+      rs[i] = bload8(sbase, sbytes, vs[i], kt * (BK / 8));
     }
   };
-  auto sstore = [&](int st) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i) *reinterpret_cast<u32x4*>(&As[st][lr + RS * i][lc * 8]) = ra[i];
+  auto wstore = [&](uint16_t (*bs)[LDK]) {
 #pragma unroll
     for (int i = 0; i < NB; ++i)
-      *reinterpret_cast<u32x4*>(&Bs[st][lr + RS * i][lc * 8]) = rebuild8(rb[i], rs[i], ab[i]);
+      *reinterpret_cast<u32x4*>(&bs[lr + RS * i][lc * 8]) = rebuild8(rb[i], rs[i], ab[i]);
   };
 
   f32x16 acc[TMW][TNW];
@@ -116,32 +182,43 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  const int nk = d_in / BK;
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int st = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
+  // One step: prefetch step kt+1 into the other stage, multiply this stage,
+  // rebuild the prefetched weights into the other weight stage, then wait for
+  // everything (LDS loads included) and synchronise.
+  auto step = [&](int kt, int nk, const unsigned char* as, uint16_t (*bs)[LDK],
+                  unsigned char* as_next, uint16_t (*bs_next)[LDK]) {
+    if (kt + 1 < nk) {
+      xload(kt + 1, as_next);
+      wload(kt + 1);
+    }
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const int kk = ks * 16 + 8 * (lane >> 5);
       u32x4 af[TMW], bf[TNW];
 #pragma unroll
-      for (int i = 0; i < TMW; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(
-            &As[st][wm * (BM / WM) + i * 32 + (lane & 31)][kk]);
+      for (int i = 0; i < TMW; ++i) af[i] = *reinterpret_cast<const u32x4*>(as + aoff[i][ks]);
 #pragma unroll
       for (int j = 0; j < TNW; ++j)
         bf[j] = *reinterpret_cast<const u32x4*>(
-            &Bs[st][wn * (BN / WN) + j * 32 + (lane & 31)][kk]);
+            &bs[wn * (BN / WN) + j * 32 + (lane & 31)][ks * 16 + 8 * (lane >> 5)]);
 #pragma unroll
       for (int i = 0; i < TMW; ++i)
 #pragma unroll
         for (int j = 0; j < TNW; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
     }
-    if (kt + 1 < nk) sstore(st ^ 1);
+    if (kt + 1 < nk) wstore(bs_next);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+
+  const int nk = d_in / BK;
+  xload(0, As0);
+  wload(0);
+  wstore(Bs0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, nk, As0, Bs0, As1, Bs1);
+    if (kt + 1 < nk) step(kt + 1, nk, As1, Bs1, As0, Bs0);
   }
 
   // MFMA 32x32 output layout: lane l, element v holds row
@@ -164,6 +241,8 @@ template <int BN, int WM, int WN>
 hipError_t launch_cfg(const uint16_t* x, int M, const uint16_t* w, const uint8_t* packed_bytes,
                       const float* alpha, int per_row, int d_out, int d_in, uint16_t* y,
                       hipStream_t stream) {
+  // Buffer offsets are 32-bit: one tile's rows of W_base must span < 2 GiB.
+  if ((int64_t)BN * d_in * 2 > (int64_t)kPrefillMaxTileBytes) return hipErrorInvalidValue;
   const int ntm = (M + BM - 1) / BM;
   const int ntn = (d_out + BN - 1) / BN;
   const int tiles = ntm * ntn;

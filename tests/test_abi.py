@@ -98,6 +98,12 @@ def test_linear_argument_errors():
     assert _c(f(A, 4, B, C + 8, D, 1, 8, 64, E, None)) == 3
     assert _c(f(A, 4, B, C, D + 2, 1, 8, 64, E, None)) == 3      # alpha needs 4 bytes
     assert _c(f(A, 4, B, C, D, 1, 8, 64, A, None)) == 9          # y overlaps x
+    # The prefill path (M > 64) addresses a 256-row weight tile with 32-bit
+    # offsets: d_in above 4194240 is rejected there, but not for M <= 64.
+    big = 4194240 + 64
+    assert _c(f(A, 65, B, C, D, 1, 8, big, E, None)) == 2
+    assert _c(f(A, 65, B, C, D, 7, 8, 4194240, E, None)) == 4    # passes the shape check
+    assert _c(f(A, 64, B, C, D, 7, 8, big, E, None)) == 4
 
 
 def test_multi_argument_errors():
