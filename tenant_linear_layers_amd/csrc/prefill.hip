@@ -9,7 +9,9 @@
 // Tile: 256 tokens x BN output rows x 64 of d_in per step, 8 waves as 4 x 2,
 // each owning 64 x (BN/2) outputs in MFMA 32x32x16 tiles (float32
 // accumulators).  Two LDS stages: while the MFMAs read one, the other is
-// filled for the next step.
+// filled for the next step.  Raw weights are loaded two steps ahead into two
+// register sets, so the rebuild of step k+1 (from registers that have already
+// arrived) is spread over the four 16-wide MFMA sub-steps of step k.
 //  * x goes from global memory straight into LDS (global_load_lds, 16 bytes
 //    per lane, no registers): each wave instruction writes one 8-row block of
 //    1 KB; chunk c of row r sits at position c ^ (r % 8) of its 128-byte row
@@ -79,6 +81,15 @@ __device__ __forceinline__ uint32_t bload8(const void* base, int nbytes, int vof
 // at lds + 16*i (lds must be the same for the whole wave).
 __device__ __forceinline__ void lds_load16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// Workgroup barrier without a memory fence.  Callers first wait for their
+// own loads and LDS stores (s_waitcnt 0), which is what makes the LDS
+// contents visible; the memory clobber keeps the compiler from moving memory
+// accesses across the barrier.
+__device__ __forceinline__ void step_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("s_barrier" ::: "memory");
 }
 
 template <int BN, int WM, int WN>
@@ -155,23 +166,23 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
     }
   }
 
-  u32x4 rb[NB];
-  uint32_t rs[NB];
+  // Two register sets of raw weights: set (k+1)%2 holds step k+1 while step
+  // k runs; set k%2 receives step k+2.
+  u32x4 rb0[NB], rb1[NB];
+  uint32_t rs0[NB], rs1[NB];
   auto xload = [&](int kt, unsigned char* as) {
 #pragma unroll
     for (int b = 0; b < AI; ++b) lds_load16(xa[b] + kt * BK, as + (wv * AI + b) * ABLK);
   };
-  auto wload = [&](int kt) {
+  auto wload = [&](int kt, u32x4 (&rb)[NB], uint32_t (&rs)[NB]) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
       rb[i] = bload128(wbase, wbytes, vw[i], kt * BK * 2);
       rs[i] = bload8(sbase, sbytes, vs[i], kt * (BK / 8));
     }
   };
-  auto wstore = [&](uint16_t (*bs)[LDK]) {
-#pragma unroll
-    for (int i = 0; i < NB; ++i)
-      *reinterpret_cast<u32x4*>(&bs[lr + RS * i][lc * 8]) = rebuild8(rb[i], rs[i], ab[i]);
+  auto wpiece = [&](int i, uint16_t (*bs)[LDK], const u32x4 (&rb)[NB], const uint32_t (&rs)[NB]) {
+    *reinterpret_cast<u32x4*>(&bs[lr + RS * i][lc * 8]) = rebuild8(rb[i], rs[i], ab[i]);
   };
 
   f32x16 acc[TMW][TNW];
@@ -182,15 +193,19 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // One step: prefetch step kt+1 into the other stage, multiply this stage,
-  // rebuild the prefetched weights into the other weight stage, then wait for
-  // everything (LDS loads included) and synchronise.
+  // Step kt: stage kt%2 holds x and W_eff of step kt.  Prefetch x of step
+  // kt+1 into the other stage and raw W of step kt+2 into rb_load; multiply
+  // this stage while rebuilding W_eff of step kt+1 (rb_use) into the other
+  // weight stage.  Prefetches are unconditional: past the last step they
+  // re-read the last step (in bounds) into buffers nobody reads.
   auto step = [&](int kt, int nk, const unsigned char* as, uint16_t (*bs)[LDK],
-                  unsigned char* as_next, uint16_t (*bs_next)[LDK]) {
-    if (kt + 1 < nk) {
-      xload(kt + 1, as_next);
-      wload(kt + 1);
-    }
+                  unsigned char* as_next, uint16_t (*bs_next)[LDK], const u32x4 (&rb_use)[NB],
+                  const uint32_t (&rs_use)[NB], u32x4 (&rb_load)[NB], uint32_t (&rs_load)[NB]) {
+    xload(min(kt + 1, nk - 1), as_next);
+    wload(min(kt + 2, nk - 1), rb_load, rs_load);
+    // Keep the prefetches at the top of the step (the scheduler would sink
+    // them towards the barrier to save registers).
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       u32x4 af[TMW], bf[TNW];
@@ -204,22 +219,29 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
       for (int i = 0; i < TMW; ++i)
 #pragma unroll
         for (int j = 0; j < TNW; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if (i % 4 == ks) wpiece(i, bs_next, rb_use, rs_use);
     }
-    if (kt + 1 < nk) wstore(bs_next);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    step_barrier();
   };
 
   const int nk = d_in / BK;
   xload(0, As0);
-  wload(0);
-  wstore(Bs0);
+  wload(0, rb0, rs0);
+  wload(min(1, nk - 1), rb1, rs1);
   __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, nk, As0, Bs0, As1, Bs1);
-    if (kt + 1 < nk) step(kt + 1, nk, As1, Bs1, As0, Bs0);
+#pragma unroll
+  for (int i = 0; i < NB; ++i) wpiece(i, Bs0, rb0, rs0);
+  step_barrier();
+  // Steps in unconditional pairs (a conditional second step lets the
+  // compiler sink the first step's loads into it), then a last odd step.
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, nk, As0, Bs0, As1, Bs1, rb1, rs1, rb0, rs0);
+    step(kt + 1, nk, As1, Bs1, As0, Bs0, rb0, rs0, rb1, rs1);
   }
+  if (kt < nk) step(kt, nk, As0, Bs0, As1, Bs1, rb1, rs1, rb0, rs0);
 
   // MFMA 32x32 output layout: lane l, element v holds row
   // 8*(v/4) + 4*(l/32) + v%4 of column l%32.
@@ -257,10 +279,12 @@ hipError_t launch_cfg(const uint16_t* x, int M, const uint16_t* w, const uint8_t
 hipError_t launch_linear_prefill(const uint16_t* x, int M, const uint16_t* w,
                                  const uint8_t* packed_bytes, const float* alpha, int per_row,
                                  int d_out, int d_in, uint16_t* y, hipStream_t stream) {
-  // 8 waves (two per SIMD, so one wave's MFMAs overlap the other's weight
-  // rebuild), 256-wide weight tiles when they give at least one tile per CU.
+  // 8 waves, two per SIMD.  256-wide weight tiles unless their last round
+  // over the 256 CUs would leave more than a quarter of the chip idle; then
+  // 128-wide tiles (twice as many, each about 55% of the time).
   const long tiles256 = (long)((M + BM - 1) / BM) * ((d_out + 255) / 256);
-  if (tiles256 >= 256)
+  const long rounds256 = (tiles256 + 255) / 256;
+  if (4 * tiles256 >= 3 * 256 * rounds256)
     return launch_cfg<256, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, stream);
   return launch_cfg<128, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, stream);
 }
