@@ -20,6 +20,20 @@ duration of each kernel, which is what value and the rooflines use.  The line
 printed reports decode effective HBM GB/s (algorithmic bytes / kernel time)
 as `value`, the prefill TFLOP/s beside it, a roofline entry per kernel, and
 the CPU oracle timed on a bounded sample of the same workload.
+
+Counter runs (HBM traffic per launch, rocprofv3 FETCH_SIZE and WRITE_SIZE in
+two separate runs):
+
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT_F -o run -- python bench.py --counter-pass
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT_W -o run -- python bench.py --counter-pass
+    python bench.py --summarize-counters OUT_F OUT_W
+
+`--counter-pass` launches each kernel of the proj_4096 step eagerly, in a fixed
+order, on distinct rotation copies, then a plain elementwise kernel that reads
+and writes a known 256 MiB (the calibration: the counters read a fixed fraction
+of the true bytes).  `--summarize-counters` scales the per-dispatch counters by
+that calibration and writes profiles/<kernel>_proj_4096_pmc.json (with a digest
+of the kernel's sources: a later change of the kernel voids the figure).
 """
 
 from __future__ import annotations
@@ -156,6 +170,24 @@ class ProjWorkload:
         self.c_out = [(torch.empty_like(packed), torch.empty_like(alpha)) for _ in range(2)]
         self.host = dict(wb=wb, wf=wf, xs=xs, more=more, x_multi=x_multi, ids=ids)
         self.k = 0
+
+    @staticmethod
+    def static_bytes():
+        """Algorithmic bytes per launch of each kernel of the step, from the
+        workload's shapes and seeded variant ids alone (no GPU needed)."""
+        wl = S.WORKLOADS["proj_4096"]
+        ids = S.zipf_ids(ProjWorkload.multi_m, ProjWorkload.n_variants, wl.seed)
+        shell = ProjWorkload.__new__(ProjWorkload)
+        shell.d_out = shell.d_in = 4096
+        shell.mode = wl.alpha_mode
+        shell.distinct = int(len(set(ids.tolist())))
+        n = 4096 * 4096
+        pm = ProjWorkload.prefill_m
+        out = {"compress": shell.compress_bytes(), "multi": shell.multi_bytes(),
+               "prefill": 2 * n + n // 8 + 4 * 4096 + 2 * pm * 4096 * 2}
+        for m in wl.tokens:
+            out[f"decode_m{m}"] = shell.decode_bytes(m)
+        return out
 
     # algorithmic bytes / flops per launch
     def decode_bytes(self, m):
@@ -322,7 +354,7 @@ def cpu_baseline(w: ProjWorkload, budget_s: float):
             nbytes += w.decode_bytes(m)
         t_dec += time.perf_counter() - t0
         passes += 1
-        if t_dec + t_comp > budget_s or passes >= 20:
+        if t_dec + t_comp > budget_s or passes >= 200:
             break
     return {
         "value": round(nbytes / t_dec / 1e9, 4),
@@ -334,6 +366,106 @@ def cpu_baseline(w: ProjWorkload, budget_s: float):
                    f"same matrix {t_comp:.1f} s ({w.compress_bytes() / t_comp / 1e9:.3f} GB/s)"),
         "host_cores_available": len(os.sched_getaffinity(0)),
     }
+
+
+# ------------------------------------------------------------------ counters
+COUNTER_BLOCKS = ("compress", "decode_m1", "decode_m4", "decode_m16", "multi", "prefill")
+CALIB_BYTES = 256 * 2**20
+LIB_KERNELS = ("compress_rows_kernel", "compress_finalize_kernel", "linear_decode_kernel",
+               "linear_multi_kernel", "prefill_kernel")
+
+
+def counter_pass(w: ProjWorkload, n: int):
+    """n eager launches of each kernel of the step, block by block, each on its
+    own rotation copy; then n launches of the calibration kernel."""
+    run = {"compress": w.run_compress, "multi": w.run_multi, "prefill": w.run_prefill}
+    for m in w.decode_ms:
+        run[f"decode_m{m}"] = lambda r, m=m: w.run_decode(m, r)
+    for name in COUNTER_BLOCKS:
+        for r in range(n):
+            run[name](r)
+        torch.cuda.synchronize()
+    src = torch.zeros(CALIB_BYTES // 2, dtype=torch.bfloat16, device=w.dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(n):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+
+
+def _counter_rows(d: str, counter: str):
+    import csv
+    rows = []
+    for dirpath, _, files in os.walk(d):
+        for f in files:
+            if f.endswith("counter_collection.csv"):
+                for r in csv.DictReader(open(os.path.join(dirpath, f))):
+                    if r["Counter_Name"] == counter:
+                        rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
+                                     float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, n: int, w_bytes: dict):
+    """Per-launch HBM bytes of each kernel from the two counter runs."""
+    out = {}
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _counter_rows(d, counter)
+        lib = [r for r in rows if any(k in r[1] for k in LIB_KERNELS)]
+        lib = lib[-n * len(COUNTER_BLOCKS):]
+        calib = [r for r in rows if r[0] > lib[-1][0]][-n:]
+        if len(lib) != n * len(COUNTER_BLOCKS) or len(calib) != n:
+            raise SystemExit(f"{counter}: expected {n} launches per block, found "
+                             f"{len(lib)} library and {len(calib)} calibration dispatches")
+        factor = CALIB_BYTES / (1024.0 * sum(v for _, _, v in calib) / n)
+        per[counter] = {"factor": factor, "calib_kernel": calib[0][1][:80]}
+        for b, name in enumerate(COUNTER_BLOCKS):
+            vals = [v for _, _, v in lib[b * n:(b + 1) * n]]
+            out.setdefault(name, {})[counter] = sum(vals) / n
+    res = {}
+    for name, c in out.items():
+        hbm = (c["FETCH_SIZE"] * 1024 * per["FETCH_SIZE"]["factor"]
+               + c["WRITE_SIZE"] * 1024 * per["WRITE_SIZE"]["factor"])
+        res[name] = {"fetch_kib": round(c["FETCH_SIZE"], 1), "write_kib": round(c["WRITE_SIZE"], 1),
+                     "hbm_bytes": round(hbm), "algorithmic_bytes": w_bytes[name]}
+    return res, per
+
+
+def write_counter_profiles(res, per, n):
+    cmd = ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT_F -o run -- python -u "
+           f"bench.py --counter-pass --counter-launches {n}; the same with WRITE_SIZE into OUT_W; "
+           f"python bench.py --summarize-counters OUT_F OUT_W --counter-launches {n}")
+    groups = {"decode": ["decode_m1", "decode_m4", "decode_m16"], "compress": ["compress"],
+              "multi": ["multi"], "prefill": ["prefill"]}
+    for kernel, labels in groups.items():
+        rec = {"kernel": kernel, "workload": "proj_4096",
+               "sources_digest": sources_digest(KERNEL_SOURCES[kernel]),
+               "hbm_bytes_per_launch": sum(res[l]["hbm_bytes"] for l in labels),
+               "algorithmic_bytes_per_launch": sum(res[l]["algorithmic_bytes"] for l in labels),
+               "launches": {l: res[l] for l in labels},
+               "calibration": {k: {"factor": round(v["factor"], 4), "kernel": v["calib_kernel"],
+                                   "bytes": CALIB_BYTES} for k, v in per.items()},
+               "unit_note": ("one launch of each decode token count (M = 1, 4, 16), as the decode "
+                             "roofline's unit" if kernel == "decode" else "one launch"),
+               "command": cmd}
+        with open(os.path.join(PROFILES, f"{kernel}_proj_4096_pmc.json"), "w") as f:
+            json.dump(rec, f, indent=1)
+            f.write("\n")
+    lines = ["# HBM traffic per launch from rocprofv3 counters: bench.py, workload proj_4096", "",
+             "Commands (on one MI355X, from the repository root):", "", "    " + cmd, "",
+             "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by the ratio of true bytes "
+             "to counter bytes measured on a plain elementwise kernel reading and writing 256 MiB "
+             f"(FETCH x{per['FETCH_SIZE']['factor']:.3f}, WRITE x{per['WRITE_SIZE']['factor']:.3f}). "
+             f"Averages over {n} launches, each on its own weight copy.", "",
+             "| Launch | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes (scaled) | Algorithmic bytes "
+             "| Ratio |", "|---|---|---|---|---|---|"]
+    for l, r in res.items():
+        lines.append(f"| {l} | {r['fetch_kib']:.0f} | {r['write_kib']:.0f} | {r['hbm_bytes']:,} | "
+                     f"{r['algorithmic_bytes']:,} | {r['hbm_bytes'] / r['algorithmic_bytes']:.3f} |")
+    with open(os.path.join(PROFILES, "counters_proj_4096.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
 
 
 def roofline_entry(bound, achieved, peak, unit, traffic=None):
@@ -350,12 +482,23 @@ def main():
                     choices=["proj_4096", "layer70b_prefill", "layer70b_multi"])
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="eager launches for a rocprofv3 --pmc run (proj_4096), then exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/*_proj_4096_pmc.json from two --pmc runs, then exit")
+    ap.add_argument("--counter-launches", type=int, default=8)
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the kernels shard by output rows, see DESIGN.md); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    if args.summarize_counters:
+        res, per = summarize_counters(*args.summarize_counters, args.counter_launches,
+                                      ProjWorkload.static_bytes())
+        write_counter_profiles(res, per, args.counter_launches)
+        print(json.dumps({"counters": res, "calibration": per}), flush=True)
+        return
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
@@ -365,6 +508,13 @@ def main():
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     w = ProjWorkload(dev) if args.workload == "proj_4096" else LayerWorkload(args.workload, dev)
     torch.cuda.synchronize()
+    if args.counter_pass:
+        if not isinstance(w, ProjWorkload):
+            raise SystemExit("--counter-pass covers the proj_4096 workload")
+        counter_pass(w, args.counter_launches)
+        print(f"[bench] counter pass done ({args.counter_launches} launches per kernel, "
+              f"D={w.distinct})", file=sys.stderr, flush=True)
+        return
     print(f"[bench] rotation copies R={w.R}, distinct variants in the mixed batch "
           f"D={w.distinct}", file=sys.stderr, flush=True)
 
