@@ -329,6 +329,64 @@ class LayerWorkload:
                 "roofline": roof, "layer_us": round(total_us, 2)}
 
 
+class StackWorkload(LayerWorkload):
+    """The 80-layer 70B-shaped stack resident on the GPU (137 GB of W_base and
+    14 packed variants, about 257 GB), mixed-variant decode of 64 tokens with a
+    Zipf(1.1) variant mix through every layer's five linears."""
+
+    def __init__(self, name, dev):
+        wl = S.WORKLOADS[name]
+        self.name, self.wl, self.dev = name, wl, dev
+        self.mode = wl.alpha_mode
+        self.kind = "multi"
+        self.m = wl.tokens[0]
+        g = S.generator(wl.seed, dev)
+        self.stack = S.draw_stack_bases(wl, g, dev)
+        scales = S.variant_scales(wl)
+        nm = len(wl.matrices)
+        self.packs = [[[None] * nm for _ in scales] for _ in range(wl.layers)]
+        self.alphas = [[[None] * nm for _ in scales] for _ in range(wl.layers)]
+        for l, v, i, wf in S.iter_stack_finetuned(self.stack, scales, g):
+            self.packs[l][v][i], self.alphas[l][v][i] = T.compress(wf, self.stack[l][i], self.mode)
+            del wf
+            if v == len(scales) - 1 and i == nm - 1 and l % 10 == 9:
+                print(f"[bench] layers 0..{l} drawn and compressed", file=sys.stderr, flush=True)
+        self.xs = S.draw_stack_inputs(wl, self.m, g, dev)
+        ids = S.zipf_ids(self.m, wl.n_variants, wl.seed)
+        self.ids = torch.from_numpy(ids).to(dev)
+        self.distinct = int(len(set(ids.tolist())))
+        self.ys = [torch.empty(self.m, d_out, dtype=torch.bfloat16, device=dev)
+                   for _, d_out, _ in wl.matrices]
+        self.R = 1
+
+    def run_li(self, l, i):
+        nv = len(self.packs[l])
+        T.linear_multi(self.xs[l][i], self.ids, self.stack[l][i],
+                       [self.packs[l][v][i] for v in range(nv)],
+                       [self.alphas[l][v][i] for v in range(nv)], self.mode, y=self.ys[i])
+
+    def one_pass(self, j):
+        for l in range(self.wl.layers):
+            for i in range(len(self.wl.matrices)):
+                self.run_li(l, i)
+
+    def ranges(self):
+        L = self.wl.layers
+        return {f"multi_{nm}": (L, lambda i=i: [self.run_li(l, i) for l in range(L)])
+                for i, (nm, _, _) in enumerate(self.wl.matrices)}
+
+    def report(self, avg_us, args):
+        rep = super().report(avg_us, args)
+        L = self.wl.layers
+        rep["layer_us"] = round(rep["layer_us"], 2)
+        rep["stack_ms"] = round(rep["layer_us"] * L / 1e3, 3)
+        rep["config"]["layers"] = L
+        rep["config"]["resident_bytes"] = sum(
+            t.numel() * t.element_size() for layer in self.stack for t in layer) + sum(
+            p.numel() * p.element_size() for layer in self.packs for vs in layer for p in vs)
+        return rep
+
+
 # ------------------------------------------------------------------ CPU oracle
 def cpu_baseline(w: ProjWorkload, budget_s: float):
     """The oracle, as it stands, on a bounded sample of the same workload:
@@ -479,7 +537,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="proj_4096",
-                    choices=["proj_4096", "layer70b_prefill", "layer70b_multi"])
+                    choices=["proj_4096", "layer70b_prefill", "layer70b_multi",
+                             "stack70b_multi"])
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
     ap.add_argument("--counter-pass", action="store_true",
@@ -506,7 +565,12 @@ def main():
     torch.cuda.set_device(dev)
     T.lib()
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
-    w = ProjWorkload(dev) if args.workload == "proj_4096" else LayerWorkload(args.workload, dev)
+    if args.workload == "proj_4096":
+        w = ProjWorkload(dev)
+    elif args.workload == "stack70b_multi":
+        w = StackWorkload(args.workload, dev)
+    else:
+        w = LayerWorkload(args.workload, dev)
     torch.cuda.synchronize()
     if args.counter_pass:
         if not isinstance(w, ProjWorkload):
@@ -566,6 +630,7 @@ def main():
                "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
                "dtype": "bf16", "data": "synthetic", "config": rep["config"],
                "per_matrix": rep["per_matrix"], "layer_us": rep["layer_us"],
+               **({"stack_ms": rep["stack_ms"]} if "stack_ms" in rep else {}),
                "roofline": rep["roofline"],
                "kernel_avg_us": {k: round(v, 3) for k, v in avg_us.items()},
                "cpu_baseline": None}

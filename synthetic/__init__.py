@@ -27,7 +27,10 @@ from .workloads import (  # noqa: F401
     draw_finetuned,
     draw_layer_bases,
     draw_layer_inputs,
+    draw_stack_bases,
+    draw_stack_inputs,
     iter_finetuned,
+    iter_stack_finetuned,
     generator,
     laplace_scales,
     small_pair,

@@ -157,3 +157,25 @@ def draw_layer_inputs(wl: Workload, m: int, gen: torch.Generator, device) -> lis
         x_down = draw_activations(m, 28672, gen, device)
         return [x_in, x_o, x_in, x_in, x_down]
     return [draw_activations(m, d_in, gen, device) for _, _, d_in in wl.matrices]
+
+
+# ----------------------------------------------------------------- stacks
+def draw_stack_bases(wl: Workload, gen: torch.Generator, device) -> list:
+    """W_base of every layer of a stack: stack[l][i] is matrix i of layer l,
+    drawn layer by layer in matrix order."""
+    return [draw_layer_bases(wl, gen, device) for _ in range(wl.layers)]
+
+
+def iter_stack_finetuned(stack: list, scales: list, gen: torch.Generator):
+    """Yield (layer, variant, matrix index, W_ft) layer-major, then variant,
+    then matrix, one temporary at a time."""
+    for l, bases in enumerate(stack):
+        for v, b in enumerate(scales):
+            for i, w in enumerate(bases):
+                yield l, v, i, draw_finetuned(w, b, gen)
+
+
+def draw_stack_inputs(wl: Workload, m: int, gen: torch.Generator, device) -> list:
+    """Per-layer activations (x ~ N(0, 1) for every layer, as the layer
+    inputs are drawn for one layer)."""
+    return [draw_layer_inputs(wl, m, gen, device) for _ in range(wl.layers)]
