@@ -185,21 +185,18 @@ __global__ __launch_bounds__(NW * kWave) void linear_decode_kernel(const SkinnyA
 // ---------------------------------------------------------------- mixed batch
 // Grouping of a mixed batch by variant, built once per workgroup in LDS.
 // Tokens are ordered by variant id (stable); slot s of the sorted order holds
-// token perm[s] of variant slotv[s] (-1 base only, -2 invalid id).  A "pair"
-// is a maximal run of slots of one variant inside one 16-token tile; dv[]
-// lists the distinct variants present and [dp0, dp1) their pairs.
+// token perm[s] of variant slotv[s] (-1 base only, -2 invalid id).  The slots
+// of one variant form a run; a "window" is a piece of at most 16 slots of a
+// run (runs are cut every 16 slots from their start): window w covers slots
+// ws0[w] .. ws0[w] + wlen[w] - 1, all of variant wvar[w].
 struct Groups {
   int perm[kMaxSkinnyTokens];
   int slotv[kMaxSkinnyTokens];
-  int pt[kMaxSkinnyTokens];
-  int plo[kMaxSkinnyTokens];
-  int phi[kMaxSkinnyTokens];
   int key[kMaxSkinnyTokens];
-  int dv[kMaxSkinnyTokens];
-  int dp0[kMaxSkinnyTokens];
-  int dp1[kMaxSkinnyTokens];
-  int np;
-  int nd;
+  int wvar[kMaxSkinnyTokens];
+  int ws0[kMaxSkinnyTokens];
+  int wlen[kMaxSkinnyTokens];
+  int nwin;
 };
 
 __device__ void build_groups(Groups& G, const int32_t* ids, int M, int n_variants) {
@@ -210,8 +207,9 @@ __device__ void build_groups(Groups& G, const int32_t* ids, int M, int n_variant
     G.key[t] = (v >= 0 && v < n_variants) ? v : (v == -1 ? n_variants : n_variants + 1);
   }
   __syncthreads();
+  int k = 0;
   if (t < M) {
-    const int k = G.key[t];
+    k = G.key[t];
     int rank = 0;
     for (int u = 0; u < M; ++u) {
       const int ku = G.key[u];
@@ -221,200 +219,247 @@ __device__ void build_groups(Groups& G, const int32_t* ids, int M, int n_variant
     G.slotv[rank] = k < n_variants ? k : (k == n_variants ? -1 : -2);
   }
   __syncthreads();
+  // window starts: slots of a variant whose offset in the variant's run is a
+  // multiple of 16 (key[] is free again and marks them)
   if (t < M) {
     const int v = G.slotv[t];
-    const bool start = v >= 0 && (t % 16 == 0 || G.slotv[t - 1] != v);
-    if (start) {
-      int idx = 0;
-      for (int u = 0; u < t; ++u) {
-        const int vu = G.slotv[u];
-        idx += (vu >= 0 && (u % 16 == 0 || G.slotv[u - 1] != vu)) ? 1 : 0;
-      }
-      int end = t + 1;
-      while (end < M && end % 16 != 0 && G.slotv[end] == v) ++end;
-      G.pt[idx] = t / 16;
-      G.plo[idx] = t % 16;
-      G.phi[idx] = end - (t / 16) * 16;
-    }
+    int rs = t;
+    while (rs > 0 && G.slotv[rs - 1] == v) --rs;
+    G.key[t] = (v >= 0 && (t - rs) % 16 == 0) ? 1 : 0;
   }
   __syncthreads();
+  if (t < M && G.key[t]) {
+    const int v = G.slotv[t];
+    int idx = 0;
+    for (int u = 0; u < t; ++u) idx += G.key[u];
+    int len = 1;
+    while (t + len < M && len < 16 && G.slotv[t + len] == v) ++len;
+    G.wvar[idx] = v;
+    G.ws0[idx] = t;
+    G.wlen[idx] = len;
+  }
   if (t == 0) {
-    int np = 0, nd = 0;
-    for (int u = 0; u < M; ++u) {
-      const int vu = G.slotv[u];
-      if (vu >= 0 && (u % 16 == 0 || G.slotv[u - 1] != vu)) {
-        if (nd == 0 || G.dv[nd - 1] != vu) {
-          if (nd > 0) G.dp1[nd - 1] = np;
-          G.dv[nd] = vu;
-          G.dp0[nd] = np;
-          ++nd;
-        }
-        ++np;
-      }
-    }
-    if (nd > 0) G.dp1[nd - 1] = np;
-    G.np = np;
-    G.nd = nd;
+    int nw = 0;
+    for (int u = 0; u < M; ++u) nw += G.key[u];
+    G.nwin = nw;
   }
   __syncthreads();
 }
 
-// The base product runs once for all tokens; the sign product once per
-// distinct variant present, with the x tile masked to that variant's tokens.
-// Each wave stages its x block in LDS next to a zero row: a variant's masked
-// tile is read by choosing, per lane, its token row or the zero row (one
-// address select instead of a select per register).  The distinct variants
-// are taken one at a time, the next one's sign words already requested.
+// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
+// at lds + 16*i (lds must be the same for the whole wave).
+__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+
+// The base product runs once for all tokens (16-token tiles); the sign
+// product once per window: the 16 staged slots starting at the window's first
+// slot times the +-1 operand of the window's variant, into the window's own
+// accumulator.  Rows of a window past its length hold other tokens' products
+// and are never read.  Windows are taken kWin at a time; a batch after the
+// first re-streams x and the sign words of its windows but not W_base.
 //
-// RT row tiles share a workgroup: its NW waves are RT row tiles x NW/RT
-// K-lanes, and the RT waves of one K-lane work on the same block at the same
-// time, so their x loads are the same addresses and all but one hit in L1.
-// With M = 32 the x bytes of a block are twice its weight bytes, so this
-// cuts the L2 traffic of the kernel by about a third for RT = 2.
-template <int MT, int NW, int RT>
+// Work split: a workgroup owns 16 output rows; its NW waves take the 128-wide
+// blocks of d_in round-robin and their partial sums are added in LDS in a
+// fixed order.  Each wave stages its block of x (the MT*16 tokens in variant
+// order, 256 bytes each) in its own LDS region with global_load_lds: one
+// instruction writes 4 rows, 16 lanes per row (coalesced), and lane (r, c)
+// fetches chunk c ^ (r % 16) so that operand reads of 16 consecutive rows at
+// one chunk hit distinct banks.  A zero row follows the tokens (windows near
+// the end of the batch read it past the last slot).
+template <int MT, int NW>
 __global__ __launch_bounds__(NW * kWave) void linear_multi_kernel(const SkinnyArgs a) {
-  constexpr int KL = NW / RT;                  // K-lanes (waves per row tile)
-  constexpr int kRedBytes = NW * MT * 2 * 4 * kWave * 4;
-  constexpr int kXRow = 128 + 8;               // bf16 per staged row (padded)
+  constexpr int kWin = 16;                     // windows per batch
   constexpr int kXRows = MT * 16 + 1;          // token rows + zero row
-  constexpr int kXWave = kXRows * kXRow;       // bf16 per wave
-  constexpr int kXBytes = NW * kXWave * 2;
+  constexpr int kXRowB = 256;                  // bytes per staged row (128 bf16)
+  constexpr int kXWave = kXRows * kXRowB;
+  constexpr int kXBytes = NW * kXWave;
+  constexpr int kRedChunk = 8;                 // f32x4 per lane and wave reduced at once
+  constexpr int kRedBytes = NW * kRedChunk * 4 * kWave * 4;
+  constexpr int kDma = MT * 4;                 // 4-row staging instructions per block
+  static_assert(MT <= kRedChunk, "base tiles reduce in one chunk");
   __shared__ __attribute__((aligned(16))) char smem[kRedBytes > kXBytes ? kRedBytes : kXBytes];
   __shared__ Groups G;
+  __shared__ float sw_slot[kMaxSkinnyTokens][16];
+  __shared__ float ss_slot[kMaxSkinnyTokens][16];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x >> 6;
-  const int rt = wv % RT;
-  const int kl = wv / RT;
   const int n = lane & 15;
   const int g = lane >> 4;
-  const int row0 = (blockIdx.x * RT + rt) * 16;
   const int d_in = a.d_in;
   const int M = a.M;
-  const int row = min(row0 + n, a.d_out - 1);
-  uint16_t* xst = reinterpret_cast<uint16_t*>(smem) + wv * kXWave;
+  char* xs = smem + wv * kXWave;
+  float* red = reinterpret_cast<float*>(smem);
 
   build_groups(G, a.ids, M, a.n_variants);
-  for (int e = lane; e < kXRow / 2; e += kWave)
-    reinterpret_cast<uint32_t*>(xst + MT * 16 * kXRow)[e] = 0u;
+  const int nwin = G.nwin;
+  const int nbatch = max((nwin + kWin - 1) / kWin, 1);  // one pass at least, for the base
+  // Window table, lane w holds window w: first slot and variant.
+  const int ws0_l = lane < nwin ? G.ws0[lane] : 0;
+  const int wvar_l = lane < nwin ? G.wvar[lane] : 0;
 
-  const uint16_t* xrow[MT];
+  // Staging sources: instruction j writes rows 4j..4j+3; lane (lane/16,
+  // c = lane%16) fetches chunk c ^ (row % 16) of slot row's token (slots past
+  // M re-read the last token; their outputs are never stored).  Packed as
+  // token | chunk << 8.
+  int xsrc[kDma];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) xrow[t] = a.x + (size_t)G.perm[min(16 * t + n, M - 1)] * d_in;
+  for (int j = 0; j < kDma; ++j) {
+    const int r = 4 * j + (lane >> 4);
+    xsrc[j] = G.perm[min(r, M - 1)] | (((lane & 15) ^ (r & 15)) << 8);
+  }
+  // Base operand reads: tile t, k-step q, lane (n, g) reads chunk 4g+q of
+  // row 16t+n (whose swizzle key is n).
+  int foff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) foff[q] = (((4 * g + q) ^ n) << 4);
+
+  const int row0 = blockIdx.x * 16;
+  const int row = min(row0 + n, a.d_out - 1);
   const uint16_t* wrow = a.w + (size_t)row * d_in;
   const size_t brow = (size_t)row * (d_in >> 5);
 
-  f32x4 accw[MT], accs[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    accw[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accs[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-
   const int nblk = (d_in + 127) >> 7;
-  const int nmine = blocks_of_wave(kl, nblk, KL);
+  const int nmine = blocks_of_wave(wv, nblk, NW);
   const bool half_tail = (d_in & 127) != 0;
-  const int nd = G.nd;
 
-  for (int i = 0; i < nmine; ++i) {
-    const int bu = kl + KL * i;
-    const int kc = min((bu << 7) + (g << 5), d_in - 32);
-    u32x4 wf[4];
-    u32x4 xf[MT][4];
+  f32x4 accw[MT];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      wf[q] = ld128(wrow + kc + 8 * q);
-#pragma unroll
-      for (int t = 0; t < MT; ++t) xf[t][q] = ld128(xrow[t] + kc + 8 * q);
-    }
-    // first variant's sign words go out with the block's weights
-    uint32_t nxt = 0u;
-    if (nd > 0) {
-      const int v0 = __builtin_amdgcn_readfirstlane(G.dv[0]);
-      nxt = ld32(a.packed[v0] + brow + (kc >> 5));
-    }
-    if (half_tail && bu == nblk - 1 && (bu << 7) + (g << 5) >= d_in) {
-#pragma unroll
-      for (int t = 0; t < MT; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) xf[t][q] = u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<u32x4*>(xst + (16 * t + n) * kXRow + 32 * g + 8 * q) = xf[t][q];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int t = 0; t < MT; ++t) accw[t] = mfma16(xf[t][q], wf[q], accw[t]);
+  for (int t = 0; t < MT; ++t) accw[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int d = 0; d < nd; ++d) {
-      const uint32_t cur = nxt;
-      if (d + 1 < nd) {
-        const int vn = __builtin_amdgcn_readfirstlane(G.dv[d + 1]);
-        nxt = ld32(a.packed[vn] + brow + (kc >> 5));
+  for (int batch = 0; batch < nbatch; ++batch) {
+    const int wb = batch * kWin;             // first window of the batch
+    const int nwb = min(kWin, nwin - wb);    // windows in the batch (<= 0: none)
+    f32x4 accv[kWin];
+#pragma unroll
+    for (int w = 0; w < kWin; ++w) accv[w] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (lane < 16) *reinterpret_cast<u32x4*>(xs + (kXRows - 1) * kXRowB + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+
+    for (int i = 0; i < nmine; ++i) {
+      const int bu = wv + NW * i;
+      const int k0 = bu << 7;
+      const bool half = half_tail && bu == nblk - 1;  // only its first 64 columns exist
+      // x block into LDS (the second half of a half block re-reads the first)
+#pragma unroll
+      for (int j = 0; j < kDma; ++j) {
+        const int ch = xsrc[j] >> 8;
+        const int col = k0 + 8 * ch - ((half && ch >= 8) ? 64 : 0);
+        lds_load16(a.x + (size_t)(xsrc[j] & 0xFF) * d_in + col, xs + j * 1024);
       }
-      const int p0 = __builtin_amdgcn_readfirstlane(G.dp0[d]);
-      const int p1 = __builtin_amdgcn_readfirstlane(G.dp1[d]);
-      uint32_t s[16];
-      sign_pairs(cur, s);
-      for (int p = p0; p < p1; ++p) {
-        const int tp = __builtin_amdgcn_readfirstlane(G.pt[p]);
-        const int lo = __builtin_amdgcn_readfirstlane(G.plo[p]);
-        const int hi = __builtin_amdgcn_readfirstlane(G.phi[p]);
-        const bool keep = (unsigned)(n - lo) < (unsigned)(hi - lo);
-        const uint16_t* src = xst + (keep ? 16 * tp + n : MT * 16) * kXRow + 32 * g;
-        u32x4 xm[4];
+      const int kc = min(k0 + (g << 5), d_in - 32);
+      u32x4 wf[4];
+      if (batch == 0) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) xm[q] = *reinterpret_cast<const u32x4*>(src + 8 * q);
+        for (int q = 0; q < 4; ++q) wf[q] = ld128(wrow + kc + 8 * q);
+      }
+      uint32_t sgn[kWin];
+#pragma unroll
+      for (int w = 0; w < kWin; ++w) {
+        if (w < nwb) {
+          const int v = __builtin_amdgcn_readlane(wvar_l, wb + w);
+          sgn[w] = ld32(a.packed[v] + brow + (kc >> 5));
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      if (half) {
+        // columns 64..127 of a half block do not exist: zero them (all rows)
+        for (int e = lane; e < (kXRows - 1) * 8; e += kWave) {
+          const int r = e >> 3;
+          const int cg = 8 + (e & 7);
+          *reinterpret_cast<u32x4*>(xs + r * kXRowB + ((cg ^ (r & 15)) << 4)) =
+              u32x4{0u, 0u, 0u, 0u};
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+      if (batch == 0) {
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          if (t == tp) {
+          const char* src = xs + (16 * t + n) * kXRowB;
+          u32x4 xf[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) accs[t] = mfma16(xm[q], quad(s, q), accs[t]);
-          }
+          for (int q = 0; q < 4; ++q) xf[q] = *reinterpret_cast<const u32x4*>(src + foff[q]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) accw[t] = mfma16(xf[q], wf[q], accw[t]);
+        }
+      }
+#pragma unroll
+      for (int w = 0; w < kWin; ++w) {
+        if (w < nwb) {
+          uint32_t sp[16];
+          sign_pairs(sgn[w], sp);
+          const int r = min(__builtin_amdgcn_readlane(ws0_l, wb + w) + n, MT * 16);
+          const char* src = xs + r * kXRowB;
+          const int key = r & 15;
+          u32x4 xw[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            xw[q] = *reinterpret_cast<const u32x4*>(src + ((((g << 2) + q) ^ key) << 4));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) accv[w] = mfma16(xw[q], quad(sp, q), accv[w]);
         }
       }
     }
+
+    // Sign sums of the batch's windows: add the waves' partials in a fixed
+    // order and file each under its slot.  MFMA 16x16 output layout: lane l
+    // holds window rows 4*(l/16)+v of output column l%16.
+#pragma unroll
+    for (int c0 = 0; c0 < kWin; c0 += kRedChunk) {
+      __syncthreads();  // staging (or the previous chunk) no longer read
+#pragma unroll
+      for (int c = 0; c < kRedChunk; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[((wv * kRedChunk + c) * 4 + v) * kWave + lane] = accv[c0 + c][v];
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < kRedChunk * 4 * kWave; idx += NW * kWave) {
+        const int l = idx & (kWave - 1);
+        const int v = (idx >> 6) & 3;
+        const int c = idx >> 8;
+        const int w = wb + c0 + c;
+        if (c0 + c < nwb) {
+          float ss = 0.f;
+#pragma unroll
+          for (int k = 0; k < NW; ++k) ss += red[((k * kRedChunk + c) * 4 + v) * kWave + l];
+          const int r = 4 * (l >> 4) + v;
+          if (r < G.wlen[w]) ss_slot[G.ws0[w] + r][l & 15] = ss;
+        }
+      }
+    }
+    if (batch == 0) {
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[((wv * kRedChunk + t) * 4 + v) * kWave + lane] = accw[t][v];
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < MT * 4 * kWave; idx += NW * kWave) {
+        const int l = idx & (kWave - 1);
+        const int v = (idx >> 6) & 3;
+        const int t = idx >> 8;
+        float sw = 0.f;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) sw += red[((k * kRedChunk + t) * 4 + v) * kWave + l];
+        const int slot = 16 * t + 4 * (l >> 4) + v;
+        if (slot < M) sw_slot[slot][l & 15] = sw;
+      }
+    }
+    __syncthreads();  // the reduction area is the next batch's staging
   }
 
-  // The LDS region may still hold other waves' staged x: barrier first.
-  __syncthreads();
-  // Partial sums: wave (rt, kl) -> its row tile's K-lane kl.
-  float* red = reinterpret_cast<float*>(smem);
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      red[(((wv * MT + t) * 2 + 0) * 4 + v) * kWave + lane] = accw[t][v];
-      red[(((wv * MT + t) * 2 + 1) * 4 + v) * kWave + lane] = accs[t][v];
-    }
-  }
-  __syncthreads();
   const int per_row = a.per_row;
-  for (int idx = threadIdx.x; idx < RT * MT * 4 * kWave; idx += NW * kWave) {
-    const int l = idx & (kWave - 1);
-    const int v = (idx >> 6) & 3;
-    const int t = (idx >> 8) % MT;
-    const int r = (idx >> 8) / MT;
-    float sw = 0.f, ss = 0.f;
-#pragma unroll
-    for (int k = 0; k < KL; ++k) {
-      const int w = k * RT + r;
-      sw += red[(((w * MT + t) * 2 + 0) * 4 + v) * kWave + l];
-      ss += red[(((w * MT + t) * 2 + 1) * 4 + v) * kWave + l];
-    }
-    // MFMA 16x16 output layout: lane l holds rows 4*(l/16)+v of column l%16.
-    const int slot = 16 * t + 4 * (l >> 4) + v;
-    const int o = (blockIdx.x * RT + r) * 16 + (l & 15);
-    if (slot < M && o < a.d_out) {
+  for (int idx = threadIdx.x; idx < M * 16; idx += NW * kWave) {
+    const int slot = idx >> 4;
+    const int ol = idx & 15;
+    const int o = row0 + ol;
+    if (o < a.d_out) {
       const int m = G.perm[slot];
       const int vv = G.slotv[slot];
+      const float sw = sw_slot[slot][ol];
       float yv;
       if (vv >= 0) {
         const float* ap = a.alpha[vv];
-        yv = sw + (per_row ? ap[o] : ap[0]) * ss;
+        yv = sw + (per_row ? ap[o] : ap[0]) * ss_slot[slot][ol];
       } else {
         yv = vv == -1 ? sw : __builtin_nanf("");
       }
@@ -434,18 +479,11 @@ hipError_t launch_decode(const SkinnyArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MT, int RT>
-hipError_t launch_multi_rt(const SkinnyArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((linear_multi_kernel<MT, kNW, RT>), dim3((a.d_out + 16 * RT - 1) / (16 * RT)),
-                     dim3(kNW * kWave), 0, stream, a);
-  return hipGetLastError();
-}
-
 template <int MT>
 hipError_t launch_multi(const SkinnyArgs& a, hipStream_t stream) {
-  // One row tile per workgroup: measured on the 70B-shaped gate matrix
-  // (M = 32, 14 variants), two row tiles sharing x through L1 were 6% slower.
-  return launch_multi_rt<MT, 1>(a, stream);
+  hipLaunchKernelGGL((linear_multi_kernel<MT, kNW>), dim3((a.d_out + 15) / 16), dim3(kNW * kWave), 0,
+                     stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
