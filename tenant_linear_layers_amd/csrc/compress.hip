@@ -11,8 +11,8 @@
 // contiguous 1 KiB.  The sign of element 8k+j is taken with one wave64
 // ballot per j; the eight 64-bit ballots are turned into the eight packed
 // words of the chunk by lanes 0..7, each doing one 8x8 bit transpose.
-// The scale is summed exactly in integers (floor(|d| * 2^48) split into two
-// 32-bit limbs), so the result does not depend on the order of summation.
+// The scale is summed exactly in integers (floor(|d| * 2^48)), so the result
+// does not depend on the order of summation.
 #include "common.h"
 #include "internal.h"
 #include "scale_round.h"
@@ -43,10 +43,55 @@ __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
   return v;
 }
 
+// Exact per-lane sum of floor(|d| * 2^48) over the lane's elements of one
+// row, by the two-limb method (hi = floor(|d| * 2^16), lo = the next 32
+// fraction bits), safe for any |d| < 2^15; *bad is set for larger, infinite
+// or NaN deltas.  Used for rows whose largest |d| is too big for the fast
+// single-sum path below.
+struct RowSum {
+  uint64_t hi, lo;
+  uint32_t bad;
+};
+
+__device__ __forceinline__ RowSum row_sum_two_limbs(const uint16_t* a_row, const uint16_t* b_row,
+                                                    int d_in, int lane) {
+  uint64_t acc_hi = 0, acc_lo = 0;
+  uint32_t b = 0;
+  for (int e0 = lane << 3; e0 < d_in; e0 += 512) {
+    const u32x4 va = ld128(a_row + e0);
+    const u32x4 vb = ld128(b_row + e0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t ua = (j & 1) ? (va[j >> 1] & 0xFFFF0000u) : (va[j >> 1] << 16);
+      const uint32_t ub = (j & 1) ? (vb[j >> 1] & 0xFFFF0000u) : (vb[j >> 1] << 16);
+      const float d = __uint_as_float(ua) - __uint_as_float(ub);
+      float ad = __builtin_fabsf(d) * 65536.0f;
+      const bool ok = ad < 2147483648.0f;  // false for NaN, inf, |d| >= 2^15
+      b |= ok ? 0u : 1u;
+      ad = ok ? ad : 0.0f;
+      const uint32_t hi = (uint32_t)ad;
+      const uint32_t lo = (uint32_t)((ad - (float)hi) * 4294967296.0f);
+      acc_hi += hi;
+      acc_lo += lo;
+    }
+  }
+  RowSum r;
+  r.hi = wave_sum_u64(acc_hi);
+  r.lo = wave_sum_u64(acc_lo);
+  r.bad = __builtin_amdgcn_ballot_w64(b != 0) != 0;
+  return r;
+}
+
 // Per-row pass.  kPerRow: write alpha[row] directly; otherwise write the
-// row's two integer limbs to partial[2*row .. 2*row+1] (limb hi = sum of
-// floor(|d|*2^16), limb lo = sum of the next 32 fraction bits; a row with a
-// bad delta gets hi = ~0).
+// row's sum as two limbs to partial[2*row .. 2*row+1] (S = hi * 2^32 + lo; a
+// row with a bad delta gets hi = ~0).
+//
+// Fast path: q = floor(|d| * 2^48) is the 64-bit pair (lo, hi) of the two
+// exact conversions hi = floor(|d| * 2^16) and lo = floor(frac(|d| * 2^16) *
+// 2^32), and the row's sum of q fits 64 bits whenever max|d| * 2^48 * d_in <
+// 2^64: each element costs one 64-bit add and one max of |d|'s bits (the
+// range check is done once per row from that maximum).  A row failing the
+// bound is summed again by the two-limb method.
 template <bool kPerRow>
 __global__ __launch_bounds__(kRowsPerBlock * kWave) void compress_rows_kernel(
     const uint16_t* __restrict__ w_ft, const uint16_t* __restrict__ w_base, int d_out, int d_in,
@@ -60,12 +105,13 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void compress_rows_kernel(
   const int n_words = d_in >> 6;
   uint64_t* p_row = packed + (size_t)row * n_words;
 
-  uint64_t acc_hi = 0, acc_lo = 0;
-  uint32_t bad = 0;
+  uint64_t acc = 0;
+  uint32_t maxbits = 0;  // largest float bits of |d| * 2^16 (NaN bits sort above inf)
   const int n_chunks = (d_in + 511) >> 9;
 
   // Four chunks per group: all eight 16-byte loads of a group are issued
-  // before any is used, so each wave keeps 8 KiB in flight.
+  // before any is used (8 KiB per wave in flight; 16 KiB measured slower),
+  // and each chunk is processed as soon as its own loads have arrived.
   constexpr int kGroup = 4;
   for (int c0 = 0; c0 < n_chunks; c0 += kGroup) {
     // Loads are never predicated (see the decode kernel): lanes past the end
@@ -81,7 +127,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void compress_rows_kernel(
 #pragma unroll
     for (int u = 0; u < kGroup; ++u) {
       const int c = c0 + u;
-      if (c >= n_chunks) break;  // uniform
+      if (c >= n_chunks) continue;  // uniform
       if ((c << 9) + 512 > d_in && (c << 9) + (lane << 3) >= d_in) {
         // d_in is a multiple of 64, so the active lanes of a partial chunk
         // cover whole 64-element words; the rest contribute +1 signs (never
@@ -97,17 +143,13 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void compress_rows_kernel(
         const float d = __uint_as_float(ua) - __uint_as_float(ub);
         // sign bit 1 <=> +1 <=> not (d < 0): +0, -0 and NaN give +1.
         ball[j] = __builtin_amdgcn_ballot_w64(!(d < 0.0f));
-        // q = floor(|d| * 2^48) = hi * 2^32 + lo with hi = floor(|d| * 2^16)
-        // and lo = floor(frac(|d| * 2^16) * 2^32); every step is exact.
-        float ad = __builtin_fabsf(d) * 65536.0f;
-        const bool ok = ad < 2147483648.0f;  // false for NaN, inf, |d| >= 2^15
-        bad |= ok ? 0u : 1u;
-        ad = ok ? ad : 0.0f;
+        const float ad = __builtin_fabsf(d) * 65536.0f;
+        maxbits = max(maxbits, __float_as_uint(ad));
+        // Conversions saturate for out-of-range values; such rows are
+        // recomputed or flagged below, so their sum here is discarded.
         const uint32_t hi = (uint32_t)ad;
-        const float fr = ad - (float)hi;
-        const uint32_t lo = (uint32_t)(fr * 4294967296.0f);
-        acc_hi += hi;  // inactive lanes hold zeros, so add zero
-        acc_lo += lo;
+        const uint32_t lo = (uint32_t)(__builtin_amdgcn_fractf(ad) * 4294967296.0f);
+        acc += ((uint64_t)hi << 32) | lo;
       }
       if (lane < 8) {
         // word `lane` of this chunk: bit 8i+j comes from ballot j, bit 8*lane+i.
@@ -120,19 +162,43 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void compress_rows_kernel(
     }
   }
 
-  acc_hi = wave_sum_u64(acc_hi);
-  acc_lo = wave_sum_u64(acc_lo);
-  const bool row_bad = __builtin_amdgcn_ballot_w64(bad != 0) != 0;
+  // Row-wide largest |d| * 2^16 (float bits; the values are >= 0, so their
+  // bit patterns order like the values, and NaN patterns sort above inf).
+  uint32_t mb = maxbits;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off, 64));
+  // Fast path valid iff max|d| * 2^16 * d_in < 2^32, i.e. the row sum of q
+  // stays below 2^64; checked in float without rounding trouble since d_in
+  // is a power-of-two multiple of 64 times an integer < 2^31.
+  const float maxad = __uint_as_float(mb);
+  const bool row_bad_fast = !(maxad < 2147483648.0f);  // also NaN, inf
+  const bool fast = !row_bad_fast && maxad * (float)d_in < 4294967296.0f * 0.5f;
+  uint64_t s_hi, s_lo;
+  uint32_t row_bad;
+  if (fast) {
+    const uint64_t s = wave_sum_u64(acc);
+    s_hi = s >> 32;
+    s_lo = s & 0xFFFFFFFFull;
+    row_bad = 0;
+  } else if (row_bad_fast) {
+    s_hi = s_lo = 0;
+    row_bad = 1;
+  } else {
+    const RowSum r = row_sum_two_limbs(a_row, b_row, d_in, lane);
+    s_hi = r.hi;
+    s_lo = r.lo;
+    row_bad = r.bad;
+  }
   if (lane == 0) {
     if (kPerRow) {
-      // S = acc_hi * 2^32 + acc_lo as a 128-bit value.
-      const uint64_t lo = (acc_hi << 32) + acc_lo;
-      const uint64_t hi = (acc_hi >> 32) + (lo < acc_lo ? 1u : 0u);
+      // S = s_hi * 2^32 + s_lo as a 128-bit value.
+      const uint64_t lo = (s_hi << 32) + s_lo;
+      const uint64_t hi = (s_hi >> 32) + (lo < s_lo ? 1u : 0u);
       const uint32_t bits = row_bad ? 0x7FC00000u : ratio_to_f32_bits(hi, lo, (uint64_t)d_in);
       alpha[row] = __uint_as_float(bits);
     } else {
-      partial[2 * (size_t)row] = row_bad ? ~0ull : acc_hi;
-      partial[2 * (size_t)row + 1] = acc_lo;
+      partial[2 * (size_t)row] = row_bad ? ~0ull : s_hi;
+      partial[2 * (size_t)row + 1] = s_lo;
     }
   }
 }

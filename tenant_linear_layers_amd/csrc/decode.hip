@@ -471,9 +471,8 @@ __global__ __launch_bounds__(NW * kWave) void linear_multi_kernel(const SkinnyAr
 // ---------------------------------------------------------------- launchers
 constexpr int kNW = 8;
 
-template <int MT>
+template <int MT, int U>
 hipError_t launch_decode(const SkinnyArgs& a, hipStream_t stream) {
-  constexpr int U = MT >= 4 ? 1 : 4 / MT;
   hipLaunchKernelGGL((linear_decode_kernel<MT, kNW, U>), dim3((a.d_out + 15) / 16),
                      dim3(kNW * kWave), 0, stream, a);
   return hipGetLastError();
@@ -489,9 +488,12 @@ hipError_t launch_multi(const SkinnyArgs& a, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_linear_skinny(const SkinnyArgs& a, hipStream_t stream) {
-  if (a.M <= 16) return launch_decode<1>(a, stream);
-  if (a.M <= 32) return launch_decode<2>(a, stream);
-  return launch_decode<4>(a, stream);
+  // Blocks in flight per wave: 4 for a single token, 2 up to 32 tokens (the
+  // x loads grow with the tiles), 1 beyond (measured on 4096x4096).
+  if (a.M == 1) return launch_decode<1, 4>(a, stream);
+  if (a.M <= 16) return launch_decode<1, 2>(a, stream);
+  if (a.M <= 32) return launch_decode<2, 2>(a, stream);
+  return launch_decode<4, 1>(a, stream);
 }
 
 hipError_t launch_linear_multi(const SkinnyArgs& a, hipStream_t stream) {
