@@ -96,7 +96,7 @@ template <int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
     const uint16_t* __restrict__ x, int M, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ bits8, const float* __restrict__ alpha, int per_row, int d_out,
-    int d_in, uint16_t* __restrict__ y, int ntm, int ntn, int chunk) {
+    int d_in, uint16_t* __restrict__ y, int ldy, int ntm, int ntn, int chunk) {
   constexpr int NT = 64 * WM * WN;   // threads
   constexpr int RS = NT / 8;         // weight rows covered by one pass of 16-byte loads
   constexpr int NB = BN / RS;        // weight pieces per thread per step
@@ -253,15 +253,16 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int m = m0 + wm * (BM / WM) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (m < M && o < d_out) y[(size_t)m * d_out + o] = f32_to_bf16_bits(acc[i][j][v]);
+        if (m < M && o < d_out) y[(size_t)m * ldy + o] = f32_to_bf16_bits(acc[i][j][v]);
       }
     }
   }
 }
 
+// Output rows [0, d_out) of the slab starting at w (rows of y are ldy apart).
 template <int BN, int WM, int WN>
 hipError_t launch_cfg(const uint16_t* x, int M, const uint16_t* w, const uint8_t* packed_bytes,
-                      const float* alpha, int per_row, int d_out, int d_in, uint16_t* y,
+                      const float* alpha, int per_row, int d_out, int d_in, uint16_t* y, int ldy,
                       hipStream_t stream) {
   // Buffer offsets are 32-bit: one tile's rows of W_base must span < 2 GiB.
   if ((int64_t)BN * d_in * 2 > (int64_t)kPrefillMaxTileBytes) return hipErrorInvalidValue;
@@ -270,7 +271,7 @@ hipError_t launch_cfg(const uint16_t* x, int M, const uint16_t* w, const uint8_t
   const int tiles = ntm * ntn;
   const int chunk = (tiles + 7) / 8;
   hipLaunchKernelGGL((prefill_kernel<BN, WM, WN>), dim3(8 * chunk), dim3(64 * WM * WN), 0, stream,
-                     x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ntm, ntn, chunk);
+                     x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy, ntm, ntn, chunk);
   return hipGetLastError();
 }
 
@@ -279,14 +280,33 @@ hipError_t launch_cfg(const uint16_t* x, int M, const uint16_t* w, const uint8_t
 hipError_t launch_linear_prefill(const uint16_t* x, int M, const uint16_t* w,
                                  const uint8_t* packed_bytes, const float* alpha, int per_row,
                                  int d_out, int d_in, uint16_t* y, hipStream_t stream) {
-  // 8 waves, two per SIMD.  256-wide weight tiles unless their last round
-  // over the 256 CUs would leave more than a quarter of the chip idle; then
-  // 128-wide tiles (twice as many, each about 55% of the time).
-  const long tiles256 = (long)((M + BM - 1) / BM) * ((d_out + 255) / 256);
-  const long rounds256 = (tiles256 + 255) / 256;
-  if (4 * tiles256 >= 3 * 256 * rounds256)
-    return launch_cfg<256, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, stream);
-  return launch_cfg<128, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, stream);
+  // 8 waves, two per SIMD; tiles are dealt in rounds over the 256 CUs.
+  constexpr int kCUs = 256;
+  const long ntm = (M + BM - 1) / BM;
+  const long tiles256 = ntm * ((d_out + 255) / 256);
+  const long full = tiles256 / kCUs;
+  if (full >= 1 && tiles256 % kCUs != 0) {
+    // Whole rounds of 256-wide weight tiles, then the remaining rows as
+    // 128-wide tiles (twice as many, about half as long), so the last round
+    // does not leave part of the chip idle.
+    const long n_split = (full * kCUs / ntm) * 256;
+    if (n_split > 0 && n_split < d_out) {
+      hipError_t e = launch_cfg<256, 4, 2>(x, M, w, packed_bytes, alpha, per_row, (int)n_split,
+                                           d_in, y, d_out, stream);
+      if (e != hipSuccess) return e;
+      return launch_cfg<128, 4, 2>(x, M, w + n_split * d_in, packed_bytes + n_split * (d_in / 8),
+                                   per_row ? alpha + n_split : alpha, per_row,
+                                   d_out - (int)n_split, d_in, y + n_split, d_out, stream);
+    }
+  }
+  // Fewer tiles than CUs, or whole rounds: 256-wide tiles unless their last
+  // round would leave more than a quarter of the CUs idle.
+  const long rounds256 = (tiles256 + kCUs - 1) / kCUs;
+  if (4 * tiles256 >= 3 * kCUs * rounds256)
+    return launch_cfg<256, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, d_out,
+                                 stream);
+  return launch_cfg<128, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, d_out,
+                               stream);
 }
 
 }  // namespace bd

@@ -139,6 +139,23 @@ def test_compress_special_values():
     check_compress(wf, wb, 0)
 
 
+def test_compress_large_deltas_either_side_of_fast_bound():
+    """The row sum takes a single 64-bit accumulator while max|d| * d_in <
+    2^16 and an exact two-limb recount above; rows on both sides of the
+    bound (d_in = 2048: |d| = 20 and |d| = 40) must stay bit-exact."""
+    rng = np.random.default_rng(12)
+    d_out, d_in = 6, 2048
+    base = rng.normal(0, 0.02, (d_out, d_in)).astype(np.float32)
+    ft = base + rng.laplace(0, 1e-3, (d_out, d_in)).astype(np.float32)
+    ft[1, 5] = base[1, 5] + 20.0
+    ft[2, 7] = base[2, 7] - 40.0
+    ft[3, :] = base[3, :] + rng.uniform(-31.0, 31.0, d_in).astype(np.float32)
+    ft[4, :] = base[4, :] + rng.uniform(-33.0, 33.0, d_in).astype(np.float32)
+    wb, wf = _bf16(base), _bf16(ft)
+    check_compress(wf, wb, 1)
+    check_compress(wf, wb, 0)
+
+
 def test_compress_is_deterministic():
     wb, wf = S.small_pair(300, 2048, 0.02, 1e-3, seed=77)
     wb, wf = to_dev(wb, wf)
