@@ -206,22 +206,36 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
     // Keep the prefetches at the top of the step (the scheduler would sink
     // them towards the barrier to save registers).
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      u32x4 af[TMW], bf[TNW];
+    // Operand fragments double-buffered across the 16-wide sub-steps: the
+    // reads of sub-step ks+1 are issued before the MFMAs of sub-step ks.
+    u32x4 afA[TMW], bfA[TNW], afB[TMW], bfB[TNW];
+    auto rd = [&](int ks, u32x4 (&af)[TMW], u32x4 (&bf)[TNW]) {
 #pragma unroll
       for (int i = 0; i < TMW; ++i) af[i] = *reinterpret_cast<const u32x4*>(as + aoff[i][ks]);
 #pragma unroll
       for (int j = 0; j < TNW; ++j)
         bf[j] = *reinterpret_cast<const u32x4*>(
             &bs[wn * (BN / WN) + j * 32 + (lane & 31)][ks * 16 + 8 * (lane >> 5)]);
+    };
+    auto mm = [&](const u32x4 (&af)[TMW], const u32x4 (&bf)[TNW]) {
 #pragma unroll
       for (int i = 0; i < TMW; ++i)
 #pragma unroll
         for (int j = 0; j < TNW; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+    };
+    rd(0, afA, bfA);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ks += 2) {
+      rd(ks + 1, afB, bfB);
+      mm(afA, bfA);
 #pragma unroll
       for (int i = 0; i < NB; ++i)
         if (i % 4 == ks) wpiece(i, bs_next, rb_use, rs_use);
+      if (ks + 2 < BK / 16) rd(ks + 2, afA, bfA);
+      mm(afB, bfB);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if (i % 4 == ks + 1) wpiece(i, bs_next, rb_use, rs_use);
     }
     step_barrier();
   };
