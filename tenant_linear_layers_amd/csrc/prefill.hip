@@ -12,11 +12,11 @@
 // filled for the next step.  Raw weights are loaded two steps ahead into two
 // register sets, so the rebuild of step k+1 (from registers that have already
 // arrived) is spread over the four 16-wide MFMA sub-steps of step k.
-//  * x goes from global memory straight into LDS (global_load_lds, 16 bytes
-//    per lane, no registers): each wave instruction writes one 8-row block of
-//    1 KB; chunk c of row r sits at position c ^ (r % 8) of its 128-byte row
-//    and consecutive blocks are 1152 bytes apart, so the MFMA operand reads
-//    (32 rows at one chunk) hit distinct banks.
+//  * x goes from global memory straight into LDS (buffer loads to LDS, 16
+//    bytes per lane, no registers): each wave instruction writes one 8-row
+//    block of 1 KB; chunk c of row r sits at position c ^ (r % 8) of its
+//    128-byte row and consecutive blocks are 1152 bytes apart, so the MFMA
+//    operand reads (32 rows at one chunk) hit distinct banks.
 //  * W_base and the sign bytes are buffer loads into registers; each thread
 //    rebuilds its 4 x 8 weights as bf16(W_base + alpha*s) and stores them to
 //    the weight stage (rows padded to 144 bytes).
@@ -77,18 +77,28 @@ __device__ __forceinline__ uint32_t bload8(const void* base, int nbytes, int vof
   return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane i's bytes land
-// at lds + 16*i (lds must be the same for the whole wave).
-__device__ __forceinline__ void lds_load16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+// 16 bytes per lane through a buffer resource straight into LDS: lane i's
+// bytes land at lds + 16*i (lds must be the same for the whole wave).  A
+// buffer load rather than a global one: the compiler then counts these loads
+// in order with the weight loads and can wait for exactly the ones a step
+// needs (with global-to-LDS loads pending it falls back to waiting for all).
+__device__ __forceinline__ void lds_bload16(const void* base, int nbytes, int voff, int soff,
+                                            void* lds) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
 }
 
 // Workgroup barrier without a memory fence.  Callers first wait for their
-// own loads and LDS stores (s_waitcnt 0), which is what makes the LDS
-// contents visible; the memory clobber keeps the compiler from moving memory
-// accesses across the barrier.
+// own loads and LDS stores, which is what makes the LDS contents visible; the
+// memory clobber keeps the compiler from moving memory accesses across the
+// barrier.  step_barrier<N> leaves the N most recent vector memory loads in
+// flight (s_waitcnt vmcnt(N) lgkmcnt(0)).
+template <int N>
 __device__ __forceinline__ void step_barrier() {
-  __builtin_amdgcn_s_waitcnt(0);
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
   asm volatile("s_barrier" ::: "memory");
 }
 
@@ -132,12 +142,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
   const int pos = lane & 7;
 
   // x: wave wv fills 8-row blocks wv*AI + b; lane (r8, pos) fetches chunk
-  // pos ^ r8 of row r8 of the block (rows past M re-read row M-1).
-  const uint16_t* xa[AI];
+  // pos ^ r8 of row r8 of the block (rows past M re-read row M-1).  Byte
+  // offsets within this tile's rows of x.
+  const uint16_t* xbase = x + (size_t)m0 * d_in;
+  const int xbytes = min(BM, M - m0) * d_in * 2;
+  int xv[AI];
 #pragma unroll
   for (int b = 0; b < AI; ++b) {
     const int row = (wv * AI + b) * 8 + r8;
-    xa[b] = x + (size_t)min(m0 + row, M - 1) * d_in + 8 * (pos ^ r8);
+    xv[b] = (min(m0 + row, M - 1) - m0) * d_in * 2 + 16 * (pos ^ r8);
   }
   // W_base and sign bytes of this tile's rows (rows past d_out read zero).
   const int nrows = min(BN, d_out - n0);
@@ -172,7 +185,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
   uint32_t rs0[NB], rs1[NB];
   auto xload = [&](int kt, unsigned char* as) {
 #pragma unroll
-    for (int b = 0; b < AI; ++b) lds_load16(xa[b] + kt * BK, as + (wv * AI + b) * ABLK);
+    for (int b = 0; b < AI; ++b)
+      lds_bload16(xbase, xbytes, xv[b], kt * BK * 2, as + (wv * AI + b) * ABLK);
   };
   auto wload = [&](int kt, u32x4 (&rb)[NB], uint32_t (&rs)[NB]) {
 #pragma unroll
@@ -202,6 +216,10 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
                   unsigned char* as_next, uint16_t (*bs_next)[LDK], const u32x4 (&rb_use)[NB],
                   const uint32_t (&rs_use)[NB], u32x4 (&rb_load)[NB], uint32_t (&rs_load)[NB]) {
     xload(min(kt + 1, nk - 1), as_next);
+    // x first, then the 2*NB weight loads: the barrier at the end of the
+    // step waits for x and leaves the weights (needed one step later) in
+    // flight.
+    __builtin_amdgcn_sched_barrier(0);
     wload(min(kt + 2, nk - 1), rb_load, rs_load);
     // Keep the prefetches at the top of the step (the scheduler would sink
     // them towards the barrier to save registers).
@@ -237,7 +255,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
       for (int i = 0; i < NB; ++i)
         if (i % 4 == ks + 1) wpiece(i, bs_next, rb_use, rs_use);
     }
-    step_barrier();
+    step_barrier<2 * NB>();
   };
 
   const int nk = d_in / BK;
@@ -247,7 +265,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
   __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll
   for (int i = 0; i < NB; ++i) wpiece(i, Bs0, rb0, rs0);
-  step_barrier();
+  step_barrier<0>();
   // Steps in unconditional pairs (a conditional second step lets the
   // compiler sink the first step's loads into it), then a last odd step.
   int kt = 0;
