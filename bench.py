@@ -14,8 +14,9 @@ Launches are captured in HIP graphs so that the GPU runs them back to back
 (a Python launch costs more host time than a decode kernel takes).  Timed
 region 1 replays K one-pass graphs (the steps), each bracketed by HIP events,
 between synchronisations: ms_per_step.  Timed region 2 replays, per kernel,
-a graph of back-to-back launches over the rotation copies with HIP events
-around each replay, on the stream the kernels run on: the average launch
+a graph of back-to-back launches that cycles four times over the rotation
+copies, with HIP events around each replay, on the stream the kernels run
+on (the cost of starting a replay is spread over many launches): the average launch
 duration of each kernel, which is what value and the rooflines use.  The line
 printed reports decode effective HBM GB/s (algorithmic bytes / kernel time)
 as `value`, the prefill TFLOP/s beside it, a roofline entry per kernel, and
@@ -58,6 +59,7 @@ import tenant_linear_layers_amd as T  # noqa: E402
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 MALL_BYTES = 256 * 2**20
+RANGE_CYCLES = 4               # passes over the rotation copies per timing graph
 METRIC = "bitdelta_linear effective HBM GB/s (decode) + bf16 TFLOP/s (prefill), 1 GPU"
 PROFILES = os.path.join(ROOT, "profiles")
 
@@ -238,14 +240,17 @@ class ProjWorkload:
         self.run_prefill(r + 5)
 
     def ranges(self):
-        """name -> (launches per graph, function making them back to back)."""
-        out = {"compress": (len(self.fts), lambda: [self.run_compress(r)
-                                                    for r in range(len(self.fts))])}
+        """name -> (launches per graph, function making them back to back).
+        Each graph cycles RANGE_CYCLES times through the rotation copies so
+        that the cost of starting a replay is spread over many launches."""
+        c = RANGE_CYCLES
+        nf = len(self.fts)
+        out = {"compress": (c * nf, lambda: [self.run_compress(r) for r in range(c * nf)])}
         for m in self.decode_ms:
-            out[f"decode_m{m}"] = (self.R, lambda m=m: [self.run_decode(m, r)
-                                                        for r in range(self.R)])
-        out["multi"] = (self.R, lambda: [self.run_multi(r) for r in range(self.R)])
-        out["prefill"] = (8, lambda: [self.run_prefill(r) for r in range(8)])
+            out[f"decode_m{m}"] = (c * self.R, lambda m=m: [self.run_decode(m, r)
+                                                            for r in range(c * self.R)])
+        out["multi"] = (c * self.R, lambda: [self.run_multi(r) for r in range(c * self.R)])
+        out["prefill"] = (c * 8, lambda: [self.run_prefill(r % 8) for r in range(c * 8)])
         return out
 
 
@@ -291,7 +296,8 @@ class LayerWorkload:
             self.run(i)
 
     def ranges(self):
-        return {f"{self.kind}_{nm}": (2, lambda i=i: [self.run(i), self.run(i)])
+        n = 2 * RANGE_CYCLES
+        return {f"{self.kind}_{nm}": (n, lambda i=i: [self.run(i) for _ in range(n)])
                 for i, (nm, _, _) in enumerate(self.wl.matrices)}
 
     def work(self, i):
