@@ -29,6 +29,7 @@ namespace bd {
 namespace {
 
 constexpr int BM = 256;
+constexpr int kCUs = 256;          // MI355X compute units: one tile per CU per round
 constexpr int BK = 64;
 constexpr int ABLK = 1152;          // bytes per 8-row block of the x stage (1 KB + 128 B skew)
 constexpr int A_STAGE = 32 * ABLK;  // 256 rows
@@ -291,6 +292,209 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
   }
 }
 
+// ------------------------------------------------- producer/consumer tiles
+// Tile: 512 tokens x 128 output rows x 64 of d_in per step, 12 waves.  Waves
+// 0..7 (4 x 2, each 128 x 64 outputs in MFMA 32x32x16 tiles) only read the
+// LDS stages and multiply; waves 8..11 are producers: they stage x with
+// buffer loads to LDS and rebuild W_eff into the next weight stage, so the
+// rebuild's ALU work runs in waves of its own beside the MFMA waves instead
+// of inside their instruction streams.  Twice the token rows of the 256-row
+// tile halve the rebuild work per MFMA.  LDS holds two x stages of 64 KB and
+// two weight stages of 16 KB (160 KB), rows of 128 bytes with chunk c of row
+// r at position c ^ ((r / 2) % 8): the MFMA operand reads (16 consecutive
+// rows at one chunk per 256 bytes of banks) are conflict free without
+// padding.  One barrier per step for all 12 waves.
+constexpr int PC_BM = 512;
+constexpr int PC_BN = 128;
+constexpr int PC_XSTAGE = PC_BM * 128;
+constexpr int PC_WSTAGE = PC_BN * 128;
+constexpr int PC_THREADS = 768;
+// x of one tile is addressed with 32-bit buffer offsets: 512 rows of d_in.
+constexpr int64_t kPcMaxDin = kPrefillMaxTileBytes / (PC_BM * 2) / 64 * 64;
+
+__device__ __forceinline__ int pc_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+__global__ __launch_bounds__(PC_THREADS, 1) void prefill_pc_kernel(
+    const uint16_t* __restrict__ x, int M, const uint16_t* __restrict__ w,
+    const uint8_t* __restrict__ bits8, const float* __restrict__ alpha, int per_row, int d_out,
+    int d_in, uint16_t* __restrict__ y, int ldy, int ntm, int ntn, int chunk) {
+  constexpr int WM = 4, WN = 2;
+  constexpr int TMW = PC_BM / WM / 32;  // 4
+  constexpr int TNW = PC_BN / WN / 32;  // 2
+  constexpr int NB = 4;                 // weight pieces per producer thread per step
+  constexpr int AI = 16;                // 8-row x blocks per producer wave per step
+  __shared__ __attribute__((aligned(16))) unsigned char X0[PC_XSTAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char X1[PC_XSTAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char W0[PC_WSTAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char W1[PC_WSTAGE];
+
+  // contiguous tile ranges per XCD, token tile fastest (as in prefill_kernel)
+  const int tile = (blockIdx.x & 7) * chunk + (blockIdx.x >> 3);
+  if (tile >= ntm * ntn) return;
+  const int m0 = (tile % ntm) * PC_BM;
+  const int n0 = (tile / ntm) * PC_BN;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int nk = d_in / BK;
+
+  if (wv >= 8) {
+    // ------------------------------------------------------------ producers
+    const int pw = wv - 8;
+    const int T = threadIdx.x - 512;
+    const int lr = T >> 3;  // 0..31: weight row within a 32-row pass
+    const int lc = T & 7;   // 16-byte chunk within the 64-wide step
+    // x rows past M lie beyond the resource and read as zero.  Block b of
+    // the tile holds rows 8b..8b+7; lane (r, p) fetches chunk p ^ ((row/2)%8)
+    // of row 8b + r, whose swizzle depends on the block's parity only.
+    const uint16_t* xbase = x + (size_t)m0 * d_in;
+    const int xbytes = min(PC_BM, M - m0) * d_in * 2;
+    int xv[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int row = par * 8 + (lane >> 3);
+      xv[par] = row * d_in * 2 + 16 * pc_swz(row, lane & 7);
+    }
+    // W_base and sign bytes of the tile's rows (rows past d_out read zero);
+    // piece i of a thread is row lr + 32 i.
+    const int nrows = min(PC_BN, d_out - n0);
+    const uint16_t* wbase = w + (size_t)n0 * d_in;
+    const int wbytes = nrows * d_in * 2;
+    const uint8_t* sbase = bits8 + (size_t)n0 * (d_in >> 3);
+    const int sbytes = nrows * (d_in >> 3);
+    const int vw0 = (lr * d_in + lc * 8) * 2;
+    const int vs0 = lr * (d_in >> 3) + lc;
+    const int woff0 = lr * 128 + 16 * pc_swz(lr, lc);  // piece i: + 4096 i, same swizzle
+    uint32_t ab[NB];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+      ab[i] = __float_as_uint(per_row ? alpha[min(n0 + lr + 32 * i, d_out - 1)] : alpha[0]);
+    u32x4 rb0[NB], rb1[NB];
+    uint32_t rs0[NB], rs1[NB];
+    auto xload = [&](int kt, unsigned char* xs) {
+#pragma unroll
+      for (int b = 0; b < AI; ++b) {
+        const int blk = pw * AI + b;
+        lds_bload16(xbase, xbytes, xv[blk & 1], kt * BK * 2 + (blk >> 1) * 16 * d_in * 2,
+                    xs + blk * 1024);
+      }
+    };
+    auto wload = [&](int kt, u32x4 (&rb)[NB], uint32_t (&rs)[NB]) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        rb[i] = bload128(wbase, wbytes, vw0, kt * BK * 2 + i * 32 * d_in * 2);
+        rs[i] = bload8(sbase, sbytes, vs0, kt * (BK / 8) + i * 32 * (d_in >> 3));
+      }
+    };
+    auto build = [&](unsigned char* ws, const u32x4 (&rb)[NB], const uint32_t (&rs)[NB]) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        *reinterpret_cast<u32x4*>(ws + woff0 + i * 4096) = rebuild8(rb[i], rs[i], ab[i]);
+    };
+    // Step kt: x of step kt+1 into the free x stage, raw weights of step
+    // kt+2 into rb_load, W_eff of step kt+1 (rb_use, loaded a step earlier)
+    // into the free weight stage; the barrier waits for x and the LDS
+    // stores and leaves the weight loads in flight.  Prefetches past the
+    // last step re-read it into buffers nobody reads.
+    auto pstep = [&](int kt, unsigned char* xs_next, unsigned char* ws_next,
+                     const u32x4 (&rb_use)[NB], const uint32_t (&rs_use)[NB],
+                     u32x4 (&rb_load)[NB], uint32_t (&rs_load)[NB]) {
+      xload(min(kt + 1, nk - 1), xs_next);
+      __builtin_amdgcn_sched_barrier(0);
+      wload(min(kt + 2, nk - 1), rb_load, rs_load);
+      __builtin_amdgcn_sched_barrier(0);
+      build(ws_next, rb_use, rs_use);
+      step_barrier<2 * NB>();
+    };
+    xload(0, X0);
+    wload(0, rb0, rs0);
+    wload(min(1, nk - 1), rb1, rs1);
+    __builtin_amdgcn_s_waitcnt(0);
+    build(W0, rb0, rs0);
+    step_barrier<0>();
+    int kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      pstep(kt, X1, W1, rb1, rs1, rb0, rs0);
+      pstep(kt + 1, X0, W0, rb0, rs0, rb1, rs1);
+    }
+    if (kt < nk) pstep(kt, X1, W1, rb1, rs1, rb0, rs0);
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+
+  // ---------------------------------------------------------- MFMA waves
+  const int wm = wv % WM;
+  const int wn = wv / WM;
+  // Operand reads of 16-wide sub-step ks; tile i (j) of the wave lies 32
+  // rows (4096 bytes) further on with the same swizzle.
+  int aoff[4], boff[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const int c = 2 * ks + (lane >> 5);
+    const int ra = wm * (PC_BM / WM) + (lane & 31);
+    aoff[ks] = ra * 128 + 16 * pc_swz(ra, c);
+    const int rw = wn * (PC_BN / WN) + (lane & 31);
+    boff[ks] = rw * 128 + 16 * pc_swz(rw, c);
+  }
+  f32x16 acc[TMW][TNW];
+#pragma unroll
+  for (int i = 0; i < TMW; ++i)
+#pragma unroll
+    for (int j = 0; j < TNW; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+  auto cstep = [&](const unsigned char* xs, const unsigned char* ws) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 af[TMW], bf[TNW];
+#pragma unroll
+      for (int i = 0; i < TMW; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(xs + aoff[ks] + i * 4096);
+#pragma unroll
+      for (int j = 0; j < TNW; ++j)
+        bf[j] = *reinterpret_cast<const u32x4*>(ws + boff[ks] + j * 4096);
+#pragma unroll
+      for (int i = 0; i < TMW; ++i)
+#pragma unroll
+        for (int j = 0; j < TNW; ++j) acc[i][j] = mfma32(af[i], bf[j], acc[i][j]);
+    }
+    step_barrier<0>();
+  };
+  step_barrier<0>();  // the producers' first stage
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    cstep(X0, W0);
+    cstep(X1, W1);
+  }
+  if (kt < nk) cstep(X0, W0);
+
+  // MFMA 32x32 output layout as in prefill_kernel.
+#pragma unroll
+  for (int i = 0; i < TMW; ++i) {
+#pragma unroll
+    for (int j = 0; j < TNW; ++j) {
+      const int o = n0 + wn * (PC_BN / WN) + j * 32 + (lane & 31);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int m = m0 + wm * (PC_BM / WM) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (m < M && o < d_out) y[(size_t)m * ldy + o] = f32_to_bf16_bits(acc[i][j][v]);
+      }
+    }
+  }
+}
+
+hipError_t launch_pc(const uint16_t* x, int M, const uint16_t* w, const uint8_t* packed_bytes,
+                     const float* alpha, int per_row, int d_out, int d_in, uint16_t* y, int ldy,
+                     hipStream_t stream) {
+  if (d_in > kPcMaxDin) return hipErrorInvalidValue;
+  const int ntm = (M + PC_BM - 1) / PC_BM;
+  const int ntn = (d_out + PC_BN - 1) / PC_BN;
+  const int tiles = ntm * ntn;
+  const int chunk = (tiles + 7) / 8;
+  hipLaunchKernelGGL(prefill_pc_kernel, dim3(8 * chunk), dim3(PC_THREADS), 0, stream, x, M, w,
+                     packed_bytes, alpha, per_row, d_out, d_in, y, ldy, ntm, ntn, chunk);
+  return hipGetLastError();
+}
+
 // Output rows [0, d_out) of the slab starting at w (rows of y are ldy apart).
 template <int BN, int WM, int WN>
 hipError_t launch_cfg(const uint16_t* x, int M, const uint16_t* w, const uint8_t* packed_bytes,
@@ -307,13 +511,11 @@ hipError_t launch_cfg(const uint16_t* x, int M, const uint16_t* w, const uint8_t
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_linear_prefill(const uint16_t* x, int M, const uint16_t* w,
-                                 const uint8_t* packed_bytes, const float* alpha, int per_row,
-                                 int d_out, int d_in, uint16_t* y, hipStream_t stream) {
-  // 8 waves, two per SIMD; tiles are dealt in rounds over the 256 CUs.
-  constexpr int kCUs = 256;
+// Rows [0, d_out) of the slab at w with 256-token tiles (rows of y ldy apart).
+hipError_t launch_256(const uint16_t* x, int M, const uint16_t* w, const uint8_t* packed_bytes,
+                      const float* alpha, int per_row, int d_out, int d_in, uint16_t* y, int ldy,
+                      hipStream_t stream) {
+  // 8 waves, two per SIMD; tiles are dealt in rounds over the CUs.
   const long ntm = (M + BM - 1) / BM;
   const long tiles256 = ntm * ((d_out + 255) / 256);
   const long full = tiles256 / kCUs;
@@ -324,21 +526,50 @@ hipError_t launch_linear_prefill(const uint16_t* x, int M, const uint16_t* w,
     const long n_split = (full * kCUs / ntm) * 256;
     if (n_split > 0 && n_split < d_out) {
       hipError_t e = launch_cfg<256, 4, 2>(x, M, w, packed_bytes, alpha, per_row, (int)n_split,
-                                           d_in, y, d_out, stream);
+                                           d_in, y, ldy, stream);
       if (e != hipSuccess) return e;
       return launch_cfg<128, 4, 2>(x, M, w + n_split * d_in, packed_bytes + n_split * (d_in / 8),
                                    per_row ? alpha + n_split : alpha, per_row,
-                                   d_out - (int)n_split, d_in, y + n_split, d_out, stream);
+                                   d_out - (int)n_split, d_in, y + n_split, ldy, stream);
     }
   }
   // Fewer tiles than CUs, or whole rounds: 256-wide tiles unless their last
   // round would leave more than a quarter of the CUs idle.
   const long rounds256 = (tiles256 + kCUs - 1) / kCUs;
   if (4 * tiles256 >= 3 * kCUs * rounds256)
-    return launch_cfg<256, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, d_out,
+    return launch_cfg<256, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy,
                                  stream);
-  return launch_cfg<128, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, d_out,
+  return launch_cfg<128, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy,
                                stream);
+}
+
+}  // namespace
+
+hipError_t launch_linear_prefill(const uint16_t* x, int M, const uint16_t* w,
+                                 const uint8_t* packed_bytes, const float* alpha, int per_row,
+                                 int d_out, int d_in, uint16_t* y, hipStream_t stream) {
+  // The producer/consumer 512 x 128 tiles take the rows that fill whole
+  // rounds over the CUs, when their token padding is at most 10% above that
+  // of 256-token tiles; the remaining rows (or the whole product) go to the
+  // 256-token tiles.
+  const long ntm = (M + BM - 1) / BM;
+  const long ntm_pc = (M + PC_BM - 1) / PC_BM;
+  if (d_in <= kPcMaxDin && 10 * ntm_pc * PC_BM <= 11 * ntm * BM) {
+    const long tiles = ntm_pc * ((d_out + PC_BN - 1) / PC_BN);
+    const long full = tiles / kCUs;
+    if (full >= 1) {
+      const long rows = tiles % kCUs == 0 ? d_out : (full * kCUs / ntm_pc) * PC_BN;
+      if (rows >= d_out)
+        return launch_pc(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, d_out, stream);
+      hipError_t e =
+          launch_pc(x, M, w, packed_bytes, alpha, per_row, (int)rows, d_in, y, d_out, stream);
+      if (e != hipSuccess) return e;
+      return launch_256(x, M, w + rows * d_in, packed_bytes + rows * (d_in / 8),
+                        per_row ? alpha + rows : alpha, per_row, d_out - (int)rows, d_in,
+                        y + rows, d_out, stream);
+    }
+  }
+  return launch_256(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, d_out, stream);
 }
 
 }  // namespace bd

@@ -189,6 +189,37 @@ def test_linear_prefill_ragged(shape, m):
     assert_y_close(y, oracle_y(x, wb, packed, alpha, mode), f"prefill {shape} M={m}")
 
 
+# Prefill shapes that take each tile path of the launcher: 512 x 128
+# producer/consumer tiles over whole rounds of the 256 CUs with the remaining
+# rows on 256-token tiles, producer/consumer tiles alone, 256 x 256 tiles over
+# whole rounds with the rest as 256 x 128 tiles (token padding rules out the
+# 512-row tiles at M = 600), and 256 x 128 tiles alone (4096 x 4096, M = 2048).
+# (M, d_out, d_in, mode, first row past the first launch or None)
+PREFILL_PATHS = [
+    (1000, 16677, 192, 1, 16384),
+    (1024, 16384, 320, 0, None),
+    (272, 33024, 192, 0, 32768),
+    (600, 22056, 128, 1, 21760),
+    (2048, 4096, 4096, 1, None),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_PATHS, ids=lambda c: f"M{c[0]}_{c[1]}x{c[2]}")
+def test_linear_prefill_tile_paths(case):
+    m, d_out, d_in, mode, split = case
+    wb, wf = S.small_pair(d_out, d_in, 0.02, 1e-3, seed=d_out + m)
+    x = S.draw_activations(m, d_in, S.generator(m + 5))
+    wb, wf, x = to_dev(wb, wf, x)
+    packed, alpha = T.compress(wf, wb, mode)
+    y = T.linear(x, wb, packed, alpha, mode)
+    rows = set(_sample_rows(d_out, 40, d_in + m).tolist()) | {127, 128, 255, 256}
+    if split is not None:
+        rows |= {split - 129, split - 128, split - 1, split, split + 1, split + 127, split + 128}
+    rows = np.array(sorted(r for r in rows if 0 <= r < d_out))
+    assert_y_close(y[:, torch.as_tensor(rows, device=DEV)],
+                   oracle_y(x, wb, packed, alpha, mode, rows=rows), f"prefill path {case}")
+
+
 @pytest.mark.parametrize("m", [3, 300])
 def test_linear_one_hot_extracts_columns(m):
     """x = e_c picks column c of W_eff: any bit-order, axis or layout slip in
