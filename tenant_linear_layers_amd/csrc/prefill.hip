@@ -72,6 +72,12 @@ __device__ __forceinline__ u32x4 bload128(const void* base, int nbytes, int voff
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
+__device__ __forceinline__ uint32_t bload32(const void* base, int nbytes, int voff, int soff) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
 __device__ __forceinline__ uint32_t bload8(const void* base, int nbytes, int voff, int soff) {
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
@@ -311,9 +317,13 @@ constexpr int PC_WSTAGE = PC_BN * 128;
 constexpr int PC_THREADS = 768;
 // x of one tile is addressed with 32-bit buffer offsets: 512 rows of d_in.
 constexpr int64_t kPcMaxDin = kPrefillMaxTileBytes / (PC_BM * 2) / 64 * 64;
+// x larger than this (a quarter of the 256 MB last-level cache) is
+// prefetched into L2 two steps ahead.
+constexpr int64_t kPcPrefetchXBytes = 64ll << 20;
 
 __device__ __forceinline__ int pc_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
+template <bool XPF>
 __global__ __launch_bounds__(PC_THREADS, 1) void prefill_pc_kernel(
     const uint16_t* __restrict__ x, int M, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ bits8, const float* __restrict__ alpha, int per_row, int d_out,
@@ -390,20 +400,33 @@ __global__ __launch_bounds__(PC_THREADS, 1) void prefill_pc_kernel(
       for (int i = 0; i < NB; ++i)
         *reinterpret_cast<u32x4*>(ws + woff0 + i * 4096) = rebuild8(rb[i], rs[i], ab[i]);
     };
+    // With XPF, one dword of each of the tile's 512 x rows two steps ahead
+    // is loaded as well, which brings those 128-byte segments into L2 a step
+    // before they are staged (for x too large to stay in the last-level
+    // cache).  The loaded values only feed a dummy sum.
+    uint32_t sink = 0, pf0 = 0, pf1 = 0;
+    const int pfv0 = 2 * T * d_in * 2;
+    const int pfv1 = (2 * T + 1) * d_in * 2;
     // Step kt: x of step kt+1 into the free x stage, raw weights of step
     // kt+2 into rb_load, W_eff of step kt+1 (rb_use, loaded a step earlier)
     // into the free weight stage; the barrier waits for x and the LDS
-    // stores and leaves the weight loads in flight.  Prefetches past the
-    // last step re-read it into buffers nobody reads.
+    // stores and leaves the weight loads (and prefetches) in flight.
+    // Prefetches past the last step re-read it into buffers nobody reads.
     auto pstep = [&](int kt, unsigned char* xs_next, unsigned char* ws_next,
                      const u32x4 (&rb_use)[NB], const uint32_t (&rs_use)[NB],
                      u32x4 (&rb_load)[NB], uint32_t (&rs_load)[NB]) {
+      if constexpr (XPF) sink ^= pf0 ^ pf1;
       xload(min(kt + 1, nk - 1), xs_next);
       __builtin_amdgcn_sched_barrier(0);
       wload(min(kt + 2, nk - 1), rb_load, rs_load);
+      if constexpr (XPF) {
+        const int so = min(kt + 2, nk - 1) * BK * 2;
+        pf0 = bload32(xbase, xbytes, pfv0, so);
+        pf1 = bload32(xbase, xbytes, pfv1, so);
+      }
       __builtin_amdgcn_sched_barrier(0);
       build(ws_next, rb_use, rs_use);
-      step_barrier<2 * NB>();
+      step_barrier<2 * NB + (XPF ? 2 : 0)>();
     };
     xload(0, X0);
     wload(0, rb0, rs0);
@@ -418,6 +441,8 @@ __global__ __launch_bounds__(PC_THREADS, 1) void prefill_pc_kernel(
     }
     if (kt < nk) pstep(kt, X1, W1, rb1, rs1, rb0, rs0);
     __builtin_amdgcn_s_waitcnt(0);
+    // keeps the prefetch loads alive; d_out is never negative
+    if (XPF && (sink ^ pf0 ^ pf1) == 0x9E3779B9u && d_out < 0) y[0] = 0;
     return;
   }
 
@@ -490,8 +515,14 @@ hipError_t launch_pc(const uint16_t* x, int M, const uint16_t* w, const uint8_t*
   const int ntn = (d_out + PC_BN - 1) / PC_BN;
   const int tiles = ntm * ntn;
   const int chunk = (tiles + 7) / 8;
-  hipLaunchKernelGGL(prefill_pc_kernel, dim3(8 * chunk), dim3(PC_THREADS), 0, stream, x, M, w,
-                     packed_bytes, alpha, per_row, d_out, d_in, y, ldy, ntm, ntn, chunk);
+  // Measured: the L2 prefetch of x pays for the 70B down projection (x of
+  // 117 MB, 3% faster) and costs 8-12% where x stays in the last-level cache.
+  if ((int64_t)M * d_in * 2 > kPcPrefetchXBytes)
+    hipLaunchKernelGGL(prefill_pc_kernel<true>, dim3(8 * chunk), dim3(PC_THREADS), 0, stream, x,
+                       M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy, ntm, ntn, chunk);
+  else
+    hipLaunchKernelGGL(prefill_pc_kernel<false>, dim3(8 * chunk), dim3(PC_THREADS), 0, stream, x,
+                       M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy, ntm, ntn, chunk);
   return hipGetLastError();
 }
 
@@ -533,14 +564,18 @@ hipError_t launch_256(const uint16_t* x, int M, const uint16_t* w, const uint8_t
                                    d_out - (int)n_split, d_in, y + n_split, ldy, stream);
     }
   }
-  // Fewer tiles than CUs, or whole rounds: 256-wide tiles unless their last
-  // round would leave more than a quarter of the CUs idle.
+  // Fewer tiles than CUs, or whole rounds: the widest tiles (256, 128, then
+  // 64 rows) whose last round leaves at most a quarter of the CUs idle.
   const long rounds256 = (tiles256 + kCUs - 1) / kCUs;
   if (4 * tiles256 >= 3 * kCUs * rounds256)
     return launch_cfg<256, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy,
                                  stream);
-  return launch_cfg<128, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy,
-                               stream);
+  const long tiles128 = ntm * ((d_out + 127) / 128);
+  const long rounds128 = (tiles128 + kCUs - 1) / kCUs;
+  if (4 * tiles128 >= 3 * kCUs * rounds128)
+    return launch_cfg<128, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy,
+                                 stream);
+  return launch_cfg<64, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy, stream);
 }
 
 }  // namespace

@@ -193,7 +193,8 @@ def test_linear_prefill_ragged(shape, m):
 # producer/consumer tiles over whole rounds of the 256 CUs with the remaining
 # rows on 256-token tiles, producer/consumer tiles alone, 256 x 256 tiles over
 # whole rounds with the rest as 256 x 128 tiles (token padding rules out the
-# 512-row tiles at M = 600), and 256 x 128 tiles alone (4096 x 4096, M = 2048).
+# 512-row tiles at M = 600), 256 x 128 tiles alone (4096 x 4096, M = 2048) and
+# 256 x 64 tiles (2048 x 2048, M = 2048: 128-wide tiles would fill half a round).
 # (M, d_out, d_in, mode, first row past the first launch or None)
 PREFILL_PATHS = [
     (1000, 16677, 192, 1, 16384),
@@ -201,6 +202,7 @@ PREFILL_PATHS = [
     (272, 33024, 192, 0, 32768),
     (600, 22056, 128, 1, 21760),
     (2048, 4096, 4096, 1, None),
+    (2048, 2048, 320, 0, None),
 ]
 
 
@@ -218,6 +220,22 @@ def test_linear_prefill_tile_paths(case):
     rows = np.array(sorted(r for r in rows if 0 <= r < d_out))
     assert_y_close(y[:, torch.as_tensor(rows, device=DEV)],
                    oracle_y(x, wb, packed, alpha, mode, rows=rows), f"prefill path {case}")
+
+
+def test_linear_prefill_large_x_prefetch():
+    """x of more than 64 MiB (1024 x 32832) takes the producer/consumer tiles
+    with x prefetched into L2 two steps ahead; 513 steps (odd)."""
+    m, d_out, d_in = 1024, 16384, 32832
+    g = S.generator(71, DEV)
+    wb = S.draw_base(d_out, d_in, 0.02, g, DEV)
+    wf = S.draw_finetuned(wb, 1e-3, g)
+    x = S.draw_activations(m, d_in, g, DEV)
+    packed, alpha = T.compress(wf, wb, 1)
+    del wf
+    y = T.linear(x, wb, packed, alpha, 1)
+    rows = np.array(sorted(set(_sample_rows(d_out, 24, 72).tolist()) | {127, 128, 8191, 8192}))
+    assert_y_close(y[:, torch.as_tensor(rows, device=DEV)],
+                   oracle_y(x, wb, packed, alpha, 1, rows=rows), "prefill large x")
 
 
 @pytest.mark.parametrize("m", [3, 300])
