@@ -8,9 +8,8 @@
 //
 // One wave per row.  Lane k of a wave reads 16 bytes of each input per
 // 512-element chunk (elements 8k..8k+7), so every wave-wide load is a
-// contiguous 1 KiB.  The sign of element 8k+j is taken with one wave64
-// ballot per j; the eight 64-bit ballots are turned into the eight packed
-// words of the chunk by lanes 0..7, each doing one 8x8 bit transpose.
+// contiguous 1 KiB.  The lane's eight signs are exactly byte k of the chunk's
+// packed bits (least significant bit first), which the lane stores itself.
 // The scale is summed exactly in integers (floor(|d| * 2^48)), so the result
 // does not depend on the order of summation.
 #include "common.h"
@@ -23,19 +22,6 @@ namespace bd {
 namespace {
 
 constexpr int kRowsPerBlock = 4;  // one wave per row, 256 threads
-
-// Transpose an 8x8 bit matrix held as eight bytes (byte r = row r, bit c =
-// column c): the result holds bit r of byte c = input bit c of byte r.
-__device__ __forceinline__ uint64_t transpose8x8(uint64_t x) {
-  uint64_t t;
-  t = (x ^ (x >> 7)) & 0x00AA00AA00AA00AAull;
-  x = x ^ t ^ (t << 7);
-  t = (x ^ (x >> 14)) & 0x0000CCCC0000CCCCull;
-  x = x ^ t ^ (t << 14);
-  t = (x ^ (x >> 28)) & 0x00000000F0F0F0F0ull;
-  x = x ^ t ^ (t << 28);
-  return x;
-}
 
 __device__ __forceinline__ uint64_t wave_sum_u64(uint64_t v) {
 #pragma unroll
@@ -102,8 +88,7 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void compress_rows_kernel(
 
   const uint16_t* a_row = w_ft + (size_t)row * d_in;
   const uint16_t* b_row = w_base + (size_t)row * d_in;
-  const int n_words = d_in >> 6;
-  uint64_t* p_row = packed + (size_t)row * n_words;
+  uint8_t* p_bytes = reinterpret_cast<uint8_t*>(packed) + (size_t)row * (d_in >> 3);
 
   uint64_t acc = 0;
   uint32_t maxbits = 0;  // largest float bits of |d| * 2^16 (NaN bits sort above inf)
@@ -135,14 +120,14 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void compress_rows_kernel(
         va[u] = u32x4{0u, 0u, 0u, 0u};
         vb[u] = u32x4{0u, 0u, 0u, 0u};
       }
-      uint64_t ball[8];
+      uint32_t sbyte = 0;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const uint32_t ua = (j & 1) ? (va[u][j >> 1] & 0xFFFF0000u) : (va[u][j >> 1] << 16);
         const uint32_t ub = (j & 1) ? (vb[u][j >> 1] & 0xFFFF0000u) : (vb[u][j >> 1] << 16);
         const float d = __uint_as_float(ua) - __uint_as_float(ub);
         // sign bit 1 <=> +1 <=> not (d < 0): +0, -0 and NaN give +1.
-        ball[j] = __builtin_amdgcn_ballot_w64(!(d < 0.0f));
+        sbyte |= (d < 0.0f) ? 0u : (1u << j);
         const float ad = __builtin_fabsf(d) * 65536.0f;
         maxbits = max(maxbits, __float_as_uint(ad));
         // Conversions saturate for out-of-range values; such rows are
@@ -151,14 +136,10 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void compress_rows_kernel(
         const uint32_t lo = (uint32_t)(__builtin_amdgcn_fractf(ad) * 4294967296.0f);
         acc += ((uint64_t)hi << 32) | lo;
       }
-      if (lane < 8) {
-        // word `lane` of this chunk: bit 8i+j comes from ballot j, bit 8*lane+i.
-        uint64_t x = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x |= ((ball[j] >> (lane << 3)) & 0xFFull) << (j << 3);
-        const int w = (c << 3) + lane;
-        if (w < n_words) p_row[w] = transpose8x8(x);
-      }
+      // Byte `lane` of the chunk's 64 packed bytes holds its elements
+      // 8*lane .. 8*lane+7 (bit j = element 8*lane+j): one byte store per
+      // lane, 64 contiguous bytes per wave.
+      if ((c << 9) + (lane << 3) < d_in) p_bytes[(c << 6) + lane] = (uint8_t)sbyte;
     }
   }
 
@@ -205,7 +186,8 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void compress_rows_kernel(
 
 // Per-matrix scale: sum the per-row limbs with 128-bit integers (exact and
 // order independent) and round once.
-constexpr int kFinalizeThreads = 256;
+constexpr int kFinalizeThreads = 1024;
+constexpr int kFinalizeUnroll = 4;  // rows whose loads are in flight together
 
 __global__ __launch_bounds__(kFinalizeThreads) void compress_finalize_kernel(
     const uint64_t* __restrict__ partial, int d_out, uint64_t n, float* __restrict__ alpha) {
@@ -214,14 +196,24 @@ __global__ __launch_bounds__(kFinalizeThreads) void compress_finalize_kernel(
   __shared__ uint32_t s_bad[kFinalizeThreads];
   unsigned __int128 hi = 0, lo = 0;
   uint32_t bad = 0;
-  for (int r = threadIdx.x; r < d_out; r += kFinalizeThreads) {
-    const uint64_t h = partial[2 * (size_t)r];
-    if (h == ~0ull) {
-      bad = 1;
-    } else {
-      hi += h;
+  for (int r0 = threadIdx.x; r0 < d_out; r0 += kFinalizeThreads * kFinalizeUnroll) {
+    uint64_t h[kFinalizeUnroll], l[kFinalizeUnroll];
+#pragma unroll
+    for (int u = 0; u < kFinalizeUnroll; ++u) {
+      const int r = min(r0 + u * kFinalizeThreads, d_out - 1);
+      h[u] = partial[2 * (size_t)r];
+      l[u] = partial[2 * (size_t)r + 1];
     }
-    lo += partial[2 * (size_t)r + 1];
+#pragma unroll
+    for (int u = 0; u < kFinalizeUnroll; ++u) {
+      if (r0 + u * kFinalizeThreads >= d_out) continue;  // re-read row, not counted
+      if (h[u] == ~0ull) {
+        bad = 1;
+      } else {
+        hi += h[u];
+      }
+      lo += l[u];
+    }
   }
   s_hi[threadIdx.x] = hi;
   s_lo[threadIdx.x] = lo;
