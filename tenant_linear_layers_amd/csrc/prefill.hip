@@ -6,12 +6,20 @@
 // is formed in fast on-chip memory (here LDS) inside the matmul kernel and
 // never written to HBM.
 //
-// Tile: 256 tokens x BN output rows x 64 of d_in per step, 8 waves as 4 x 2,
-// each owning 64 x (BN/2) outputs in MFMA 32x32x16 tiles (float32
-// accumulators).  Two LDS stages: while the MFMAs read one, the other is
-// filled for the next step.  Raw weights are loaded two steps ahead into two
-// register sets, so the rebuild of step k+1 (from registers that have already
-// arrived) is spread over the four 16-wide MFMA sub-steps of step k.
+// Two kernels, chosen per product by launch_linear_prefill:
+//  - prefill_pc_kernel (further below): 512-token tiles with producer waves
+//    that stage x and rebuild W_eff beside the MFMA waves, for the rows that
+//    fill whole rounds of the CUs;
+//  - prefill_kernel (this comment): 256-token tiles in which every wave both
+//    rebuilds and multiplies, for the rest.
+//
+// prefill_kernel tile: 256 tokens x BN output rows x 64 of d_in per step, 8
+// waves as 4 x 2, each owning 64 x (BN/2) outputs in MFMA 32x32x16 tiles
+// (float32 accumulators).  Two LDS stages: while the MFMAs read one, the
+// other is filled for the next step.  Raw weights are loaded two steps ahead
+// into two register sets, so the rebuild of step k+1 (from registers that
+// have already arrived) is spread over the four 16-wide MFMA sub-steps of
+// step k.
 //  * x goes from global memory straight into LDS (buffer loads to LDS, 16
 //    bytes per lane, no registers): each wave instruction writes one 8-row
 //    block of 1 KB; chunk c of row r sits at position c ^ (r % 8) of its
@@ -29,7 +37,7 @@ namespace bd {
 namespace {
 
 constexpr int BM = 256;
-constexpr int kCUs = 256;          // MI355X compute units: one tile per CU per round
+constexpr int kCUs = 256;           // MI355X compute units: one tile per CU per round
 constexpr int BK = 64;
 constexpr int ABLK = 1152;          // bytes per 8-row block of the x stage (1 KB + 128 B skew)
 constexpr int A_STAGE = 32 * ABLK;  // 256 rows
