@@ -7,11 +7,11 @@
 // never written to HBM.
 //
 // Two kernels, chosen per product by launch_linear_prefill:
-//  - prefill_pc_kernel (further below): 512-token tiles with producer waves
-//    that stage x and rebuild W_eff beside the MFMA waves, for the rows that
-//    fill whole rounds of the CUs;
+//  - prefill_pc_kernel (further below): 512- or 256-token x 128-row tiles
+//    with producer waves that stage x and rebuild W_eff beside the MFMA
+//    waves; 512-token tiles take the rows that fill whole rounds of the CUs;
 //  - prefill_kernel (this comment): 256-token tiles in which every wave both
-//    rebuilds and multiplies, for the rest.
+//    rebuilds and multiplies, 256 or 64 rows wide, for the rest.
 //
 // prefill_kernel tile: 256 tokens x BN output rows x 64 of d_in per step, 8
 // waves as 4 x 2, each owning 64 x (BN/2) outputs in MFMA 32x32x16 tiles
@@ -307,22 +307,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void prefill_kernel(
 }
 
 // ------------------------------------------------- producer/consumer tiles
-// Tile: 512 tokens x 128 output rows x 64 of d_in per step, 12 waves.  Waves
-// 0..7 (4 x 2, each 128 x 64 outputs in MFMA 32x32x16 tiles) only read the
-// LDS stages and multiply; waves 8..11 are producers: they stage x with
-// buffer loads to LDS and rebuild W_eff into the next weight stage, so the
-// rebuild's ALU work runs in waves of its own beside the MFMA waves instead
-// of inside their instruction streams.  Twice the token rows of the 256-row
-// tile halve the rebuild work per MFMA.  LDS holds two x stages of 64 KB and
-// two weight stages of 16 KB (160 KB), rows of 128 bytes with chunk c of row
-// r at position c ^ ((r / 2) % 8): the MFMA operand reads (16 consecutive
-// rows at one chunk per 256 bytes of banks) are conflict free without
-// padding.  One barrier per step for all 12 waves.
+// Tile: TBM (512 or 256) tokens x 128 output rows x 64 of d_in per step.
+// WM x WN MFMA waves (4 x 2: each (TBM/4) x 64 outputs in MFMA 32x32x16
+// tiles) only read the LDS stages and multiply; 4 producer waves follow
+// them: they stage x with buffer loads to LDS and rebuild W_eff into the
+// next weight stage, so the rebuild's ALU work runs in waves of its own
+// beside the MFMA waves instead of inside their instruction streams.  512
+// token rows per weight tile halve the rebuild work per MFMA against 256.
+// LDS holds two x stages of TBM x 128 bytes and two weight stages of 16 KB
+// (160 KB at 512 tokens), rows of 128 bytes with chunk c of row r at
+// position c ^ ((r / 2) % 8): the MFMA operand reads (16 consecutive rows at
+// one chunk per 256 bytes of banks) are conflict free without padding.  One
+// barrier per step for all waves.
 constexpr int PC_BM = 512;
 constexpr int PC_BN = 128;
-constexpr int PC_XSTAGE = PC_BM * 128;
 constexpr int PC_WSTAGE = PC_BN * 128;
-constexpr int PC_THREADS = 768;
 // x of one tile is addressed with 32-bit buffer offsets: 512 rows of d_in.
 constexpr int64_t kPcMaxDin = kPrefillMaxTileBytes / (PC_BM * 2) / 64 * 64;
 // x larger than this (a quarter of the 256 MB last-level cache) is
@@ -331,41 +330,44 @@ constexpr int64_t kPcPrefetchXBytes = 64ll << 20;
 
 __device__ __forceinline__ int pc_swz(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-template <bool XPF>
-__global__ __launch_bounds__(PC_THREADS, 1) void prefill_pc_kernel(
+template <bool XPF, int TBM, int WM, int WN>
+__global__ __launch_bounds__(64 * (WM * WN + 4), 1) void prefill_pc_kernel(
     const uint16_t* __restrict__ x, int M, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ bits8, const float* __restrict__ alpha, int per_row, int d_out,
     int d_in, uint16_t* __restrict__ y, int ldy, int ntm, int ntn, int chunk) {
-  constexpr int WM = 4, WN = 2;
-  constexpr int TMW = PC_BM / WM / 32;  // 4
-  constexpr int TNW = PC_BN / WN / 32;  // 2
+  constexpr int NMW = WM * WN;          // MFMA waves; 4 producer waves follow
+  constexpr int TMW = TBM / WM / 32;    // 32-row MFMA tiles per wave
+  constexpr int TNW = PC_BN / WN / 32;  // 32-column MFMA tiles per wave
+  constexpr int XSTAGE = TBM * 128;
+  static_assert(TMW >= 1 && TNW >= 1, "tile shape");
+  static_assert(!XPF || TBM == 512, "x prefetch covers 512 rows");
   constexpr int NB = 4;                 // weight pieces per producer thread per step
-  constexpr int AI = 16;                // 8-row x blocks per producer wave per step
-  __shared__ __attribute__((aligned(16))) unsigned char X0[PC_XSTAGE];
-  __shared__ __attribute__((aligned(16))) unsigned char X1[PC_XSTAGE];
+  constexpr int AI = TBM / 32;          // 8-row x blocks per producer wave per step
+  __shared__ __attribute__((aligned(16))) unsigned char X0[XSTAGE];
+  __shared__ __attribute__((aligned(16))) unsigned char X1[XSTAGE];
   __shared__ __attribute__((aligned(16))) unsigned char W0[PC_WSTAGE];
   __shared__ __attribute__((aligned(16))) unsigned char W1[PC_WSTAGE];
 
   // contiguous tile ranges per XCD, token tile fastest (as in prefill_kernel)
   const int tile = (blockIdx.x & 7) * chunk + (blockIdx.x >> 3);
   if (tile >= ntm * ntn) return;
-  const int m0 = (tile % ntm) * PC_BM;
+  const int m0 = (tile % ntm) * TBM;
   const int n0 = (tile / ntm) * PC_BN;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int nk = d_in / BK;
 
-  if (wv >= 8) {
+  if (wv >= NMW) {
     // ------------------------------------------------------------ producers
-    const int pw = wv - 8;
-    const int T = threadIdx.x - 512;
+    const int pw = wv - NMW;
+    const int T = threadIdx.x - 64 * NMW;
     const int lr = T >> 3;  // 0..31: weight row within a 32-row pass
     const int lc = T & 7;   // 16-byte chunk within the 64-wide step
     // x rows past M lie beyond the resource and read as zero.  Block b of
     // the tile holds rows 8b..8b+7; lane (r, p) fetches chunk p ^ ((row/2)%8)
     // of row 8b + r, whose swizzle depends on the block's parity only.
     const uint16_t* xbase = x + (size_t)m0 * d_in;
-    const int xbytes = min(PC_BM, M - m0) * d_in * 2;
+    const int xbytes = min(TBM, M - m0) * d_in * 2;
     int xv[2];
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
@@ -463,7 +465,7 @@ __global__ __launch_bounds__(PC_THREADS, 1) void prefill_pc_kernel(
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
     const int c = 2 * ks + (lane >> 5);
-    const int ra = wm * (PC_BM / WM) + (lane & 31);
+    const int ra = wm * (TBM / WM) + (lane & 31);
     aoff[ks] = ra * 128 + 16 * pc_swz(ra, c);
     const int rw = wn * (PC_BN / WN) + (lane & 31);
     boff[ks] = rw * 128 + 16 * pc_swz(rw, c);
@@ -508,30 +510,40 @@ __global__ __launch_bounds__(PC_THREADS, 1) void prefill_pc_kernel(
       const int o = n0 + wn * (PC_BN / WN) + j * 32 + (lane & 31);
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int m = m0 + wm * (PC_BM / WM) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int m = m0 + wm * (TBM / WM) + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (m < M && o < d_out) y[(size_t)m * ldy + o] = f32_to_bf16_bits(acc[i][j][v]);
       }
     }
   }
 }
 
-hipError_t launch_pc(const uint16_t* x, int M, const uint16_t* w, const uint8_t* packed_bytes,
-                     const float* alpha, int per_row, int d_out, int d_in, uint16_t* y, int ldy,
-                     hipStream_t stream) {
+// Producer/consumer tiles of TBM tokens x 128 rows over rows [0, d_out) of
+// the slab at w (rows of y ldy apart).
+template <bool XPF, int TBM, int WM, int WN>
+hipError_t launch_pc_cfg(const uint16_t* x, int M, const uint16_t* w, const uint8_t* packed_bytes,
+                         const float* alpha, int per_row, int d_out, int d_in, uint16_t* y, int ldy,
+                         hipStream_t stream) {
   if (d_in > kPcMaxDin) return hipErrorInvalidValue;
-  const int ntm = (M + PC_BM - 1) / PC_BM;
+  const int ntm = (M + TBM - 1) / TBM;
   const int ntn = (d_out + PC_BN - 1) / PC_BN;
   const int tiles = ntm * ntn;
   const int chunk = (tiles + 7) / 8;
+  hipLaunchKernelGGL((prefill_pc_kernel<XPF, TBM, WM, WN>), dim3(8 * chunk),
+                     dim3(64 * (WM * WN + 4)), 0, stream, x, M, w, packed_bytes, alpha, per_row,
+                     d_out, d_in, y, ldy, ntm, ntn, chunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_pc(const uint16_t* x, int M, const uint16_t* w, const uint8_t* packed_bytes,
+                     const float* alpha, int per_row, int d_out, int d_in, uint16_t* y, int ldy,
+                     hipStream_t stream) {
   // Measured: the L2 prefetch of x pays for the 70B down projection (x of
   // 117 MB, 3% faster) and costs 8-12% where x stays in the last-level cache.
   if ((int64_t)M * d_in * 2 > kPcPrefetchXBytes)
-    hipLaunchKernelGGL(prefill_pc_kernel<true>, dim3(8 * chunk), dim3(PC_THREADS), 0, stream, x,
-                       M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy, ntm, ntn, chunk);
-  else
-    hipLaunchKernelGGL(prefill_pc_kernel<false>, dim3(8 * chunk), dim3(PC_THREADS), 0, stream, x,
-                       M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy, ntm, ntn, chunk);
-  return hipGetLastError();
+    return launch_pc_cfg<true, PC_BM, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in,
+                                            y, ldy, stream);
+  return launch_pc_cfg<false, PC_BM, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y,
+                                           ldy, stream);
 }
 
 // Output rows [0, d_out) of the slab starting at w (rows of y are ldy apart).
@@ -548,6 +560,18 @@ hipError_t launch_cfg(const uint16_t* x, int M, const uint16_t* w, const uint8_t
   hipLaunchKernelGGL((prefill_kernel<BN, WM, WN>), dim3(8 * chunk), dim3(64 * WM * WN), 0, stream,
                      x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy, ntm, ntn, chunk);
   return hipGetLastError();
+}
+
+// 256 tokens x 128 rows: producer/consumer tiles (8 MFMA waves of 64 x 64
+// outputs and 4 producers; measured 3-6% faster than the 8-wave kernel's
+// 256 x 128 tiles on every shape tried, with identical results).
+hipError_t launch_256x128(const uint16_t* x, int M, const uint16_t* w, const uint8_t* packed_bytes,
+                          const float* alpha, int per_row, int d_out, int d_in, uint16_t* y,
+                          int ldy, hipStream_t stream) {
+  if (d_in <= kPcMaxDin)
+    return launch_pc_cfg<false, 256, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y,
+                                           ldy, stream);
+  return launch_cfg<128, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy, stream);
 }
 
 // Rows [0, d_out) of the slab at w with 256-token tiles (rows of y ldy apart).
@@ -567,9 +591,9 @@ hipError_t launch_256(const uint16_t* x, int M, const uint16_t* w, const uint8_t
       hipError_t e = launch_cfg<256, 4, 2>(x, M, w, packed_bytes, alpha, per_row, (int)n_split,
                                            d_in, y, ldy, stream);
       if (e != hipSuccess) return e;
-      return launch_cfg<128, 4, 2>(x, M, w + n_split * d_in, packed_bytes + n_split * (d_in / 8),
-                                   per_row ? alpha + n_split : alpha, per_row,
-                                   d_out - (int)n_split, d_in, y + n_split, ldy, stream);
+      return launch_256x128(x, M, w + n_split * d_in, packed_bytes + n_split * (d_in / 8),
+                            per_row ? alpha + n_split : alpha, per_row, d_out - (int)n_split,
+                            d_in, y + n_split, ldy, stream);
     }
   }
   // Fewer tiles than CUs, or whole rounds: the widest tiles (256, 128, then
@@ -581,8 +605,7 @@ hipError_t launch_256(const uint16_t* x, int M, const uint16_t* w, const uint8_t
   const long tiles128 = ntm * ((d_out + 127) / 128);
   const long rounds128 = (tiles128 + kCUs - 1) / kCUs;
   if (4 * tiles128 >= 3 * kCUs * rounds128)
-    return launch_cfg<128, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy,
-                                 stream);
+    return launch_256x128(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy, stream);
   return launch_cfg<64, 4, 2>(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, ldy, stream);
 }
 

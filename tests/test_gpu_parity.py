@@ -192,9 +192,11 @@ def test_linear_prefill_ragged(shape, m):
 # Prefill shapes that take each tile path of the launcher: 512 x 128
 # producer/consumer tiles over whole rounds of the 256 CUs with the remaining
 # rows on 256-token tiles, producer/consumer tiles alone, 256 x 256 tiles over
-# whole rounds with the rest as 256 x 128 tiles (token padding rules out the
-# 512-row tiles at M = 600), 256 x 128 tiles alone (4096 x 4096, M = 2048) and
-# 256 x 64 tiles (2048 x 2048, M = 2048: 128-wide tiles would fill half a round).
+# whole rounds with the rest as 256 x 128 producer/consumer tiles (token
+# padding rules out the 512-row tiles at M = 600), 256 x 128 producer/consumer
+# tiles alone (4096 x 4096, M = 2048; and M = 200 with 193 row tiles, the last
+# one ragged, over an odd number of 64-wide steps) and 256 x 64 tiles
+# (2048 x 2048, M = 2048: 128-wide tiles would fill half a round).
 # (M, d_out, d_in, mode, first row past the first launch or None)
 PREFILL_PATHS = [
     (1000, 16677, 192, 1, 16384),
@@ -202,6 +204,7 @@ PREFILL_PATHS = [
     (272, 33024, 192, 0, 32768),
     (600, 22056, 128, 1, 21760),
     (2048, 4096, 4096, 1, None),
+    (200, 24600, 192, 1, None),
     (2048, 2048, 320, 0, None),
 ]
 
