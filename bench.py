@@ -457,7 +457,11 @@ def cpu_baseline(w: ProjWorkload, budget_s: float):
 COUNTER_BLOCKS = ("compress", "decode_m1", "decode_m4", "decode_m16", "multi", "prefill")
 CALIB_BYTES = 256 * 2**20
 LIB_KERNELS = ("compress_rows_kernel", "compress_finalize_kernel", "linear_decode_kernel",
-               "linear_multi_kernel", "prefill_kernel")
+               "linear_multi_kernel", "prefill_kernel", "prefill_pc_kernel")
+# kernel name that every launch of a counter block must carry
+BLOCK_KERNEL = {"compress": "compress_rows_kernel", "decode_m1": "linear_decode_kernel",
+                "decode_m4": "linear_decode_kernel", "decode_m16": "linear_decode_kernel",
+                "multi": "linear_multi_kernel", "prefill": "prefill_"}
 
 
 def counter_pass(w: ProjWorkload, n: int):
@@ -507,7 +511,11 @@ def summarize_counters(fetch_dir: str, write_dir: str, n: int, w_bytes: dict):
         factor = CALIB_BYTES / (1024.0 * sum(v for _, _, v in calib) / n)
         per[counter] = {"factor": factor, "calib_kernel": calib[0][1][:80]}
         for b, name in enumerate(COUNTER_BLOCKS):
-            vals = [v for _, _, v in lib[b * n:(b + 1) * n]]
+            block = lib[b * n:(b + 1) * n]
+            wrong = [k for _, k, _ in block if BLOCK_KERNEL[name] not in k]
+            if wrong:
+                raise SystemExit(f"{counter}: block {name} holds other kernels: {wrong[0][:80]}")
+            vals = [v for _, _, v in block]
             out.setdefault(name, {})[counter] = sum(vals) / n
     res = {}
     for name, c in out.items():
