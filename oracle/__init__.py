@@ -27,11 +27,13 @@ from .bitdelta_oracle import (  # noqa: F401
     bf16_bits_to_f32,
     compress,
     delta_f32,
+    f32_to_bf16_bits,
     fixed_point_scope_sums,
     linear,
     linear_dense,
     linear_multi,
     pack_sign_bits,
+    reconstruct,
     rne_ratio_to_f32_bits,
     sign_bits,
     unpack_sign_bits,

@@ -218,6 +218,39 @@ def linear_dense(x_bits, w_base_bits, packed, alpha, alpha_mode: int) -> np.ndar
     return x @ w_eff.T
 
 
+def f32_to_bf16_bits(f) -> np.ndarray:
+    """bf16 bit patterns (uint16) of float32 values, rounded to the nearest
+    bf16 with ties to the even pattern: add 0x7FFF plus the lowest kept bit to
+    the float32 bits, then keep the top 16 bits (a carry out of the mantissa
+    moves to the next binade, and past the largest finite value to
+    infinity).  Every NaN becomes the quiet NaN 0x7FC0."""
+    u = np.asarray(f, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    rounded = (u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))) >> np.uint64(16)
+    nan = (u & np.uint64(0x7FFFFFFF)) > np.uint64(0x7F800000)
+    return np.where(nan, np.uint64(0x7FC0), rounded).astype(np.uint16)
+
+
+def reconstruct(w_base_bits, packed, alpha, alpha_mode: int) -> np.ndarray:
+    """W_eff = W_base + alpha*sign(Delta), stored as bf16 (page: section
+    "Sunum mimarisi": the effective weight of the conceptual fused kernel,
+    which a server without the fused kernel writes out before a standard
+    matmul; "Matematiksel temel", the approximation W_ft ~ W_base +
+    alpha*sign(Delta)).
+
+    Per element: W_base widened to float32 (exact) plus +alpha_o or -alpha_o
+    in one float32 addition (nearest, ties to even), then rounded to bf16
+    (nearest, ties to even).  Returns bf16 bits, uint16 [d_out, d_in]."""
+    w = bf16_bits_to_f32(w_base_bits)
+    d_out, d_in = w.shape
+    s = unpack_sign_bits(packed, d_in)
+    # alpha arrives as float32, so this float64 -> float32 step is exact
+    a = _alpha_per_output(alpha, d_out, alpha_mode).astype(np.float32)
+    t = np.where(s > 0, a[:, None], -a[:, None]).astype(np.float32)
+    with np.errstate(invalid="ignore", over="ignore"):
+        v = (w + t).astype(np.float32, copy=False)
+    return f32_to_bf16_bits(v)
+
+
 def linear_multi(x_bits, variant_ids, w_base_bits, packed_list, alpha_list,
                  alpha_mode: int) -> np.ndarray:
     """Token batch that mixes variants (page: section "Sunum mimarisi", many

@@ -373,3 +373,104 @@ def test_multi_bad_id_gives_nan_row():
     x = bf16_bits(draw_activations(3, 64, generator(36)))
     y = O.linear_multi(x, np.array([0, 5, -2], np.int32), wb, packs, alphas, 1)
     assert np.all(np.isfinite(y[0])) and np.all(np.isnan(y[1])) and np.all(np.isnan(y[2]))
+
+
+# ------------------------------------------------------- unfused W_eff (bf16)
+@pytest.mark.parametrize("f32, bf16", [
+    (0x3F800000, 0x3F80),  # 1.0
+    (0x3F808000, 0x3F80),  # 1 + 2^-8: halfway, the even neighbour is 1.0
+    (0x3F818000, 0x3F82),  # 1 + 3*2^-8: halfway, the even neighbour is above
+    (0x3F808001, 0x3F81),  # just above halfway
+    (0x3F807FFF, 0x3F80),  # just below halfway
+    (0xBF818000, 0xBF82),  # negative ties round the magnitude the same way
+    (0x7F7FFFFF, 0x7F80),  # the largest float32 rounds up to +inf
+    (0x7F7F7FFF, 0x7F7F),  # below the halfway point of the largest bf16
+    (0xFF800000, 0xFF80),  # -inf
+    (0x80000000, 0x8000),  # -0
+    (0x00000001, 0x0000),  # the smallest subnormal rounds to +0
+    (0x00008000, 0x0000),  # subnormal tie, even neighbour 0
+    (0x00018000, 0x0002),  # subnormal tie, even neighbour above
+    (0x7FC00000, 0x7FC0),  # quiet NaN
+    (0xFFC00001, 0x7FC0),  # NaN with sign and payload
+    (0x7F800001, 0x7FC0),  # signalling NaN
+])
+def test_bf16_rounding_hand_derived(f32, bf16):
+    f = np.array([f32], dtype=np.uint32).view(np.float32)
+    assert int(O.f32_to_bf16_bits(f)[0]) == bf16
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(5)
+    u = rng.integers(0, 2**32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    # every exponent, and the patterns on both sides of each halfway point
+    u[:4096] = (u[:4096] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    u[4096:8192] = (u[4096:8192] & np.uint32(0xFFFF0000)) | np.uint32(0x7FFF)
+    f = u.view(np.float32)
+    f = f[~np.isnan(f)]
+    ref = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(O.f32_to_bf16_bits(f), ref)
+
+
+def test_reconstruct_constant_magnitude_gives_w_ft():
+    """A delta of constant magnitude c compresses to alpha = c, and W_eff
+    rebuilt from it is W_ft itself, bit for bit."""
+    rng = np.random.default_rng(23)
+    for m in (1, 3, 7):
+        j = rng.integers(-120, 121, size=(16, 192))
+        sgn = rng.choice([-1, 1], size=(16, 192))
+        wb = bf16_exact(j * 2.0 ** -12)
+        wf = bf16_exact((j + sgn * m) * 2.0 ** -12)
+        for mode in (0, 1):
+            packed, alpha = O.compress(wf, wb, mode)
+            np.testing.assert_array_equal(O.reconstruct(wb, packed, alpha, mode), wf)
+
+
+def test_reconstruct_alpha_zero_is_base():
+    wb, _ = small_case(24, 128, 3)
+    wb = np.where(wb & 0x7FFF == 0, np.uint16(0x3C00), wb)  # no signed zeros
+    packed = O.pack_sign_bits(np.random.default_rng(4).random((24, 128)) < 0.5)
+    np.testing.assert_array_equal(
+        O.reconstruct(wb, packed, np.zeros(24, np.float32), 1), wb)
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_reconstruct_is_a_bf16_neighbour_of_the_exact_sum(mode):
+    """Brute force per element: the exact W_base +- alpha (float64 holds it
+    exactly here) lies between two adjacent bf16 values; W_eff must be one of
+    them, and the nearer one unless the sum lies within float32 rounding
+    reach of the halfway point between them."""
+    d_out, d_in = 24, 256
+    wb, wf = small_case(d_out, d_in, 31)
+    packed, alpha = O.compress(wf, wb, mode)
+    if mode == 1:  # rows with scales of very different size
+        alpha = (alpha * np.float32(2.0) ** np.arange(d_out, dtype=np.float32) % 9).astype(np.float32)
+    r = O.reconstruct(wb, packed, alpha, mode)
+    w = O.bf16_bits_to_f32(wb).astype(np.float64)
+    s = O.unpack_sign_bits(packed, d_in).astype(np.float64)
+    a = np.broadcast_to(np.asarray(alpha, np.float64).reshape(-1, 1), (d_out, 1))
+    exact = w + s * a
+    assert np.all(exact != 0)
+    ulp = 2.0 ** (np.floor(np.log2(np.abs(exact))) - 7)
+    down = np.floor(exact / ulp) * ulp
+    up = down + ulp
+    got = O.bf16_bits_to_f32(r).astype(np.float64)
+    assert np.all((got == down) | (got == up))
+    nearer = np.where(exact - down < up - exact, down, up)
+    clear = np.abs((exact - down) - ulp / 2) > np.abs(exact) * 2.0 ** -24
+    np.testing.assert_array_equal(got[clear], nearer[clear])
+
+
+def test_reconstruct_rounds_twice_float32_then_bf16():
+    """1 + (2^-8 + 2^-30): the float32 sum is exactly halfway between the bf16
+    values 1 and 1 + 2^-7 and ties to 1.0, although the exact sum lies above
+    the halfway point (a single rounding would give 1 + 2^-7)."""
+    wb = bf16_exact(np.full((1, 64), 1.0))
+    packed = O.pack_sign_bits(np.ones((1, 64), bool))
+    alpha = np.array([2.0 ** -8 + 2.0 ** -30], np.float32)
+    assert float(alpha[0]) == 2.0 ** -8 + 2.0 ** -30
+    r = O.reconstruct(wb, packed, alpha, 0)
+    assert np.all(r == 0x3F80)
+    # minus sign: 1 - (2^-8 + 2^-30) rounds in float32 to 1 - 2^-8, which
+    # bf16 holds exactly (0x3F7F)
+    r = O.reconstruct(wb, O.pack_sign_bits(np.zeros((1, 64), bool)), alpha, 0)
+    assert np.all(r == 0x3F7F)
