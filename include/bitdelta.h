@@ -158,6 +158,27 @@ int bitdelta_linear_multi(const uint16_t* x, int64_t M, const int32_t* variant_i
                           int alpha_mode, int64_t d_out, int64_t d_in, uint16_t* y,
                           void* stream);
 
+/*
+ * bitdelta_reconstruct - the effective weight written out (unfused path):
+ *   W_eff[o, i] = bf16(W_base[o, i] + alpha_o * s[o, i])
+ * (section "Sunum mimarisi": the W_eff that the fused kernel keeps on chip;
+ * a server without it writes W_eff to memory and then runs a standard
+ * matmul; section "Matematiksel temel", W_ft ~ W_base + alpha*sign(Delta)).
+ * Per element one float32 addition of W_base and +alpha_o or -alpha_o, then
+ * rounding to bf16 (nearest even): the same values the prefill GEMM of
+ * bitdelta_linear multiplies by.  A NaN alpha gives NaN weights in its scope.
+ * Reads 2 + 1/8 bytes and writes 2 bytes per weight.
+ *
+ *   w_base  device, bf16 [d_out, d_in]
+ *   packed  device, uint64 [d_out, d_in/64]
+ *   alpha   device, float32 [1] or [d_out] (4-byte aligned)
+ *   w_eff   device, bf16 [d_out, d_in], written; must not overlap the inputs
+ * Returns BITDELTA_OK or an error status; nothing is enqueued on error.
+ */
+int bitdelta_reconstruct(const uint16_t* w_base, const uint64_t* packed, const float* alpha,
+                         int alpha_mode, int64_t d_out, int64_t d_in, uint16_t* w_eff,
+                         void* stream);
+
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* bitdelta_status_string(int status);
 

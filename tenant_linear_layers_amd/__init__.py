@@ -18,5 +18,6 @@ from .bitdelta import (  # noqa: F401
     linear,
     linear_multi,
     ratio_to_f32_bits,
+    reconstruct,
     status_string,
 )

@@ -38,6 +38,7 @@ EXPORTS = (
     "bitdelta_compress",
     "bitdelta_linear",
     "bitdelta_linear_multi",
+    "bitdelta_reconstruct",
     "bitdelta_status_string",
     "bitdelta_ratio_to_f32_bits",
 )
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
     L.bitdelta_linear_multi.argtypes = [vp, i64, vp, vp, ctypes.c_int32, vp, vp, i32, i64, i64,
                                         vp, vp]
     L.bitdelta_linear_multi.restype = i32
+    L.bitdelta_reconstruct.argtypes = [vp, vp, vp, i32, i64, i64, vp, vp]
+    L.bitdelta_reconstruct.restype = i32
     L.bitdelta_status_string.argtypes = [i32]
     L.bitdelta_status_string.restype = ctypes.c_char_p
     L.bitdelta_ratio_to_f32_bits.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64]
@@ -209,3 +212,23 @@ def linear_multi(x: torch.Tensor, variant_ids: torch.Tensor, w_base: torch.Tenso
                                          d_in, _ptr(y), _stream(stream))
     _check(st, "bitdelta_linear_multi")
     return y
+
+
+def reconstruct(w_base: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor,
+                alpha_mode: int, w_eff=None, stream=None) -> torch.Tensor:
+    """W_eff = bf16(W_base + alpha sign(Delta)), bf16 [d_out, d_in] (the unfused path)."""
+    _need(w_base, "w_base", torch.bfloat16)
+    dev = w_base.device
+    _need(packed, "packed", torch.int64, dev)
+    _need(alpha, "alpha", torch.float32, dev)
+    if w_base.dim() != 2:
+        raise ValueError("w_base must be 2-D")
+    d_out, d_in = w_base.shape
+    if w_eff is None:
+        w_eff = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=dev)
+    _need(w_eff, "w_eff", torch.bfloat16, dev)
+    with _on(dev):
+        st = lib().bitdelta_reconstruct(_ptr(w_base), _ptr(packed), _ptr(alpha), alpha_mode,
+                                        d_out, d_in, _ptr(w_eff), _stream(stream))
+    _check(st, "bitdelta_reconstruct")
+    return w_eff

@@ -204,3 +204,24 @@ BD_EXPORT int bitdelta_linear_multi(const uint16_t* x, int64_t M, const int32_t*
   }
   return BITDELTA_OK;
 }
+
+BD_EXPORT int bitdelta_reconstruct(const uint16_t* w_base, const uint64_t* packed,
+                                   const float* alpha, int alpha_mode, int64_t d_out,
+                                   int64_t d_in, uint16_t* w_eff, void* stream) {
+  if (!w_base || !packed || !alpha || !w_eff) return BITDELTA_ERR_NULL;
+  if (!shape_ok(d_out, d_in)) return BITDELTA_ERR_SHAPE;
+  if (alpha_mode != BITDELTA_ALPHA_PER_MATRIX && alpha_mode != BITDELTA_ALPHA_PER_ROW)
+    return BITDELTA_ERR_MODE;
+  if (!aligned16(w_base) || !aligned16(packed) || !aligned16(w_eff)) return BITDELTA_ERR_ALIGN;
+  if (reinterpret_cast<uintptr_t>(alpha) & 3u) return BITDELTA_ERR_ALIGN;
+  const size_t wbytes = (size_t)d_out * (size_t)d_in * 2u;
+  const size_t abytes = alpha_mode == BITDELTA_ALPHA_PER_ROW ? (size_t)d_out * 4u : 4u;
+  if (overlap(w_eff, wbytes, w_base, wbytes) || overlap(w_eff, wbytes, packed, wbytes / 16u) ||
+      overlap(w_eff, wbytes, alpha, abytes))
+    return BITDELTA_ERR_OVERLAP;
+  const int dev = check_device();
+  if (dev != BITDELTA_OK) return dev;
+  return status_of(bd::launch_reconstruct(w_base, reinterpret_cast<const uint8_t*>(packed), alpha,
+                                          alpha_mode == BITDELTA_ALPHA_PER_ROW, (int)d_out,
+                                          (int)d_in, w_eff, static_cast<hipStream_t>(stream)));
+}

@@ -36,6 +36,35 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (lo in bits 0..15), round to nearest even, one
+// instruction.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// Eight weights of one row: bf16(W_base + alpha*s), s from the sign byte
+// (bit j = element j, 1 = +1).  The sign of alpha is flipped by xor for -1:
+// bitop3 table 0x78 is a ^ (b & c).
+__device__ __forceinline__ u32x4 rebuild8(u32x4 w, uint32_t byte, uint32_t ab) {
+  const uint32_t nb = ~byte;
+  u32x4 out;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float lo = __uint_as_float(w[d] << 16);
+    const float hi = __uint_as_float(w[d] & 0xFFFF0000u);
+    const float slo =
+        __uint_as_float(__builtin_amdgcn_bitop3_b32(ab, nb << (31 - 2 * d), 0x80000000u, 0x78));
+    const float shi =
+        __uint_as_float(__builtin_amdgcn_bitop3_b32(ab, nb << (30 - 2 * d), 0x80000000u, 0x78));
+    out[d] = cvt_pk_bf16(lo + slo, hi + shi);
+  }
+  return out;
+}
+
 // Global loads that bypass nothing special but keep the 128-bit width explicit.
 __device__ __forceinline__ u32x4 ld128(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);

@@ -40,4 +40,10 @@ hipError_t launch_linear_prefill(const uint16_t* x, int M, const uint16_t* w,
                                  const uint8_t* packed_bytes, const float* alpha, int per_row,
                                  int d_out, int d_in, uint16_t* y, hipStream_t stream);
 
+// W_eff = bf16(W_base + alpha*s) of a whole matrix, written to out
+// [d_out, d_in] (the unfused path's materialisation).
+hipError_t launch_reconstruct(const uint16_t* w, const uint8_t* packed_bytes, const float* alpha,
+                              int per_row, int d_out, int d_in, uint16_t* out,
+                              hipStream_t stream);
+
 }  // namespace bd

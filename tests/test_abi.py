@@ -121,3 +121,18 @@ def test_multi_argument_errors():
     assert _c(f(A, 4, B, E, 2, pa, aa, 3, 8, 64, E + 65536, None)) == 4
     assert _c(f(A, 4, B, E, 2, pa, aa, 1, 8, 32, E + 65536, None)) == 2
     assert _c(f(A, 4, B, E, 2, pa, aa, 1, 8, 64, A, None)) == 9
+
+
+def test_reconstruct_argument_errors():
+    f = T.lib().bitdelta_reconstruct
+    assert _c(f(A, C, D, 1, 8, 64, None, None)) == 1
+    assert _c(f(None, C, D, 1, 8, 64, E, None)) == 1
+    assert _c(f(A, C, D, 1, 8, 96, E, None)) == 2          # d_in % 64
+    assert _c(f(A, C, D, 1, 0, 64, E, None)) == 2          # d_out = 0
+    assert _c(f(A, C, D, 7, 8, 64, E, None)) == 4
+    assert _c(f(A, C + 8, D, 1, 8, 64, E, None)) == 3
+    assert _c(f(A, C, D + 2, 1, 8, 64, E, None)) == 3      # alpha needs 4 bytes
+    assert _c(f(A, C, D, 1, 8, 64, E + 8, None)) == 3
+    assert _c(f(A, C, D, 1, 8, 64, A + 16, None)) == 9     # w_eff overlaps w_base
+    assert _c(f(A, C, D, 1, 8, 64, C, None)) == 9          # ... the packed signs
+    assert _c(f(A, C, E + 4, 1, 8, 64, E, None)) == 9      # ... per-row alpha

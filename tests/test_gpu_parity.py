@@ -472,6 +472,96 @@ def test_layer70b_prefill_full_size():
                        f"layer70b_prefill {name}")
 
 
+# ---------------------------------------------------------------- unfused W_eff
+def check_reconstruct(wb, packed, alpha, mode, rows=None):
+    """GPU W_eff vs oracle, bit for bit (NaN positions compared as NaN).
+    rows: sampled rows (W_eff row o depends on row o only)."""
+    w_eff = T.reconstruct(wb, packed, alpha, mode)
+    torch.cuda.synchronize()
+    if rows is None:
+        ref = O.reconstruct(bits16(wb), packed_u64(packed), alpha.cpu().numpy(), mode)
+        got = bits16(w_eff)
+    else:
+        ridx = torch.as_tensor(rows, device=DEV)
+        a = alpha[ridx] if mode == 1 else alpha
+        ref = O.reconstruct(bits16(wb[ridx]), packed_u64(packed[ridx]), a.cpu().numpy(), mode)
+        got = bits16(w_eff[ridx])
+    nan_ref = (ref & 0x7FFF) > 0x7F80
+    np.testing.assert_array_equal((got & 0x7FFF) > 0x7F80, nan_ref)
+    np.testing.assert_array_equal(got[~nan_ref], ref[~nan_ref])
+    return w_eff
+
+
+# 8-weight pieces per row: 8 .. 2048, one or two workgroups per row, 1, 2 or 4
+# pieces per thread, last workgroup of a row partly past it
+@pytest.mark.parametrize("shape", [(1, 64), (17, 192), (100, 320), (3, 2112), (5, 4096),
+                                   (7, 8256), (2, 16384)])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_reconstruct_ragged(shape, mode):
+    wb, wf = S.small_pair(*shape, 0.02, 1e-3, seed=shape[0] * 13 + shape[1] + mode)
+    wb, wf = to_dev(wb, wf)
+    packed, alpha = T.compress(wf, wb, mode)
+    check_reconstruct(wb, packed, alpha, mode)
+
+
+def test_reconstruct_constant_magnitude_gives_w_ft():
+    """A delta of constant magnitude compresses to alpha = |delta| and W_eff
+    rebuilt on the GPU is W_ft, bit for bit (no oracle involved)."""
+    rng = np.random.default_rng(17)
+    j = rng.integers(-120, 121, size=(40, 1024))
+    sgn = rng.choice([-1, 1], size=(40, 1024))
+    wb = _bf16(j * 2.0 ** -12)
+    wf = _bf16((j + 5 * sgn) * 2.0 ** -12)
+    for mode in (0, 1):
+        packed, alpha = T.compress(wf, wb, mode)
+        assert torch.equal(T.reconstruct(wb, packed, alpha, mode).view(torch.int16),
+                           wf.view(torch.int16))
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_reconstruct_nan_alpha_scope(mode):
+    wb, wf = S.small_pair(12, 576, 0.02, 1e-3, seed=9)
+    wf[5, 100] = float("inf")
+    wb, wf = to_dev(wb, wf)
+    packed, alpha = T.compress(wf, wb, mode)
+    w_eff = check_reconstruct(wb, packed, alpha, mode)
+    nan_rows = torch.isnan(w_eff.float()).all(dim=1).cpu().numpy()
+    expect = np.ones(12, bool) if mode == 0 else np.arange(12) == 5
+    np.testing.assert_array_equal(nan_rows, expect)
+
+
+def test_reconstruct_is_what_prefill_multiplies():
+    """x times the materialised W_eff (float64 on the host) agrees with the
+    fused prefill GEMM, which rebuilds the same bf16 W_eff tiles in LDS."""
+    wb, wf = S.small_pair(300, 640, 0.02, 1e-3, seed=19)
+    x = S.draw_activations(300, 640, S.generator(20))
+    wb, wf, x = to_dev(wb, wf, x)
+    packed, alpha = T.compress(wf, wb, 1)
+    w_eff = T.reconstruct(wb, packed, alpha, 1)
+    y = T.linear(x, wb, packed, alpha, 1)
+    ref = (O.bf16_bits_to_f32(bits16(x)).astype(np.float64)
+           @ O.bf16_bits_to_f32(bits16(w_eff)).astype(np.float64).T)
+    rel, mx = assert_y_close(y, ref, "prefill vs materialised W_eff")
+    assert rel < 2e-3  # only y's bf16 rounding and float32 accumulation differ
+
+
+def test_proj4096_reconstruct(proj4096):
+    wb, wf, _ = proj4096
+    packed, alpha = T.compress(wf, wb, 1)
+    check_reconstruct(wb, packed, alpha, 1, rows=_sample_rows(4096, 64, 5))
+
+
+def test_reconstruct_gate_full_size():
+    """28672 x 8192 (the 70B-shaped gate projection), per-matrix alpha:
+    sampled rows bit for bit."""
+    g = S.generator(61, DEV)
+    wb = S.draw_base(28672, 8192, 0.015, g, DEV)
+    wf = S.draw_finetuned(wb, 1e-3, g)
+    packed, alpha = T.compress(wf, wb, 0)
+    del wf
+    check_reconstruct(wb, packed, alpha, 0, rows=_sample_rows(28672, 24, 62))
+
+
 # ---------------------------------------------------------------- graph capture
 def test_graph_replays_match_eager():
     """Every entry point captured in one HIP graph: each replay, with eager
@@ -485,7 +575,8 @@ def test_graph_replays_match_eager():
     outs = dict(p=torch.empty_like(packs[0]), a=torch.empty_like(alphas[0]),
                 y4=torch.empty(4, 96, dtype=torch.bfloat16, device=DEV),
                 y100=torch.empty(100, 96, dtype=torch.bfloat16, device=DEV),
-                ym=torch.empty(4, 96, dtype=torch.bfloat16, device=DEV))
+                ym=torch.empty(4, 96, dtype=torch.bfloat16, device=DEV),
+                we=torch.empty(96, 512, dtype=torch.bfloat16, device=DEV))
     ws = torch.empty(T.compress_workspace_size(96, 512, 0), dtype=torch.uint8, device=DEV)
 
     def run():
@@ -493,6 +584,7 @@ def test_graph_replays_match_eager():
         T.linear(x4, wb, packs[1], alphas[1], 0, y=outs["y4"])
         T.linear(x100, wb, packs[2], alphas[2], 0, y=outs["y100"])
         T.linear_multi(x4, ids, wb, packs, alphas, 0, y=outs["ym"])
+        T.reconstruct(wb, packs[0], alphas[0], 0, w_eff=outs["we"])
 
     run()
     torch.cuda.synchronize()
