@@ -22,6 +22,13 @@ printed reports decode effective HBM GB/s (algorithmic bytes / kernel time)
 as `value`, the prefill TFLOP/s beside it, a roofline entry per kernel, and
 the CPU oracle timed on a bounded sample of the same workload.
 
+Outside the step, the line also carries the unfused A/B (`unfused_ab`): for
+each decode token count and for prefill, the fused call's kernel time, the
+time of bitdelta_reconstruct (W_eff written to HBM) plus the library GEMM on
+it (torch.mm, hipBLASLt), and that GEMM alone on a stored W_eff (a dense bf16
+layer of the same shape, no BitDelta at all).  Their graphs are checked
+against eager launches after each timed range.
+
 Counter runs (HBM traffic per launch, rocprofv3 FETCH_SIZE and WRITE_SIZE in
 two separate runs):
 
@@ -77,6 +84,7 @@ KERNEL_SOURCES = {
     "multi": ("decode.hip", "common.h", "internal.h"),
     "compress": ("compress.hip", "common.h", "scale_round.h"),
     "prefill": ("prefill.hip", "common.h", "internal.h"),
+    "reconstruct": ("reconstruct.hip", "common.h", "internal.h"),
 }
 
 
@@ -170,6 +178,17 @@ class ProjWorkload:
         self.y_multi = torch.empty(self.multi_m, 4096, dtype=torch.bfloat16, device=dev)
         self.y_prefill = torch.empty(self.prefill_m, 4096, dtype=torch.bfloat16, device=dev)
         self.c_out = [(torch.empty_like(packed), torch.empty_like(alpha)) for _ in range(2)]
+        # unfused A/B: W_eff written by bitdelta_reconstruct, and stored copies
+        # of it (one per rotation copy) for a plain library GEMM
+        self.w_eff = torch.empty(4096, 4096, dtype=torch.bfloat16, device=dev)
+        self.w_effs = []
+        for r in range(self.R):
+            p, a = self.vsets[r][0]
+            self.w_effs.append(T.reconstruct(self.bases[r], p, a, self.mode))
+        self.ys_dense = {m: torch.empty(m, 4096, dtype=torch.bfloat16, device=dev)
+                         for m in list(wl.tokens) + [self.prefill_m]}
+        self.x_dense = dict(self.xs)
+        self.x_dense[self.prefill_m] = self.x_prefill
         self.host = dict(wb=wb, wf=wf, xs=xs, more=more, x_multi=x_multi, ids=ids)
         self.k = 0
 
@@ -186,7 +205,8 @@ class ProjWorkload:
         n = 4096 * 4096
         pm = ProjWorkload.prefill_m
         out = {"compress": shell.compress_bytes(), "multi": shell.multi_bytes(),
-               "prefill": 2 * n + n // 8 + 4 * 4096 + 2 * pm * 4096 * 2}
+               "prefill": 2 * n + n // 8 + 4 * 4096 + 2 * pm * 4096 * 2,
+               "reconstruct": shell.reconstruct_bytes()}
         for m in wl.tokens:
             out[f"decode_m{m}"] = shell.decode_bytes(m)
         return out
@@ -207,6 +227,11 @@ class ProjWorkload:
         n = self.d_out * self.d_in
         alpha = 4 * (self.d_out if self.mode == 1 else 1)
         return 4 * n + n // 8 + alpha
+
+    def reconstruct_bytes(self):
+        n = self.d_out * self.d_in
+        alpha = 4 * (self.d_out if self.mode == 1 else 1)
+        return 2 * n + n // 8 + alpha + 2 * n
 
     def prefill_flops(self):
         return 2 * self.prefill_m * self.d_out * self.d_in
@@ -230,6 +255,14 @@ class ProjWorkload:
         p, a = self.vsets[r % self.R][0]
         T.linear(self.x_prefill, self.bases[r % self.R], p, a, self.mode, y=self.y_prefill)
 
+    def run_reconstruct(self, r):
+        p, a = self.vsets[r % self.R][0]
+        T.reconstruct(self.bases[r % self.R], p, a, self.mode, w_eff=self.w_eff)
+
+    def run_dense(self, m, r):
+        """The library GEMM (torch.mm, hipBLASLt) on a stored W_eff copy."""
+        torch.mm(self.x_dense[m], self.w_effs[r % self.R].t(), out=self.ys_dense[m])
+
     def one_pass(self, j):
         """One pass of the whole path (a step), on copies 6j .. 6j+5."""
         r = 6 * j
@@ -251,6 +284,13 @@ class ProjWorkload:
                                                             for r in range(c * self.R)])
         out["multi"] = (c * self.R, lambda: [self.run_multi(r) for r in range(c * self.R)])
         out["prefill"] = (c * 8, lambda: [self.run_prefill(r % 8) for r in range(c * 8)])
+        out["reconstruct"] = (c * self.R, lambda: [self.run_reconstruct(r)
+                                                   for r in range(c * self.R)])
+        for m in self.decode_ms:
+            out[f"dense_m{m}"] = (c * self.R, lambda m=m: [self.run_dense(m, r)
+                                                           for r in range(c * self.R)])
+        out[f"dense_m{self.prefill_m}"] = (c * 8, lambda: [self.run_dense(self.prefill_m, r % 8)
+                                                           for r in range(c * 8)])
         return out
 
 
@@ -284,6 +324,7 @@ class LayerWorkload:
         self.distinct = int(len(set(ids.tolist())))
         self.ys = [torch.empty(self.m, d_out, dtype=torch.bfloat16, device=dev)
                    for _, d_out, _ in wl.matrices]
+        self.ys_dense = [torch.empty_like(y) for y in self.ys]
         self.R = 1
         # operand copies per matrix: (x, W_base, packed list, alpha list)
         self.rot = []
@@ -303,6 +344,12 @@ class LayerWorkload:
         else:
             T.linear_multi(x, self.ids, wb, packs, alphas, self.mode, y=self.ys[i])
 
+    def run_dense(self, i, c=0):
+        """The library GEMM (torch.mm, hipBLASLt) on W_base alone: the base
+        model's dense bf16 layer of the same shape and tokens."""
+        x, wb, _, _ = self.rot[i][c % len(self.rot[i])]
+        torch.mm(x, wb.t(), out=self.ys_dense[i])
+
     def one_pass(self, j):
         for i in range(len(self.bases)):
             self.run(i)
@@ -312,6 +359,7 @@ class LayerWorkload:
         for i, (nm, _, _) in enumerate(self.wl.matrices):
             n = len(self.rot[i]) * RANGE_CYCLES
             out[f"{self.kind}_{nm}"] = (n, lambda i=i, n=n: [self.run(i, c) for c in range(n)])
+            out[f"dense_{nm}"] = (n, lambda i=i, n=n: [self.run_dense(i, c) for c in range(n)])
         return out
 
     def work(self, i):
@@ -347,6 +395,15 @@ class LayerWorkload:
             cfg["distinct_variants"] = self.distinct
         out = {"value": round(val, 2), "unit": unit, "config": cfg, "per_matrix": per,
                "roofline": roof, "layer_us": round(total_us, 2)}
+        if all(f"dense_{nm}" in avg_us for nm in names):
+            # the fused BitDelta layer against the base model's own dense layer
+            dense = {nm: avg_us[f"dense_{nm}"] for nm in names}
+            d_tot = sum(dense.values())
+            out["dense_base_ab"] = {
+                "per_matrix_us": {nm: {"fused": round(avg_us[f"{self.kind}_{nm}"], 2),
+                                       "dense_base": round(dense[nm], 2)} for nm in names},
+                "layer_fused_us": round(total_us, 2), "layer_dense_base_us": round(d_tot, 2),
+                "fused_over_dense_base": round(total_us / d_tot, 4)}
         if step_ms:
             # the same work over the measured one-pass steps (launch gaps and
             # the matrices' order included)
@@ -454,20 +511,23 @@ def cpu_baseline(w: ProjWorkload, budget_s: float):
 
 
 # ------------------------------------------------------------------ counters
-COUNTER_BLOCKS = ("compress", "decode_m1", "decode_m4", "decode_m16", "multi", "prefill")
+COUNTER_BLOCKS = ("compress", "decode_m1", "decode_m4", "decode_m16", "multi", "prefill",
+                  "reconstruct")
 CALIB_BYTES = 256 * 2**20
 LIB_KERNELS = ("compress_rows_kernel", "compress_finalize_kernel", "linear_decode_kernel",
-               "linear_multi_kernel", "prefill_kernel", "prefill_pc_kernel")
+               "linear_multi_kernel", "prefill_kernel", "prefill_pc_kernel", "reconstruct_kernel")
 # kernel name that every launch of a counter block must carry
 BLOCK_KERNEL = {"compress": "compress_rows_kernel", "decode_m1": "linear_decode_kernel",
                 "decode_m4": "linear_decode_kernel", "decode_m16": "linear_decode_kernel",
-                "multi": "linear_multi_kernel", "prefill": "prefill_"}
+                "multi": "linear_multi_kernel", "prefill": "prefill_",
+                "reconstruct": "reconstruct_kernel"}
 
 
 def counter_pass(w: ProjWorkload, n: int):
     """n eager launches of each kernel of the step, block by block, each on its
     own rotation copy; then n launches of the calibration kernel."""
-    run = {"compress": w.run_compress, "multi": w.run_multi, "prefill": w.run_prefill}
+    run = {"compress": w.run_compress, "multi": w.run_multi, "prefill": w.run_prefill,
+           "reconstruct": w.run_reconstruct}
     for m in w.decode_ms:
         run[f"decode_m{m}"] = lambda r, m=m: w.run_decode(m, r)
     for name in COUNTER_BLOCKS:
@@ -531,7 +591,7 @@ def write_counter_profiles(res, per, n):
            f"bench.py --counter-pass --counter-launches {n}; the same with WRITE_SIZE into OUT_W; "
            f"python bench.py --summarize-counters OUT_F OUT_W --counter-launches {n}")
     groups = {"decode": ["decode_m1", "decode_m4", "decode_m16"], "compress": ["compress"],
-              "multi": ["multi"], "prefill": ["prefill"]}
+              "multi": ["multi"], "prefill": ["prefill"], "reconstruct": ["reconstruct"]}
     for kernel, labels in groups.items():
         rec = {"kernel": kernel, "workload": "proj_4096",
                "sources_digest": sources_digest(KERNEL_SOURCES[kernel]),
@@ -631,6 +691,15 @@ def main():
         w.run_decode(16, 0)
         torch.cuda.synchronize()
         assert torch.equal(w.ys[16], y_eager), "graph replay differs from eager launch"
+        # eager references of the unfused A/B outputs, checked again after
+        # every timed replay below
+        eager_ref = {}
+        for m in list(w.decode_ms) + [w.prefill_m]:
+            w.run_dense(m, 0)
+            eager_ref[f"dense_m{m}"] = (w.ys_dense[m], w.ys_dense[m].clone())
+        w.run_reconstruct(0)
+        eager_ref["reconstruct"] = (w.w_eff, w.w_eff.clone())
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         passes[_ % n_pass].replay()
     torch.cuda.synchronize()
@@ -655,6 +724,10 @@ def main():
     for name, (n, g) in range_graphs.items():
         g.replay()
         avg_us[name] = 1e3 * time_replays(g, max(3, args.steps // 4)) / n
+        if isinstance(w, ProjWorkload) and name in eager_ref:
+            buf, ref = eager_ref[name]
+            assert torch.equal(buf.view(torch.int16), ref.view(torch.int16)), (
+                f"graph replays of {name} differ from the eager launch")
     print(f"[bench] timed {args.steps} steps in {wall:.3f} s "
           f"(GPU {step_ms:.3f} ms per step)", file=sys.stderr, flush=True)
 
@@ -665,6 +738,7 @@ def main():
                "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
                "dtype": "bf16", "data": "synthetic", "config": rep["config"],
                "per_matrix": rep["per_matrix"], "layer_us": rep["layer_us"],
+               **({"dense_base_ab": rep["dense_base_ab"]} if "dense_base_ab" in rep else {}),
                "value_per_step": rep.get("value_per_step"),
                **({"stack_ms": rep["stack_ms"]} if "stack_ms" in rep else {}),
                "roofline": rep["roofline"],
@@ -690,7 +764,22 @@ def main():
                                 HBM_PEAK_GBS, "GB/s", counter_traffic("multi", w.name)),
         "prefill": roofline_entry("mfma", pre_tflops, BF16_PEAK_TFLOPS, "TFLOP/s",
                                   counter_traffic("prefill", w.name)),
+        "reconstruct": roofline_entry("hbm", w.reconstruct_bytes() / (avg_us["reconstruct"] * 1e-6)
+                                      / 1e9, HBM_PEAK_GBS, "GB/s",
+                                      counter_traffic("reconstruct", w.name)),
     }
+    # Unfused A/B: the fused call against W_eff materialised by
+    # bitdelta_reconstruct and multiplied by the library GEMM (torch.mm on
+    # hipBLASLt), and against that GEMM alone on a stored W_eff (a dense bf16
+    # layer of the same shape, no BitDelta at all).
+    rec_us = avg_us["reconstruct"]
+    unfused = {}
+    for m in list(w.decode_ms) + [w.prefill_m]:
+        key = f"decode_m{m}" if m in w.decode_ms else "prefill"
+        dense = avg_us[f"dense_m{m}"]
+        unfused[key] = {"tokens": m, "fused_us": round(avg_us[key], 3),
+                        "reconstruct_plus_gemm_us": round(rec_us + dense, 3),
+                        "gemm_on_stored_weff_us": round(dense, 3)}
     kernel_us = {name: round(v, 3) for name, v in avg_us.items()}
 
     cpu = None
@@ -723,6 +812,7 @@ def main():
         "prefill_tflops": round(pre_tflops, 2),
         "roofline": rooflines["decode"],
         "roofline_by_kernel": rooflines,
+        "unfused_ab": unfused,
         "kernel_avg_us": kernel_us,
         "cpu_baseline": cpu,
     }
