@@ -123,6 +123,20 @@ def _need(t: torch.Tensor, name: str, dtype, device=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _size(t: torch.Tensor, name: str, n: int):
+    """The library reads or writes exactly n elements through t's pointer."""
+    if t.numel() != n:
+        raise ValueError(f"{name} must hold {n} elements, got {t.numel()} ({tuple(t.shape)})")
+
+
+def _signs_and_scale(packed, alpha, d_out: int, d_in: int, alpha_mode: int, pname="packed",
+                     aname="alpha"):
+    if d_in % 64 == 0:  # other widths are rejected by the library itself
+        _size(packed, pname, d_out * (d_in // 64))
+    if alpha_mode in (ALPHA_PER_MATRIX, ALPHA_PER_ROW):
+        _size(alpha, aname, d_out if alpha_mode == ALPHA_PER_ROW else 1)
+
+
 def ratio_to_f32_bits(s: int, n: int) -> int:
     """Host copy of the scale's final rounding: float32 bits of s / (n * 2^48)."""
     return int(lib().bitdelta_ratio_to_f32_bits((s >> 64) & (2**64 - 1), s & (2**64 - 1), n))
@@ -147,6 +161,9 @@ def compress(w_ft: torch.Tensor, w_base: torch.Tensor, alpha_mode: int, packed=N
     if alpha is None:
         alpha = torch.empty((d_out if alpha_mode == ALPHA_PER_ROW else 1,), dtype=torch.float32,
                             device=dev)
+    _need(packed, "packed", torch.int64, dev)
+    _need(alpha, "alpha", torch.float32, dev)
+    _signs_and_scale(packed, alpha, d_out, d_in, alpha_mode)
     need = compress_workspace_size(d_out, d_in, alpha_mode)
     if workspace is None and need:
         workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
@@ -172,9 +189,11 @@ def linear(x: torch.Tensor, w_base: torch.Tensor, packed: torch.Tensor, alpha: t
         raise ValueError("x's last dimension must equal d_in")
     lead = x.shape[:-1]
     m = x.numel() // d_in
+    _signs_and_scale(packed, alpha, d_out, d_in, alpha_mode)
     if y is None:
         y = torch.empty((*lead, d_out), dtype=torch.bfloat16, device=dev)
     _need(y, "y", torch.bfloat16, dev)
+    _size(y, "y", m * d_out)
     with _on(dev):
         st = lib().bitdelta_linear(_ptr(x), m, _ptr(w_base), _ptr(packed), _ptr(alpha),
                                    alpha_mode, d_out, d_in, _ptr(y), _stream(stream))
@@ -196,13 +215,14 @@ def linear_multi(x: torch.Tensor, variant_ids: torch.Tensor, w_base: torch.Tenso
     nv = len(packed_list)
     if nv != len(alpha_list):
         raise ValueError("one alpha per packed variant")
-    for p in packed_list:
+    for p, a in zip(packed_list, alpha_list):
         _need(p, "packed", torch.int64, dev)
-    for a in alpha_list:
         _need(a, "alpha", torch.float32, dev)
+        _signs_and_scale(p, a, d_out, d_in, alpha_mode)
     if y is None:
         y = torch.empty((*x.shape[:-1], d_out), dtype=torch.bfloat16, device=dev)
     _need(y, "y", torch.bfloat16, dev)
+    _size(y, "y", m * d_out)
     parr = (ctypes.c_void_p * max(nv, 1))(*[p.data_ptr() for p in packed_list])
     aarr = (ctypes.c_void_p * max(nv, 1))(*[a.data_ptr() for a in alpha_list])
     with _on(dev):
@@ -224,9 +244,11 @@ def reconstruct(w_base: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor,
     if w_base.dim() != 2:
         raise ValueError("w_base must be 2-D")
     d_out, d_in = w_base.shape
+    _signs_and_scale(packed, alpha, d_out, d_in, alpha_mode)
     if w_eff is None:
         w_eff = torch.empty((d_out, d_in), dtype=torch.bfloat16, device=dev)
     _need(w_eff, "w_eff", torch.bfloat16, dev)
+    _size(w_eff, "w_eff", d_out * d_in)
     with _on(dev):
         st = lib().bitdelta_reconstruct(_ptr(w_base), _ptr(packed), _ptr(alpha), alpha_mode,
                                         d_out, d_in, _ptr(w_eff), _stream(stream))

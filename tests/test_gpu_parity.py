@@ -562,6 +562,36 @@ def test_reconstruct_gate_full_size():
     check_reconstruct(wb, packed, alpha, 0, rows=_sample_rows(28672, 24, 62))
 
 
+def test_binding_rejects_wrong_sizes():
+    """The C ABI sees pointers only; the binding checks every tensor's size
+    before any launch, so a short output or operand is an error, not an
+    out-of-bounds access."""
+    wb, wf = to_dev(*S.small_pair(32, 128, 0.02, 1e-3, seed=3))
+    x = S.draw_activations(4, 128, S.generator(4)).to(DEV)
+    packed, alpha = T.compress(wf, wb, 1)
+    short_y = torch.empty(4, 31, dtype=torch.bfloat16, device=DEV)
+    ids = torch.zeros(4, dtype=torch.int32, device=DEV)
+    with pytest.raises(ValueError):
+        T.linear(x, wb, packed, alpha, 1, y=short_y)
+    with pytest.raises(ValueError):
+        T.linear(x, wb, packed[:31], alpha, 1)
+    with pytest.raises(ValueError):
+        T.linear(x, wb, packed, alpha[:31], 1)
+    with pytest.raises(ValueError):
+        T.linear(x, wb, packed, alpha, 0)             # per-matrix mode needs one alpha
+    with pytest.raises(ValueError):
+        T.linear_multi(x, ids, wb, [packed], [alpha[:1]], 1)
+    with pytest.raises(ValueError):
+        T.linear_multi(x, ids, wb, [packed], [alpha], 1, y=short_y)
+    with pytest.raises(ValueError):
+        T.reconstruct(wb, packed, alpha, 1, w_eff=torch.empty(32, 64, dtype=torch.bfloat16,
+                                                               device=DEV))
+    with pytest.raises(ValueError):
+        T.compress(wf, wb, 1, packed=torch.empty(32, 1, dtype=torch.int64, device=DEV))
+    with pytest.raises(ValueError):
+        T.compress(wf, wb, 0, alpha=torch.empty(32, dtype=torch.float32, device=DEV))
+
+
 # ---------------------------------------------------------------- graph capture
 def test_graph_replays_match_eager():
     """Every entry point captured in one HIP graph: each replay, with eager
