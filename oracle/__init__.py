@@ -14,9 +14,10 @@ foundation, "Sunum mimarisi" = serving architecture, "Altyapı ayrıntıları" =
 infrastructure details) and the equation or figure in it.
 
 Every function here is pinned by a ``-m "not gpu"`` test in
-``tests/test_oracle_pins.py`` against something other than itself (closed
-forms, textbook routines, brute force, hand-built cases).  No function is
-"parity unpinned".
+``tests/test_oracle_pins.py`` (the arithmetic) or ``tests/test_cache_policy.py``
+(the delta-cache policy of ``cache_policy``) against something other than
+itself (closed forms, textbook routines, brute force, hand-built cases).  No
+function is "parity unpinned".
 """
 
 from .bitdelta_oracle import (  # noqa: F401

@@ -1,0 +1,158 @@
+"""Delta-cache policy: the oracle pinned against hand-derived traces and a
+textbook LRU, then the library's native policy (C ABI, host only, no GPU)
+checked against the oracle decision by decision on synthetic Zipf traces."""
+
+import collections
+import ctypes
+import os
+
+import numpy as np
+import pytest
+
+from oracle import cache_policy as CP
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "cache_traces.txt")
+ACTIONS = {"HIT": CP.HIT, "QUEUED": CP.QUEUED, "LOAD": CP.LOAD, "FULL": CP.FULL}
+
+
+def read_traces():
+    traces, cur = [], None
+    for raw in open(GOLDEN):
+        line = raw.split("#", 1)[0].split()
+        if not line:
+            continue
+        if line[0] == "trace":
+            cur = (tuple(int(t) for t in line[1:5]), [])
+        elif line[0] == "end":
+            traces.append(cur)
+            cur = None
+        elif line[0] == "req":
+            cur[1].append(("req", int(line[1]), ACTIONS[line[2]], int(line[3]), int(line[4])))
+        else:
+            cur[1].append((line[0], int(line[1])))
+    return traces
+
+
+def zipf_trace(n, n_variants, seed, a=1.1):
+    rng = np.random.default_rng(seed)
+    p = np.arange(1, n_variants + 1, dtype=np.float64) ** -a
+    return rng.choice(n_variants, size=n, p=p / p.sum())
+
+
+# ---------------------------------------------------------------- oracle pins
+def test_oracle_golden_traces():
+    traces = read_traces()
+    assert len(traces) == 3
+    for (V, S, P, H), steps in traces:
+        c = CP.CachePolicy(V, S, P, H)
+        for st in steps:
+            if st[0] == "req":
+                assert c.request(st[1]) == st[2:], (V, S, P, H, st)
+            elif st[0] == "loaded":
+                c.loaded(st[1])
+            else:
+                c.release(st[1])
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 5])
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_oracle_without_pinning_is_textbook_lru(S, seed):
+    """No pinned variants, loads that finish at once, every request released
+    at once: hits, misses and victims are those of an LRU cache of S entries
+    (collections.OrderedDict)."""
+    V = 8
+    c = CP.CachePolicy(V, S, 0, 0)
+    lru = collections.OrderedDict()
+    for v in zipf_trace(400, V, seed):
+        v = int(v)
+        act, slot, ev = c.request(v)
+        if v in lru:
+            lru.move_to_end(v)
+            assert (act, ev) == (CP.HIT, -1)
+        else:
+            want_ev = -1
+            if len(lru) == S:
+                want_ev, _ = lru.popitem(last=False)
+            lru[v] = True
+            assert (act, ev) == (CP.LOAD, want_ev)
+            c.loaded(v)
+        c.release(v)
+
+
+@pytest.mark.parametrize("P", [0, 3, 6])
+def test_oracle_room_for_all_loads_each_variant_once(P):
+    """With a slot for every variant only the first request of each loads."""
+    V = 14
+    c = CP.CachePolicy(V, V, P, 16)
+    seen = set()
+    for v in zipf_trace(500, V, 5):
+        v = int(v)
+        act, slot, ev = c.request(v)
+        assert ev == -1
+        if v in seen:
+            assert act in (CP.HIT, CP.QUEUED)
+        else:
+            assert act == CP.LOAD and slot == len(seen)
+            seen.add(v)
+        if act == CP.LOAD:
+            c.loaded(v)
+        c.release(v)
+
+
+def test_oracle_requests_queue_behind_one_load():
+    c = CP.CachePolicy(4, 2, 1, 0)
+    assert c.request(3) == (CP.LOAD, 0, -1)
+    for _ in range(5):
+        assert c.request(3) == (CP.QUEUED, 0, -1)
+    c.loaded(3)
+    assert c.request(3) == (CP.HIT, 0, -1)
+
+
+def test_oracle_full_changes_nothing():
+    c = CP.CachePolicy(3, 1, 0, 0)
+    assert c.request(0) == (CP.LOAD, 0, -1)
+    c.loaded(0)
+    before = (c.time, list(c.rate), list(c.last))
+    assert c.request(1) == (CP.FULL, -1, -1)   # variant 0 still in use
+    assert (c.time, c.rate, c.last) == before
+    c.release(0)
+    assert c.request(1) == (CP.LOAD, 0, 0)
+
+
+def test_oracle_pinned_top_variants_never_evicted():
+    """Zipf traffic over 14 variants with 8 slots and the top 6 pinned (the
+    page's split): every victim is outside the top 6 by the request counts
+    kept here independently of the oracle."""
+    V, S, P = 14, 8, 6
+    c = CP.CachePolicy(V, S, P, 0)
+    counts = [0] * V
+    last = [0] * V
+    for t, v in enumerate(zipf_trace(3000, V, 11), start=1):
+        v = int(v)
+        act, slot, ev = c.request(v)
+        counts[v] += 1
+        last[v] = t
+        if ev >= 0:
+            top = sorted(range(V), key=lambda u: (-counts[u], u))[:P]
+            assert ev not in top
+            # the victim is the least recently requested resident outsider
+            others = [u for u in range(V) if c.state[u] == CP.RESIDENT and u not in top
+                      and u != v]
+            assert all(last[ev] < last[u] for u in others)
+        if act == CP.LOAD:
+            c.loaded(v)
+        c.release(v)
+    top = sorted(range(V), key=lambda u: (-counts[u], u))[:P]
+    assert all(c.state[u] == CP.RESIDENT for u in top)
+
+
+def test_oracle_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        CP.CachePolicy(4, 2, 2, 0)
+    c = CP.CachePolicy(4, 2, 1, 0)
+    with pytest.raises(ValueError):
+        c.request(4)
+    with pytest.raises(ValueError):
+        c.loaded(0)
+    with pytest.raises(ValueError):
+        c.release(0)
