@@ -63,6 +63,8 @@ extern "C" {
 #define BITDELTA_ERR_HIP 7       /* the HIP runtime reported an error at launch */
 #define BITDELTA_ERR_DEVICE 8    /* the current device is not a gfx950 GPU */
 #define BITDELTA_ERR_OVERLAP 9   /* an output buffer overlaps an input buffer */
+#define BITDELTA_ERR_CACHE 10    /* delta cache: parameter or variant out of range,
+                                    or a call out of order */
 
 /* alpha_mode values. */
 #define BITDELTA_ALPHA_PER_MATRIX 0
@@ -178,6 +180,135 @@ int bitdelta_linear_multi(const uint16_t* x, int64_t M, const int32_t* variant_i
 int bitdelta_reconstruct(const uint16_t* w_base, const uint64_t* packed, const float* alpha,
                          int alpha_mode, int64_t d_out, int64_t d_in, uint16_t* w_eff,
                          void* stream);
+
+/*
+ * Delta cache - which variant's packed delta lives in which device slot, and
+ * the host-to-device loads that fill the slots (section "Altyapı
+ * ayrıntıları": the cold-start paragraph, a delta that is not resident is
+ * loaded into device memory on its first request and stays until evicted;
+ * the eviction paragraph, least-recently-used eviction weighted by request
+ * rate with the highest-rate variants pinned, the page pinning 6 of 14; the
+ * routing paragraph, requests for a variant whose delta is loading wait for
+ * that load instead of starting another).
+ *
+ * Policy, exactly:
+ * - rate[v] counts requests for v; after every halve_every-th counted
+ *   request all rates are halved (integer shift right); halve_every = 0
+ *   never halves.  A request is counted first, then the halving applies.
+ * - the n_pinned variants of highest rate (ties to the lower id) are pinned:
+ *   a resident pinned variant is never evicted (no slot is reserved for a
+ *   pinned variant that is not resident).
+ * - a request for a resident variant is a HIT; for a variant whose load is in
+ *   flight it is QUEUED (no second load); otherwise it is a LOAD into the
+ *   lowest-numbered free slot, or into the slot of the evicted variant: the
+ *   least recently requested variant that is resident, not pinned, not in
+ *   use and not the one requested.  A variant is in use from each request
+ *   that returned it until the matching release.  A variant still loading is
+ *   never evicted.
+ * - with no free slot and nothing to evict the request is FULL and changes
+ *   no state (it is not counted); the caller retries later.
+ *
+ * A cache is a host object.  Without attached memory it runs the policy only
+ * (bitdelta_cache_request / _loaded / _release: no HIP call at all).  With
+ * memory attached (bitdelta_cache_attach) it moves the bytes itself
+ * (bitdelta_cache_acquire / _release / _poll), and the policy-only calls
+ * request and loaded are refused.  Calls on one cache are serialised by a
+ * lock; the cache allocates host memory only (its state and, once memory is
+ * attached, one HIP event per variant and per slot).
+ */
+typedef struct bitdelta_cache bitdelta_cache;
+
+/* Request outcomes (action). */
+#define BITDELTA_CACHE_HIT 0     /* resident and loaded: use the slot */
+#define BITDELTA_CACHE_QUEUED 1  /* its load is in flight: wait for it */
+#define BITDELTA_CACHE_LOAD 2    /* this request starts the load into the slot */
+#define BITDELTA_CACHE_FULL 3    /* nothing can be evicted now; no state changed */
+
+/* Variant states. */
+#define BITDELTA_CACHE_ABSENT 0
+#define BITDELTA_CACHE_LOADING 1
+#define BITDELTA_CACHE_RESIDENT 2
+
+/*
+ * bitdelta_cache_create - a cache of n_slots slots for variants
+ * 0 .. n_variants-1.  1 <= n_variants, n_slots <= 65536,
+ * 0 <= n_pinned < n_slots, halve_every >= 0.  *out receives the cache (NULL
+ * on error).  Returns BITDELTA_OK, BITDELTA_ERR_NULL or BITDELTA_ERR_CACHE.
+ */
+int bitdelta_cache_create(int32_t n_variants, int32_t n_slots, int32_t n_pinned,
+                          int64_t halve_every, bitdelta_cache** out);
+
+/* Frees the cache's host state and events (not the caller's memory).  Work
+ * already enqueued keeps running.  NULL is ignored. */
+void bitdelta_cache_destroy(bitdelta_cache* cache);
+
+/*
+ * bitdelta_cache_request - policy only (no memory attached): one request for
+ * `variant`.  *action receives HIT, QUEUED, LOAD or FULL, *slot the slot
+ * (-1 for FULL), *evicted the variant evicted by a LOAD or -1.  Except for
+ * FULL the variant is in use until bitdelta_cache_release.  After a LOAD the
+ * caller moves the bytes and reports it with bitdelta_cache_loaded.
+ * Returns BITDELTA_ERR_CACHE for a variant out of range or a cache with
+ * memory attached.
+ */
+int bitdelta_cache_request(bitdelta_cache* cache, int32_t variant, int32_t* action,
+                           int32_t* slot, int32_t* evicted);
+
+/* Policy only: the load of `variant` has finished (LOADING -> RESIDENT).
+ * BITDELTA_ERR_CACHE if it is not loading or memory is attached. */
+int bitdelta_cache_loaded(bitdelta_cache* cache, int32_t variant);
+
+/*
+ * bitdelta_cache_release - one use of `variant` ends.  With memory attached
+ * an event is recorded on `stream` (a hipStream_t, NULL = null stream): a
+ * later load into the variant's slot waits for it, so work enqueued on that
+ * stream before the release still reads the old bytes.  A slot's releases
+ * must come from one stream (or the caller orders its streams).  Without
+ * memory `stream` is ignored.  BITDELTA_ERR_CACHE if the variant is not in use.
+ */
+int bitdelta_cache_release(bitdelta_cache* cache, int32_t variant, void* stream);
+
+/* State (ABSENT / LOADING / RESIDENT), slot (-1 when absent) and current
+ * rate of `variant`. */
+int bitdelta_cache_state(bitdelta_cache* cache, int32_t variant, int32_t* state,
+                         int32_t* slot, int64_t* rate);
+
+/*
+ * bitdelta_cache_attach - give the cache its memory, before any request.
+ *   slots         HOST array of n_slots device pointers, each 16-byte
+ *                 aligned, slot_bytes long, not overlapping
+ *   sources       HOST array of n_variants host pointers: the bytes of each
+ *                 variant's delta (its packed signs and alpha, in whatever
+ *                 layout the caller reads them back from the slot); they
+ *                 should be page-locked (hipHostMalloc) for the copy to run
+ *                 asynchronously, and must stay valid while the cache lives
+ *   source_bytes  HOST array of n_variants sizes, each <= slot_bytes
+ * The current device becomes the cache's device.  Creates the events.
+ * Returns BITDELTA_ERR_CACHE if a request was made already or a source is
+ * larger than a slot, BITDELTA_ERR_ALIGN / _OVERLAP / _NULL for bad slots.
+ */
+int bitdelta_cache_attach(bitdelta_cache* cache, void* const* slots, size_t slot_bytes,
+                          const void* const* sources, const size_t* source_bytes);
+
+/*
+ * bitdelta_cache_acquire - one request for `variant` that moves the bytes.
+ * First finished loads are marked resident (their events polled), then the
+ * request runs the policy.  LOAD: copy_stream waits for the slot's last
+ * release event, the variant's source bytes are copied into the slot
+ * (hipMemcpyAsync, host to device, on copy_stream) and the variant's load
+ * event is recorded there.  LOAD and QUEUED: use_stream waits for that
+ * event.  *slot_ptr receives the slot's device pointer (NULL for FULL):
+ * kernels enqueued on use_stream after this call read the variant's bytes.
+ * The current device must be the cache's (BITDELTA_ERR_DEVICE otherwise).
+ * On BITDELTA_ERR_HIP nothing is left in use.
+ */
+int bitdelta_cache_acquire(bitdelta_cache* cache, int32_t variant, void* copy_stream,
+                           void* use_stream, int32_t* action, void** slot_ptr,
+                           int32_t* evicted);
+
+/* Marks loads whose events have completed resident; *n_loaded (may be NULL)
+ * receives how many.  BITDELTA_ERR_CACHE without attached memory. */
+int bitdelta_cache_poll(bitdelta_cache* cache, int32_t* n_loaded);
 
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* bitdelta_status_string(int status);

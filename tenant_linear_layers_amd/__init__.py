@@ -8,12 +8,22 @@ binding with the same names.
 from .bitdelta import (  # noqa: F401
     ALPHA_PER_MATRIX,
     ALPHA_PER_ROW,
+    CACHE_ABSENT,
+    CACHE_FULL,
+    CACHE_HIT,
+    CACHE_LOAD,
+    CACHE_LOADING,
+    CACHE_QUEUED,
+    CACHE_RESIDENT,
     EXPORTS,
     LIB_PATH,
     MAX_VARIANTS,
     BitDeltaError,
+    DeltaCache,
     compress,
     compress_workspace_size,
+    delta_layout,
+    delta_views,
     lib,
     linear,
     linear_multi,

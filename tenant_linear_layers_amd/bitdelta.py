@@ -31,7 +31,12 @@ STATUS_NAMES = {
     7: "BITDELTA_ERR_HIP",
     8: "BITDELTA_ERR_DEVICE",
     9: "BITDELTA_ERR_OVERLAP",
+    10: "BITDELTA_ERR_CACHE",
 }
+
+# Delta cache request outcomes and variant states (include/bitdelta.h).
+CACHE_HIT, CACHE_QUEUED, CACHE_LOAD, CACHE_FULL = 0, 1, 2, 3
+CACHE_ABSENT, CACHE_LOADING, CACHE_RESIDENT = 0, 1, 2
 
 EXPORTS = (
     "bitdelta_compress_workspace_size",
@@ -41,6 +46,15 @@ EXPORTS = (
     "bitdelta_reconstruct",
     "bitdelta_status_string",
     "bitdelta_ratio_to_f32_bits",
+    "bitdelta_cache_create",
+    "bitdelta_cache_destroy",
+    "bitdelta_cache_request",
+    "bitdelta_cache_loaded",
+    "bitdelta_cache_release",
+    "bitdelta_cache_state",
+    "bitdelta_cache_attach",
+    "bitdelta_cache_acquire",
+    "bitdelta_cache_poll",
 )
 
 
@@ -79,6 +93,27 @@ def lib() -> ctypes.CDLL:
     L.bitdelta_status_string.restype = ctypes.c_char_p
     L.bitdelta_ratio_to_f32_bits.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64]
     L.bitdelta_ratio_to_f32_bits.restype = ctypes.c_uint32
+    pi32, pi64 = ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)
+    L.bitdelta_cache_create.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, i64,
+                                        ctypes.POINTER(vp)]
+    L.bitdelta_cache_create.restype = i32
+    L.bitdelta_cache_destroy.argtypes = [vp]
+    L.bitdelta_cache_destroy.restype = None
+    L.bitdelta_cache_request.argtypes = [vp, ctypes.c_int32, pi32, pi32, pi32]
+    L.bitdelta_cache_request.restype = i32
+    L.bitdelta_cache_loaded.argtypes = [vp, ctypes.c_int32]
+    L.bitdelta_cache_loaded.restype = i32
+    L.bitdelta_cache_release.argtypes = [vp, ctypes.c_int32, vp]
+    L.bitdelta_cache_release.restype = i32
+    L.bitdelta_cache_state.argtypes = [vp, ctypes.c_int32, pi32, pi32, pi64]
+    L.bitdelta_cache_state.restype = i32
+    L.bitdelta_cache_attach.argtypes = [vp, vp, sz, vp, vp]
+    L.bitdelta_cache_attach.restype = i32
+    L.bitdelta_cache_acquire.argtypes = [vp, ctypes.c_int32, vp, vp, pi32, ctypes.POINTER(vp),
+                                         pi32]
+    L.bitdelta_cache_acquire.restype = i32
+    L.bitdelta_cache_poll.argtypes = [vp, pi32]
+    L.bitdelta_cache_poll.restype = i32
     _lib = L
     return L
 
@@ -254,3 +289,129 @@ def reconstruct(w_base: torch.Tensor, packed: torch.Tensor, alpha: torch.Tensor,
                                         d_out, d_in, _ptr(w_eff), _stream(stream))
     _check(st, "bitdelta_reconstruct")
     return w_eff
+
+
+# ------------------------------------------------------------------ delta cache
+def delta_layout(shapes, alpha_mode: int, align: int = 256):
+    """Byte layout of one variant's delta for a list of matrix shapes
+    [(d_out, d_in), ...]: each matrix's packed signs (d_out*d_in/8 bytes),
+    then its alpha (4*d_out or 4 bytes), every piece starting on `align`
+    bytes.  Returns ([(packed_offset, alpha_offset), ...], total_bytes)."""
+    off, out = 0, []
+    for d_out, d_in in shapes:
+        p = off
+        off = -(-(p + d_out * d_in // 8) // align) * align
+        a = off
+        off = -(-(a + 4 * (d_out if alpha_mode == ALPHA_PER_ROW else 1)) // align) * align
+        out.append((p, a))
+    return out, off
+
+
+def delta_views(buf: torch.Tensor, shapes, alpha_mode: int):
+    """(packed int64 [d_out, d_in/64], alpha float32) views of each matrix's
+    piece of a uint8 buffer laid out by delta_layout (host or device)."""
+    if buf.dtype != torch.uint8 or buf.dim() != 1:
+        raise TypeError("buf must be a 1-D uint8 tensor")
+    offs, total = delta_layout(shapes, alpha_mode)
+    if buf.numel() < total:
+        raise ValueError(f"buf holds {buf.numel()} bytes, the layout needs {total}")
+    views = []
+    for (d_out, d_in), (p, a) in zip(shapes, offs):
+        na = d_out if alpha_mode == ALPHA_PER_ROW else 1
+        packed = buf[p:p + d_out * d_in // 8].view(torch.int64).view(d_out, d_in // 64)
+        alpha = buf[a:a + 4 * na].view(torch.float32)
+        views.append((packed, alpha))
+    return views
+
+
+class DeltaCache:
+    """A libbitdelta delta cache (bitdelta_cache_*): the request-rate pinned
+    LRU policy over device slots, and, once attach() has given it slots and
+    per-variant host sources, the host-to-device loads that fill them."""
+
+    def __init__(self, n_variants: int, n_slots: int, n_pinned: int = 0,
+                 halve_every: int = 0):
+        h = ctypes.c_void_p()
+        _check(lib().bitdelta_cache_create(n_variants, n_slots, n_pinned, halve_every,
+                                           ctypes.byref(h)), "bitdelta_cache_create")
+        self._h = h
+        self.n_variants, self.n_slots = n_variants, n_slots
+        self._slots = None
+        self._sources = None
+        self._slot_of_ptr = {}
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().bitdelta_cache_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def _triple(self):
+        return ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+
+    def request(self, variant: int):
+        """Policy only: (action, slot, evicted) of one request."""
+        a, s, e = self._triple()
+        _check(lib().bitdelta_cache_request(self._h, variant, ctypes.byref(a), ctypes.byref(s),
+                                            ctypes.byref(e)), "bitdelta_cache_request")
+        return a.value, s.value, e.value
+
+    def loaded(self, variant: int) -> None:
+        _check(lib().bitdelta_cache_loaded(self._h, variant), "bitdelta_cache_loaded")
+
+    def release(self, variant: int, stream=None) -> None:
+        st = _stream(stream) if self._slots is not None else ctypes.c_void_p(None)
+        _check(lib().bitdelta_cache_release(self._h, variant, st), "bitdelta_cache_release")
+
+    def state(self, variant: int):
+        """(state, slot, rate) of a variant."""
+        st, sl, r = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+        _check(lib().bitdelta_cache_state(self._h, variant, ctypes.byref(st), ctypes.byref(sl),
+                                          ctypes.byref(r)), "bitdelta_cache_state")
+        return st.value, sl.value, r.value
+
+    def attach(self, slots, sources) -> None:
+        """slots: n_slots device uint8 tensors of one size; sources: n_variants
+        host uint8 tensors (page-locked for asynchronous copies), each no
+        larger than a slot.  Both lists are kept alive by the cache."""
+        if len(slots) != self.n_slots or len(sources) != self.n_variants:
+            raise ValueError("one tensor per slot and one source per variant")
+        nbytes = slots[0].numel()
+        for t in slots:
+            _need(t, "slot", torch.uint8, slots[0].device)
+            _size(t, "slot", nbytes)
+        for t in sources:
+            if t.dtype != torch.uint8 or t.is_cuda or not t.is_contiguous():
+                raise ValueError("sources must be contiguous host uint8 tensors")
+        sarr = (ctypes.c_void_p * len(slots))(*[t.data_ptr() for t in slots])
+        varr = (ctypes.c_void_p * len(sources))(*[t.data_ptr() for t in sources])
+        barr = (ctypes.c_size_t * len(sources))(*[t.numel() for t in sources])
+        with _on(slots[0].device):
+            st = lib().bitdelta_cache_attach(self._h, ctypes.cast(sarr, ctypes.c_void_p), nbytes,
+                                             ctypes.cast(varr, ctypes.c_void_p),
+                                             ctypes.cast(barr, ctypes.c_void_p))
+        _check(st, "bitdelta_cache_attach")
+        self._slots, self._sources = list(slots), list(sources)
+        self._slot_of_ptr = {t.data_ptr(): i for i, t in enumerate(slots)}
+
+    def acquire(self, variant: int, copy_stream, use_stream=None):
+        """(action, slot tensor or None, evicted) of one request that moves the
+        bytes: after it, work on use_stream reads the variant's delta."""
+        if self._slots is None:
+            raise RuntimeError("attach() the cache's memory first")
+        a, e = ctypes.c_int32(), ctypes.c_int32()
+        ptr = ctypes.c_void_p()
+        with _on(self._slots[0].device):
+            st = lib().bitdelta_cache_acquire(self._h, variant, _stream(copy_stream),
+                                              _stream(use_stream), ctypes.byref(a),
+                                              ctypes.byref(ptr), ctypes.byref(e))
+        _check(st, "bitdelta_cache_acquire")
+        slot = None if not ptr.value else self._slots[self._slot_of_ptr[ptr.value]]
+        return a.value, slot, e.value
+
+    def poll(self) -> int:
+        n = ctypes.c_int32()
+        _check(lib().bitdelta_cache_poll(self._h, ctypes.byref(n)), "bitdelta_cache_poll")
+        return n.value

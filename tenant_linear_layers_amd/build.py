@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbitdelta.so")
 
-SOURCES = ("api.hip", "compress.hip", "decode.hip", "prefill.hip", "reconstruct.hip")
+SOURCES = ("api.hip", "compress.hip", "decode.hip", "prefill.hip", "reconstruct.hip",
+           "cache.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

@@ -63,6 +63,8 @@ BD_EXPORT const char* bitdelta_status_string(int status) {
     case BITDELTA_ERR_HIP: return "HIP runtime error";
     case BITDELTA_ERR_DEVICE: return "current device is not a gfx950 GPU";
     case BITDELTA_ERR_OVERLAP: return "an output buffer overlaps an input buffer";
+    case BITDELTA_ERR_CACHE:
+      return "delta cache: parameter or variant out of range, or call out of order";
     default: return "unknown status";
   }
 }

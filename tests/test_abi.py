@@ -34,7 +34,7 @@ def test_header_functions_are_exported():
 
 
 def test_status_strings():
-    for s in range(10):
+    for s in range(11):
         txt = T.status_string(s)
         assert txt and txt != "unknown status"
     assert T.status_string(123) == "unknown status"

@@ -156,3 +156,119 @@ def test_oracle_rejects_bad_arguments():
         c.loaded(0)
     with pytest.raises(ValueError):
         c.release(0)
+
+
+# ------------------------------------------------- library policy vs the oracle
+def _lib_cache(V, S, P, H):
+    import tenant_linear_layers_amd as T
+    return T.DeltaCache(V, S, P, H)
+
+
+def test_library_golden_traces():
+    for (V, S, P, H), steps in read_traces():
+        c = _lib_cache(V, S, P, H)
+        for st in steps:
+            if st[0] == "req":
+                assert c.request(st[1]) == st[2:], (V, S, P, H, st)
+            elif st[0] == "loaded":
+                c.loaded(st[1])
+            else:
+                c.release(st[1])
+
+
+@pytest.mark.parametrize("V,S,P,H", [(14, 8, 6, 0), (14, 8, 6, 64), (14, 4, 2, 7),
+                                     (5, 1, 0, 0), (30, 10, 3, 100), (3, 5, 4, 1)])
+@pytest.mark.parametrize("seed", [0, 1])
+def test_library_matches_oracle_on_zipf_traffic(V, S, P, H, seed):
+    """Every decision of the native policy equals the oracle's on Zipf(1.1)
+    traffic with loads that finish out of order after random delays and
+    uses released in random order (FULL refusals included)."""
+    rng = np.random.default_rng(1000 * seed + V)
+    lib_c = _lib_cache(V, S, P, H)
+    orc = CP.CachePolicy(V, S, P, H)
+    loading, in_use = [], []
+    seen = collections.Counter()
+    for v in zipf_trace(1500, V, seed):
+        v = int(v)
+        got = lib_c.request(v)
+        want = orc.request(v)
+        assert got == want, (v, got, want)
+        seen[want[0]] += 1
+        if want[0] != CP.FULL:
+            in_use.append(v)
+            if want[0] == CP.LOAD:
+                loading.append(v)
+        # finish some loads, end some uses, in random order
+        for _ in range(int(rng.integers(0, 3))):
+            if loading:
+                u = loading.pop(int(rng.integers(len(loading))))
+                lib_c.loaded(u)
+                orc.loaded(u)
+        for _ in range(int(rng.integers(0, 3))):
+            if in_use:
+                u = in_use.pop(int(rng.integers(len(in_use))))
+                lib_c.release(u)
+                orc.release(u)
+        if rng.random() < 0.05:
+            u = int(rng.integers(V))
+            assert lib_c.state(u) == (orc.state[u], orc.slot[u], orc.rate[u])
+    print(dict(seen))
+    assert seen[CP.LOAD] and seen[CP.HIT] and seen[CP.QUEUED]
+    if S < V:
+        assert seen[CP.FULL]   # refusals were exercised too
+
+
+def test_library_rejects_bad_calls():
+    import tenant_linear_layers_amd as T
+    for args in [(0, 2, 0, 0), (4, 0, 0, 0), (4, 2, 2, 0), (4, 2, -1, 0), (4, 2, 1, -1)]:
+        with pytest.raises(T.BitDeltaError) as e:
+            T.DeltaCache(*args)
+        assert e.value.status == 10
+    c = T.DeltaCache(4, 2, 1, 0)
+    for call in (lambda: c.request(4), lambda: c.request(-1), lambda: c.loaded(0),
+                 lambda: c.release(0), lambda: c.state(9)):
+        with pytest.raises(T.BitDeltaError) as e:
+            call()
+        assert e.value.status == 10
+    with pytest.raises(RuntimeError):
+        c.acquire(0, None)
+
+
+def test_library_attach_argument_checks():
+    """attach validates its arguments before any HIP call (these addresses
+    are never dereferenced)."""
+    import tenant_linear_layers_amd as T
+    L = T.lib()
+    c = T.DeltaCache(2, 2, 0, 0)
+    slots = (ctypes.c_void_p * 2)(0x100000, 0x200000)
+    srcs = (ctypes.c_void_p * 2)(0x300000, 0x400000)
+    small = (ctypes.c_size_t * 2)(64, 64)
+    big = (ctypes.c_size_t * 2)(64, 4096)
+    cast = lambda a: ctypes.cast(a, ctypes.c_void_p)  # noqa: E731
+    assert L.bitdelta_cache_attach(c._h, cast(slots), 1024, cast(srcs), cast(big)) == 10
+    bad = (ctypes.c_void_p * 2)(0x100008, 0x200000)
+    assert L.bitdelta_cache_attach(c._h, cast(bad), 1024, cast(srcs), cast(small)) == 3
+    over = (ctypes.c_void_p * 2)(0x100000, 0x100200)
+    assert L.bitdelta_cache_attach(c._h, cast(over), 1024, cast(srcs), cast(small)) == 9
+    nul = (ctypes.c_void_p * 2)(0x100000, None)
+    assert L.bitdelta_cache_attach(c._h, cast(nul), 1024, cast(srcs), cast(small)) == 1
+    c.request(0)   # a request was made: attaching afterwards is refused
+    assert L.bitdelta_cache_attach(c._h, cast(slots), 1024, cast(srcs), cast(small)) == 10
+    assert L.bitdelta_cache_poll(c._h, None) == 10
+
+
+def test_delta_layout_offsets():
+    import tenant_linear_layers_amd as T
+    offs, total = T.delta_layout([(10240, 8192), (8192, 8192), (28672, 8192), (28672, 8192),
+                                  (8192, 28672)], T.ALPHA_PER_ROW)
+    packed = sum(a * b // 8 for a, b in [(10240, 8192), (8192, 8192), (28672, 8192),
+                                         (28672, 8192), (8192, 28672)])
+    assert packed == 106_954_752            # one 70B-shaped layer, n/8 bytes
+    assert all(p % 256 == 0 and a % 256 == 0 for p, a in offs)
+    assert packed < total <= packed + 4 * 83968 + 10 * 256
+    import torch
+    buf = torch.zeros(total, dtype=torch.uint8)
+    views = T.delta_views(buf, [(10240, 8192), (8192, 8192), (28672, 8192), (28672, 8192),
+                                (8192, 28672)], T.ALPHA_PER_ROW)
+    assert [tuple(p.shape) for p, _ in views][0] == (10240, 128)
+    assert [a.numel() for _, a in views] == [10240, 8192, 28672, 28672, 8192]
