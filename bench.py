@@ -621,6 +621,91 @@ def write_counter_profiles(res, per, n):
         f.write("\n".join(lines) + "\n")
 
 
+PCIE_PEAK_GBS = 64.0           # PCIe 5.0 x16 host link, one direction, published
+
+
+def measure_delta_loads(decode_graph, n_decode: int, decode_alone_us: float):
+    """Cold loads through the delta cache (bitdelta_cache_acquire): one
+    70B-shaped layer's delta per variant (packed signs of its five linears
+    and per-row alpha, laid out by delta_layout), from page-locked host
+    memory into device slots on a copy stream.  Four variants cycle through
+    two slots, so every request is a miss that loads (a request that finds
+    both slots still loading is refused by the policy and retried once the
+    copy stream is idle).  Then the same loads
+    run while the decode range (back-to-back decode launches) replays on the
+    compute stream: the decode's launch time with loads in flight against
+    its time alone.  The bytes are checked after the loads."""
+    shapes = [(d_out, d_in) for _, d_out, d_in in S.LAYER_70B]
+    _, total = T.delta_layout(shapes, T.ALPHA_PER_ROW)
+    n_var, n_slots = 4, 2
+    blobs = [torch.full((total,), v + 1, dtype=torch.uint8, pin_memory=True)
+             for v in range(n_var)]
+    slots = [torch.empty(total, dtype=torch.uint8, device="cuda") for _ in range(n_slots)]
+    cache = T.DeltaCache(n_var, n_slots, 0, 0)
+    cache.attach(slots, blobs)
+    copy = torch.cuda.Stream()
+    use = torch.cuda.Stream()   # the consumer of the loaded deltas (not the decode's stream)
+
+    def loads(first: int, k: int):
+        evs = []
+        for j in range(k):
+            v = (first + j) % n_var
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            act, slot = T.CACHE_FULL, None
+            while act == T.CACHE_FULL:   # both slots still loading: wait, as a router would
+                a.record(copy)
+                act, slot, _ = cache.acquire(v, copy, use)
+                if act == T.CACHE_FULL:
+                    copy.synchronize()
+            b.record(copy)
+            if act != T.CACHE_LOAD:
+                raise RuntimeError(f"expected a load of variant {v}, got action {act}")
+            cache.release(v, use)
+            evs.append((a, b, v, slot))
+        return evs
+
+    loads(0, 4)   # warm-up: first touch of every slot and source
+    torch.cuda.synchronize()
+    evs = loads(0, 8)
+    torch.cuda.synchronize()
+    load_ms = [a.elapsed_time(b) for a, b, _, _ in evs]
+    for _, _, v, slot in evs[-2:]:
+        if not bool((slot[:: 1 << 20] == v + 1).all()):
+            raise RuntimeError("loaded delta bytes differ from the source")
+    # loads during decode
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    evs2 = loads(0, 4)
+    d0.record()
+    decode_graph.replay()
+    d1.record()
+    torch.cuda.synchronize()
+    # the first two loads fill both slots and the host waits for them before
+    # the last two can be requested; the last two overlap the decode replay
+    load_ms_during = [a.elapsed_time(b) for a, b, _, _ in evs2[2:]]
+    decode_during_us = 1e3 * d0.elapsed_time(d1) / n_decode
+    mean_ms = sum(load_ms) / len(load_ms)
+    gbs = total / (mean_ms * 1e-3) / 1e9
+    variant_80 = 80 * total
+    cache.close()
+    return {
+        "what": "one 70B-shaped layer's delta per load (packed signs of QKV, O, gate, up, "
+                "down + per-row alpha), page-locked host -> HBM via bitdelta_cache_acquire "
+                "on a copy stream, 4 variants cycling through 2 slots (every request loads)",
+        "bytes_per_load": total,
+        "load_ms": round(mean_ms, 4),
+        "achieved_gbs": round(gbs, 2),
+        "pcie_peak_gbs": PCIE_PEAK_GBS,
+        "frac": round(gbs / PCIE_PEAK_GBS, 4),
+        "variant_80_layers_bytes": variant_80,
+        "variant_80_layers_ms_at_this_rate": round(variant_80 / (gbs * 1e9) * 1e3, 1),
+        "load_ms_during_decode": round(sum(load_ms_during) / len(load_ms_during), 4),
+        "decode_m16_us_alone": round(decode_alone_us, 3),
+        "decode_m16_us_during_loads": round(decode_during_us, 3),
+    }
+
+
 def roofline_entry(bound, achieved, peak, unit, traffic=None):
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -782,6 +867,10 @@ def main():
                         "gemm_on_stored_weff_us": round(dense, 3)}
     kernel_us = {name: round(v, 3) for name, v in avg_us.items()}
 
+    print("[bench] delta-cache loads", file=sys.stderr, flush=True)
+    n16, g16 = range_graphs["decode_m16"]
+    delta_load = measure_delta_loads(g16, n16, avg_us["decode_m16"])
+
     cpu = None
     if args.cpu_budget > 0:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
@@ -814,6 +903,7 @@ def main():
         "roofline_by_kernel": rooflines,
         "unfused_ab": unfused,
         "kernel_avg_us": kernel_us,
+        "delta_load": delta_load,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -98,7 +98,8 @@ def test_proj4096_linear(proj4096, m):
 
 
 # ---------------------------------------------------------------- edge cases
-@pytest.mark.parametrize("shape", [(1, 64), (3, 128), (17, 192), (33, 576), (5, 1088), (70, 4160)])
+@pytest.mark.parametrize("shape", [(1, 64), (3, 128), (17, 192), (33, 576), (5, 1088), (70, 4160),
+                                   (71, 2112), (2, 4096), (1, 2048)])
 @pytest.mark.parametrize("mode", [0, 1])
 def test_compress_ragged_shapes(shape, mode):
     wb, wf = S.small_pair(*shape, 0.02, 1e-3, seed=shape[0] * 7 + shape[1])
@@ -110,9 +111,12 @@ def _bf16(a):
     return torch.from_numpy(np.asarray(a, np.float32)).to(torch.bfloat16).to(DEV)
 
 
-def test_compress_special_values():
+@pytest.mark.parametrize("d_in", [256, 2048, 4160])
+def test_compress_special_values(d_in):
+    """Zero deltas of either sign, a constant magnitude, inf, NaN and |d| on
+    either side of 2^15; the wider rows are split over two waves."""
     rng = np.random.default_rng(5)
-    d_out, d_in = 8, 256
+    d_out = 8
     base = rng.normal(0, 0.02, (d_out, d_in)).astype(np.float32)
     wb = _bf16(base)
     # row 0: zero delta (+0 and -0); row 1: constant magnitude 2^-12
