@@ -413,6 +413,83 @@ class LayerWorkload:
         return out
 
 
+class DecodeLayerWorkload(LayerWorkload):
+    """One 70B-shaped layer, one variant, per-row alpha, through the decode
+    kernel at M = 1, 4 and 16 tokens: the single-variant decode at the
+    layer's shapes (the default workload measures it on 4096x4096).  Each
+    (matrix, M) range cycles over operand copies of at least twice the
+    last-level cache, as for the other layer workloads."""
+
+    def __init__(self, name, dev):
+        wl = S.WORKLOADS[name]
+        self.name, self.wl, self.dev = name, wl, dev
+        self.mode = wl.alpha_mode
+        self.kind = "decode"
+        self.ms = tuple(wl.tokens)
+        self.m = max(self.ms)
+        g = S.generator(wl.seed, dev)
+        self.bases = S.draw_layer_bases(wl, g, dev)
+        self.packs, self.alphas = [], []
+        for _, i, wf in S.iter_finetuned(self.bases, S.variant_scales(wl), g):
+            p, a = T.compress(wf, self.bases[i], self.mode)
+            self.packs.append(p)
+            self.alphas.append(a)
+            del wf
+        self.xs = S.draw_layer_inputs(wl, self.m, g, dev)
+        self.distinct = 1
+        self.ys = [torch.empty(self.m, d_out, dtype=torch.bfloat16, device=dev)
+                   for _, d_out, _ in wl.matrices]
+        self.R = 1
+        self.rot = []
+        for i in range(len(self.bases)):
+            ops = (self.xs[i], self.bases[i], self.packs[i], self.alphas[i])
+            nbytes = sum(t.numel() * t.element_size() for t in ops)
+            copies = max(2, math.ceil(2 * MALL_BYTES / nbytes))
+            self.rot.append([ops] + [tuple(t.clone() for t in ops) for _ in range(copies - 1)])
+
+    def run_m(self, i, m, c=0):
+        x, wb, p, a = self.rot[i][c % len(self.rot[i])]
+        T.linear(x[:m], wb, p, a, self.mode, y=self.ys[i][:m])
+
+    def one_pass(self, j):
+        for m in self.ms:
+            for i in range(len(self.bases)):
+                self.run_m(i, m)
+
+    def ranges(self):
+        out = {}
+        for i, (nm, _, _) in enumerate(self.wl.matrices):
+            n = len(self.rot[i]) * RANGE_CYCLES
+            for m in self.ms:
+                out[f"decode_m{m}_{nm}"] = (n, lambda i=i, m=m, n=n: [self.run_m(i, m, c)
+                                                                      for c in range(n)])
+        return out
+
+    def bytes_of(self, i, m):
+        _, d_out, d_in = self.wl.matrices[i]
+        n = d_out * d_in
+        return 2 * n + n // 8 + 4 * d_out + 2 * m * d_in + 2 * m * d_out
+
+    def report(self, avg_us, args, step_ms=None):
+        names = [nm for nm, _, _ in self.wl.matrices]
+        total_b = sum(self.bytes_of(i, m) for i in range(len(names)) for m in self.ms)
+        total_us = sum(avg_us[f"decode_m{m}_{nm}"] for nm in names for m in self.ms)
+        val = total_b / (total_us * 1e-6) / 1e9
+        per = {f"{nm}_m{m}": round(self.bytes_of(i, m) / (avg_us[f"decode_m{m}_{nm}"] * 1e-6)
+                                   / 1e9, 2)
+               for i, nm in enumerate(names) for m in self.ms}
+        layer_us = {f"m{m}": round(sum(avg_us[f"decode_m{m}_{nm}"] for nm in names), 2)
+                    for m in self.ms}
+        cfg = {"workload": f"{self.name}: {self.wl.note}", "tokens": list(self.ms),
+               "alpha_mode": "per_row", "matrices": [list(mm) for mm in self.wl.matrices]}
+        out = {"value": round(val, 2), "unit": "GB/s", "config": cfg, "per_matrix": per,
+               "roofline": roofline_entry("hbm", val, HBM_PEAK_GBS, "GB/s", None),
+               "layer_us": layer_us}
+        if step_ms:
+            out["value_per_step"] = round(total_b / (step_ms * 1e-3) / 1e9, 2)
+        return out
+
+
 class StackWorkload(LayerWorkload):
     """The 80-layer 70B-shaped stack resident on the GPU (137 GB of W_base and
     14 packed variants, about 257 GB), mixed-variant decode of 64 tokens with a
@@ -718,7 +795,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="proj_4096",
                     choices=["proj_4096", "layer70b_prefill", "layer70b_multi",
-                             "stack70b_multi"])
+                             "layer70b_decode", "stack70b_multi"])
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
     ap.add_argument("--counter-pass", action="store_true",
@@ -749,6 +826,8 @@ def main():
         w = ProjWorkload(dev)
     elif args.workload == "stack70b_multi":
         w = StackWorkload(args.workload, dev)
+    elif args.workload == "layer70b_decode":
+        w = DecodeLayerWorkload(args.workload, dev)
     else:
         w = LayerWorkload(args.workload, dev)
     torch.cuda.synchronize()

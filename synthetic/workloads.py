@@ -52,6 +52,10 @@ WORKLOADS = {
     "layer70b_prefill": Workload(
         "layer70b_prefill", 4, LAYER_70B, 0.015, 1e-3, 0, (2048,),
         note="one 70B-shaped layer, one variant, per-matrix alpha, prefill M=2048"),
+    "layer70b_decode": Workload(
+        "layer70b_decode", 6, LAYER_70B, 0.015, 5e-4, 1, (1, 4, 16),
+        note="one 70B-shaped layer, one variant, per-row alpha, decode M=1,4,16 "
+             "(the projection's decode token counts at the layer's shapes)"),
     "stack70b_multi": Workload(
         "stack70b_multi", 5, LAYER_70B, 0.015, 5e-4, 1, (64,), n_variants=14,
         layers=80,

@@ -388,6 +388,30 @@ def test_layer70b_multi_full_size():
         assert_y_close(y[:, ridx], ref, f"layer70b_multi {name}")
 
 
+def test_layer70b_decode_full_size():
+    """One variant of a 70B-shaped layer (per-row alpha) through the decode
+    kernel at M = 1, 4, 16, as the layer decode benchmark runs it: every
+    compression bit-exact on sampled rows, every output on sampled rows."""
+    wl = S.WORKLOADS["layer70b_decode"]
+    g = S.generator(wl.seed, DEV)
+    bases = S.draw_layer_bases(wl, g, DEV)
+    packs, alphas = [], []
+    for _, i, wf in S.iter_finetuned(bases, S.variant_scales(wl), g):
+        rows = _sample_rows(wf.shape[0], 6, 500 + i)
+        p, a = check_compress(wf, bases[i], 1, rows=rows)
+        packs.append(p)
+        alphas.append(a)
+        del wf
+    xs = S.draw_layer_inputs(wl, max(wl.tokens), g, DEV)
+    for i, (name, d_out, d_in) in enumerate(wl.matrices):
+        rows = _sample_rows(d_out, 48, 600 + i)
+        for m in wl.tokens:
+            y = T.linear(xs[i][:m], bases[i], packs[i], alphas[i], 1)
+            ref = oracle_y(xs[i][:m], bases[i], packs[i], alphas[i], 1, rows=rows)
+            assert_y_close(y[:, torch.as_tensor(rows, device=DEV)], ref,
+                           f"layer70b_decode {name} M={m}")
+
+
 def _progress(msg):
     import sys
     sys.__stderr__.write(f"  [stack70b] {msg}\n")
