@@ -90,9 +90,36 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void compress_rows_kernel(
   const uint16_t* b_row = w_base + (size_t)row * d_in;
   uint8_t* p_bytes = reinterpret_cast<uint8_t*>(packed) + (size_t)row * (d_in >> 3);
 
-  uint64_t acc = 0;
+  // Row sum of q = hi * 2^32 + lo as a (acc_lo, acc_hi) pair: one add with
+  // carry-out and one add with carry-in per element.
+  uint32_t acc_lo = 0, acc_hi = 0;
   uint32_t maxbits = 0;  // largest float bits of |d| * 2^16 (NaN bits sort above inf)
   const int n_chunks = (d_in + 511) >> 9;
+  const int n_full = d_in >> 9;  // chunks with all 512 elements present
+
+  // Sign byte, magnitude sum and running maximum of one chunk's 8 elements
+  // per lane.
+  auto chunk = [&](const u32x4& va, const u32x4& vb) -> uint32_t {
+    uint32_t sbyte = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t ua = (j & 1) ? (va[j >> 1] & 0xFFFF0000u) : (va[j >> 1] << 16);
+      const uint32_t ub = (j & 1) ? (vb[j >> 1] & 0xFFFF0000u) : (vb[j >> 1] << 16);
+      const float d = __uint_as_float(ua) - __uint_as_float(ub);
+      // sign bit 1 <=> +1 <=> not (d < 0): +0, -0 and NaN give +1.
+      sbyte |= (d < 0.0f) ? 0u : (1u << j);
+      const float ad = __builtin_fabsf(d) * 65536.0f;
+      maxbits = max(maxbits, __float_as_uint(ad));
+      // Conversions saturate for out-of-range values; such rows are
+      // recomputed or flagged below, so their sum here is discarded.
+      const uint32_t hi = (uint32_t)ad;
+      const uint32_t lo = (uint32_t)(__builtin_amdgcn_fractf(ad) * 4294967296.0f);
+      const uint32_t nl = acc_lo + lo;
+      acc_hi += hi + (nl < lo ? 1u : 0u);
+      acc_lo = nl;
+    }
+    return sbyte;
+  };
 
   // Four chunks per group: all eight 16-byte loads of a group are issued
   // before any is used (8 KiB per wave in flight; 16 KiB measured slower),
@@ -109,39 +136,31 @@ __global__ __launch_bounds__(kRowsPerBlock * kWave) void compress_rows_kernel(
       va[u] = ld128(a_row + e0);
       vb[u] = ld128(b_row + e0);
     }
+    // Byte `lane` of a chunk's 64 packed bytes holds its elements
+    // 8*lane .. 8*lane+7 (bit j = element 8*lane+j): one byte store per
+    // lane, 64 contiguous bytes per wave.
+    if (c0 + kGroup <= n_full) {  // uniform: a group of whole chunks, no checks
 #pragma unroll
-    for (int u = 0; u < kGroup; ++u) {
-      const int c = c0 + u;
-      if (c >= n_chunks) continue;  // uniform
-      if ((c << 9) + 512 > d_in && (c << 9) + (lane << 3) >= d_in) {
-        // d_in is a multiple of 64, so the active lanes of a partial chunk
-        // cover whole 64-element words; the rest contribute +1 signs (never
-        // stored) and zero magnitudes.
-        va[u] = u32x4{0u, 0u, 0u, 0u};
-        vb[u] = u32x4{0u, 0u, 0u, 0u};
-      }
-      uint32_t sbyte = 0;
+      for (int u = 0; u < kGroup; ++u)
+        p_bytes[((c0 + u) << 6) + lane] = (uint8_t)chunk(va[u], vb[u]);
+    } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const uint32_t ua = (j & 1) ? (va[u][j >> 1] & 0xFFFF0000u) : (va[u][j >> 1] << 16);
-        const uint32_t ub = (j & 1) ? (vb[u][j >> 1] & 0xFFFF0000u) : (vb[u][j >> 1] << 16);
-        const float d = __uint_as_float(ua) - __uint_as_float(ub);
-        // sign bit 1 <=> +1 <=> not (d < 0): +0, -0 and NaN give +1.
-        sbyte |= (d < 0.0f) ? 0u : (1u << j);
-        const float ad = __builtin_fabsf(d) * 65536.0f;
-        maxbits = max(maxbits, __float_as_uint(ad));
-        // Conversions saturate for out-of-range values; such rows are
-        // recomputed or flagged below, so their sum here is discarded.
-        const uint32_t hi = (uint32_t)ad;
-        const uint32_t lo = (uint32_t)(__builtin_amdgcn_fractf(ad) * 4294967296.0f);
-        acc += ((uint64_t)hi << 32) | lo;
+      for (int u = 0; u < kGroup; ++u) {
+        const int c = c0 + u;
+        if (c >= n_chunks) continue;  // uniform
+        if (c >= n_full && (c << 9) + (lane << 3) >= d_in) {
+          // d_in is a multiple of 64, so the active lanes of a partial chunk
+          // cover whole 64-element words; the rest contribute +1 signs
+          // (never stored) and zero magnitudes.
+          va[u] = u32x4{0u, 0u, 0u, 0u};
+          vb[u] = u32x4{0u, 0u, 0u, 0u};
+        }
+        const uint32_t sbyte = chunk(va[u], vb[u]);
+        if ((c << 9) + (lane << 3) < d_in) p_bytes[(c << 6) + lane] = (uint8_t)sbyte;
       }
-      // Byte `lane` of the chunk's 64 packed bytes holds its elements
-      // 8*lane .. 8*lane+7 (bit j = element 8*lane+j): one byte store per
-      // lane, 64 contiguous bytes per wave.
-      if ((c << 9) + (lane << 3) < d_in) p_bytes[(c << 6) + lane] = (uint8_t)sbyte;
     }
   }
+  const uint64_t acc = ((uint64_t)acc_hi << 32) | acc_lo;
 
   // Row-wide largest |d| * 2^16 (float bits; the values are >= 0, so their
   // bit patterns order like the values, and NaN patterns sort above inf).
