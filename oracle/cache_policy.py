@@ -131,3 +131,62 @@ class CachePolicy:
                 if best is None or self.last[u] < self.last[best]:
                     best = u
         return best
+
+
+class Router:
+    """Decode batches fed from a request queue over a CachePolicy.
+
+    Page section "Altyapı ayrıntıları", the routing paragraph: the router
+    keeps track of the requests in flight per variant and avoids head-of-line
+    blocking; requests for a variant whose delta is loading wait for that one
+    load.  Reading taken (listed in the design doc):
+
+    * a request registers with the cache once, the first time a batch is
+      formed after it arrived (so the cache counts it once); a FULL refusal
+      leaves it unregistered, to be tried again at the next batch;
+    * a registered request is ready once its variant is resident; a request
+      for the base model alone (variant -1) is ready at once and never
+      touches the cache;
+    * a batch takes the ready requests in arrival order, at most max_batch:
+      a later request whose variant is resident does not wait behind an
+      earlier one whose variant is still loading;
+    * completing a batch releases each served request's variant.
+    """
+
+    NEW, WAITING, READY = 0, 1, 2
+
+    def __init__(self, cache: CachePolicy):
+        self.cache = cache
+        self.queue = []          # [request id, variant, state, slot] in arrival order
+
+    def submit(self, rid: int, variant: int) -> None:
+        if not -1 <= variant < self.cache.V:
+            raise ValueError("variant out of range")
+        self.queue.append([rid, variant, self.READY if variant < 0 else self.NEW, -1])
+
+    def next_batch(self, max_batch: int):
+        """[(request id, variant, slot)] of the next batch, slot -1 for the base."""
+        if max_batch < 1:
+            raise ValueError("max_batch must be positive")
+        for r in self.queue:
+            if r[2] == self.NEW:
+                act, slot, _ = self.cache.request(r[1])
+                if act != FULL:
+                    r[2] = self.READY if act == HIT else self.WAITING
+                    r[3] = slot
+        for r in self.queue:
+            if r[2] == self.WAITING and self.cache.state[r[1]] == RESIDENT:
+                r[2] = self.READY
+        batch, rest = [], []
+        for r in self.queue:
+            if r[2] == self.READY and len(batch) < max_batch:
+                batch.append((r[0], r[1], r[3]))
+            else:
+                rest.append(r)
+        self.queue = rest
+        return batch
+
+    def complete(self, batch) -> None:
+        for _, v, _ in batch:
+            if v >= 0:
+                self.cache.release(v)

@@ -272,3 +272,111 @@ def test_delta_layout_offsets():
                                 (8192, 28672)], T.ALPHA_PER_ROW)
     assert [tuple(p.shape) for p, _ in views][0] == (10240, 128)
     assert [a.numel() for _, a in views] == [10240, 8192, 28672, 28672, 8192]
+
+
+# ------------------------------------------------------------------ router
+def read_router_traces():
+    traces, cur = [], None
+    for raw in open(GOLDEN):
+        line = raw.split("#", 1)[0].split()
+        if not line:
+            continue
+        if line[0] == "router":
+            cur = (tuple(int(t) for t in line[1:5]), [])
+        elif line[0] == "trace":
+            cur = None
+        elif cur is None:
+            continue
+        elif line[0] == "end":
+            traces.append(cur)
+            cur = None
+        elif line[0] == "batch":
+            want = [tuple(int(f) for f in item.split(":")) for item in line[3:]]
+            cur[1].append(("batch", int(line[1]), want))
+        elif line[0] == "submit":
+            cur[1].append(("submit", int(line[1]), int(line[2])))
+        elif line[0] == "loaded":
+            cur[1].append(("loaded", int(line[1])))
+        else:
+            cur[1].append(("complete",))
+    return traces
+
+
+def run_router_trace(make, steps):
+    cache, router = make()
+    open_batches = []
+    for st in steps:
+        if st[0] == "submit":
+            router.submit(st[1], st[2])
+        elif st[0] == "loaded":
+            cache.loaded(st[1])
+        elif st[0] == "batch":
+            got = router.next_batch(st[1])
+            assert [tuple(b) for b in got] == st[2], (st, got)
+            open_batches.append(got)
+        else:
+            router.complete(open_batches.pop())
+
+
+def test_router_oracle_golden_traces():
+    traces = read_router_traces()
+    assert len(traces) == 2
+    for (V, S, P, H), steps in traces:
+        def make():
+            c = CP.CachePolicy(V, S, P, H)
+            return c, CP.Router(c)
+        run_router_trace(make, steps)
+
+
+def test_router_oracle_properties_on_zipf_traffic():
+    """Every request is served exactly once, only when its variant is
+    resident, ready requests leave in arrival order, each request is counted
+    by the cache once, and with room for every variant and instant loads the
+    batches are plain arrival-order chunks."""
+    V = 14
+    rng = np.random.default_rng(21)
+    for S_, P in ((14, 6), (8, 6), (4, 2)):
+        c = CP.CachePolicy(V, S_, P, 0)
+        r = CP.Router(c)
+        served, submitted, counted = [], [], [0] * V
+        rid = 0
+        for step in range(400):
+            for _ in range(int(rng.integers(0, 4))):
+                v = int(zipf_trace(1, V, 1000 * step + rid)[0]) if rng.random() > 0.1 else -1
+                r.submit(rid, v)
+                submitted.append((rid, v))
+                rid += 1
+            for u in range(V):          # loads finish at random
+                if c.state[u] == CP.LOADING and rng.random() < 0.5:
+                    c.loaded(u)
+            batch = r.next_batch(int(rng.integers(1, 9)))
+            order = [b[0] for b in batch]
+            assert order == sorted(order)
+            for b_rid, v, slot in batch:
+                if v >= 0:
+                    assert c.state[v] == CP.RESIDENT and c.slot[v] == slot
+            served.extend(order)
+            r.complete(batch)
+        assert len(served) == len(set(served))
+        assert set(served) <= {i for i, _ in submitted}
+        for i, v in submitted:
+            if v >= 0 and (i in served or any(q[0] == i and q[2] != CP.Router.NEW
+                                               for q in r.queue)):
+                counted[v] += 1
+        assert counted == c.rate            # no halving: rate = registered requests
+    # room for all and instant loads: arrival-order chunks
+    c = CP.CachePolicy(V, V, 0, 0)
+    r = CP.Router(c)
+    for i in range(37):
+        r.submit(i, i % V)
+    served = []
+    for _ in range(20):
+        b = r.next_batch(8)          # the first call registers everything and serves nothing
+        for u in range(V):
+            if c.state[u] == CP.LOADING:
+                c.loaded(u)
+        if b:
+            served.append([x[0] for x in b])
+            r.complete(b)
+    flat = [i for chunk in served for i in chunk]
+    assert flat == list(range(37)) and all(len(ch) == 8 for ch in served[:-1])
