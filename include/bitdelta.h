@@ -310,6 +310,44 @@ int bitdelta_cache_acquire(bitdelta_cache* cache, int32_t variant, void* copy_st
  * receives how many.  BITDELTA_ERR_CACHE without attached memory. */
 int bitdelta_cache_poll(bitdelta_cache* cache, int32_t* n_loaded);
 
+/*
+ * Router - decode batches fed from a request queue over a delta cache
+ * (section "Altyapı ayrıntıları", the routing paragraph: requests are
+ * tracked per variant and none waits behind a variant whose delta is
+ * loading).  Exactly:
+ * - bitdelta_router_submit appends a request (caller's id, variant in
+ *   [-1, n_variants); -1 = the base model alone) to the queue;
+ * - bitdelta_router_next_batch first registers every unregistered request
+ *   with the cache, in arrival order: one cache request each (counted once);
+ *   FULL leaves it unregistered for the next batch.  Without cache memory
+ *   this is bitdelta_cache_request; with memory attached it is the request
+ *   of bitdelta_cache_acquire, whose loads go on copy_stream and which makes
+ *   no stream wait (finished loads are polled first).  A registered request
+ *   is ready once its variant is resident; a base request is ready at once.
+ *   The batch is the ready requests in arrival order, at most max_batch;
+ *   they leave the queue.  ids, variants and slots (each >= max_batch
+ *   entries, host) receive the batch's request ids, variants and slot
+ *   numbers (-1 for base requests); *n its size (0 allowed).  With memory
+ *   attached every slot of the batch holds its variant's bytes already.
+ * - bitdelta_router_complete releases the variants of a served batch (the
+ *   variants array as next_batch wrote it); with memory attached the
+ *   releases record their events on use_stream.
+ * The cache must outlive the router; router calls lock the router, then the
+ * cache.  Returns BITDELTA_ERR_CACHE for a variant out of range,
+ * max_batch < 1 or a release of a variant not in use.
+ */
+typedef struct bitdelta_router bitdelta_router;
+
+int bitdelta_router_create(bitdelta_cache* cache, bitdelta_router** out);
+void bitdelta_router_destroy(bitdelta_router* router);
+int bitdelta_router_submit(bitdelta_router* router, int64_t request_id, int32_t variant);
+int bitdelta_router_next_batch(bitdelta_router* router, int32_t max_batch, void* copy_stream,
+                               int64_t* ids, int32_t* variants, int32_t* slots, int32_t* n);
+int bitdelta_router_complete(bitdelta_router* router, int32_t n, const int32_t* variants,
+                             void* use_stream);
+/* Requests still queued (submitted, not yet in a batch). */
+int bitdelta_router_pending(bitdelta_router* router, int32_t* n);
+
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* bitdelta_status_string(int status);
 

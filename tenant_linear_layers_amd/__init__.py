@@ -27,6 +27,7 @@ from .bitdelta import (  # noqa: F401
     lib,
     linear,
     linear_multi,
+    Router,
     ratio_to_f32_bits,
     reconstruct,
     status_string,

@@ -55,6 +55,12 @@ EXPORTS = (
     "bitdelta_cache_attach",
     "bitdelta_cache_acquire",
     "bitdelta_cache_poll",
+    "bitdelta_router_create",
+    "bitdelta_router_destroy",
+    "bitdelta_router_submit",
+    "bitdelta_router_next_batch",
+    "bitdelta_router_complete",
+    "bitdelta_router_pending",
 )
 
 
@@ -114,6 +120,18 @@ def lib() -> ctypes.CDLL:
     L.bitdelta_cache_acquire.restype = i32
     L.bitdelta_cache_poll.argtypes = [vp, pi32]
     L.bitdelta_cache_poll.restype = i32
+    L.bitdelta_router_create.argtypes = [vp, ctypes.POINTER(vp)]
+    L.bitdelta_router_create.restype = i32
+    L.bitdelta_router_destroy.argtypes = [vp]
+    L.bitdelta_router_destroy.restype = None
+    L.bitdelta_router_submit.argtypes = [vp, i64, ctypes.c_int32]
+    L.bitdelta_router_submit.restype = i32
+    L.bitdelta_router_next_batch.argtypes = [vp, ctypes.c_int32, vp, pi64, pi32, pi32, pi32]
+    L.bitdelta_router_next_batch.restype = i32
+    L.bitdelta_router_complete.argtypes = [vp, ctypes.c_int32, pi32, vp]
+    L.bitdelta_router_complete.restype = i32
+    L.bitdelta_router_pending.argtypes = [vp, pi32]
+    L.bitdelta_router_pending.restype = i32
     _lib = L
     return L
 
@@ -414,4 +432,56 @@ class DeltaCache:
     def poll(self) -> int:
         n = ctypes.c_int32()
         _check(lib().bitdelta_cache_poll(self._h, ctypes.byref(n)), "bitdelta_cache_poll")
+        return n.value
+
+
+class Router:
+    """A libbitdelta router (bitdelta_router_*) over a DeltaCache: decode
+    batches of ready requests in arrival order; with the cache's memory
+    attached, registering a request starts its load on the copy stream."""
+
+    def __init__(self, cache: DeltaCache):
+        h = ctypes.c_void_p()
+        _check(lib().bitdelta_router_create(cache._h, ctypes.byref(h)), "bitdelta_router_create")
+        self._h = h
+        self.cache = cache          # kept alive: the cache must outlive the router
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None and self._h.value:
+            lib().bitdelta_router_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        self.close()
+
+    def submit(self, request_id: int, variant: int) -> None:
+        _check(lib().bitdelta_router_submit(self._h, request_id, variant), "bitdelta_router_submit")
+
+    def next_batch(self, max_batch: int, copy_stream=None):
+        """[(request id, variant, slot)] of the next batch (slot -1 for the base)."""
+        ids = (ctypes.c_int64 * max(max_batch, 1))()
+        vs = (ctypes.c_int32 * max(max_batch, 1))()
+        ss = (ctypes.c_int32 * max(max_batch, 1))()
+        n = ctypes.c_int32()
+        attached = self.cache._slots is not None
+        cs = _stream(copy_stream) if attached else ctypes.c_void_p(None)
+        if attached:
+            with _on(self.cache._slots[0].device):
+                st = lib().bitdelta_router_next_batch(self._h, max_batch, cs, ids, vs, ss,
+                                                      ctypes.byref(n))
+        else:
+            st = lib().bitdelta_router_next_batch(self._h, max_batch, cs, ids, vs, ss,
+                                                  ctypes.byref(n))
+        _check(st, "bitdelta_router_next_batch")
+        return [(int(ids[i]), int(vs[i]), int(ss[i])) for i in range(n.value)]
+
+    def complete(self, batch, use_stream=None) -> None:
+        vs = (ctypes.c_int32 * max(len(batch), 1))(*[b[1] for b in batch])
+        st_ = _stream(use_stream) if self.cache._slots is not None else ctypes.c_void_p(None)
+        _check(lib().bitdelta_router_complete(self._h, len(batch), vs, st_),
+               "bitdelta_router_complete")
+
+    def pending(self) -> int:
+        n = ctypes.c_int32()
+        _check(lib().bitdelta_router_pending(self._h, ctypes.byref(n)), "bitdelta_router_pending")
         return n.value

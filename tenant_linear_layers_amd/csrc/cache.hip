@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <deque>
 #include <mutex>
 #include <new>
 #include <numeric>
@@ -147,6 +148,48 @@ int poll_locked(bitdelta_cache* c, int32_t* n_loaded) {
   return BITDELTA_OK;
 }
 
+// One use of v ends (caller holds the lock; v is in use).
+int release_locked(bitdelta_cache* c, int32_t v, hipStream_t stream) {
+  if (c->attached) {
+    const int32_t s = c->slot[v];
+    if (hipEventRecord(c->free_ev[s], stream) != hipSuccess) return BITDELTA_ERR_HIP;
+    c->free_recorded[s] = 1;
+  }
+  c->users[v] -= 1;
+  return BITDELTA_OK;
+}
+
+// One request that moves the bytes (caller holds the lock, memory attached):
+// on a LOAD, the copy into the slot after the slot's last release; with a
+// use stream, LOAD and QUEUED make it wait for the load.
+int acquire_locked(bitdelta_cache* c, int32_t v, hipStream_t cs, bool wait_use, hipStream_t us,
+                   int32_t* action, int32_t* slot, int32_t* evicted) {
+  request_locked(c, v, action, slot, evicted);
+  if (*action == BITDELTA_CACHE_FULL) return BITDELTA_OK;
+  const int32_t s = *slot;
+  if (*action == BITDELTA_CACHE_LOAD) {
+    hipError_t e = hipSuccess;
+    if (c->free_recorded[s]) e = hipStreamWaitEvent(cs, c->free_ev[s], 0);
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(c->slot_dev[s], c->src[v], c->src_bytes[v], hipMemcpyHostToDevice, cs);
+    if (e == hipSuccess) e = hipEventRecord(c->load_ev[v], cs);
+    if (e != hipSuccess) {
+      // the variant is not loading after all; the evicted one stays evicted
+      c->state[v] = BITDELTA_CACHE_ABSENT;
+      c->slot[v] = -1;
+      c->owner[s] = -1;
+      c->users[v] -= 1;
+      return BITDELTA_ERR_HIP;
+    }
+  }
+  if (wait_use && *action != BITDELTA_CACHE_HIT &&
+      hipStreamWaitEvent(us, c->load_ev[v], 0) != hipSuccess) {
+    c->users[v] -= 1;  // the caller gets no slot and releases nothing
+    return BITDELTA_ERR_HIP;
+  }
+  return BITDELTA_OK;
+}
+
 void destroy_events(bitdelta_cache* c) {
   for (auto& e : c->load_ev)
     if (e) (void)hipEventDestroy(e);
@@ -210,14 +253,7 @@ BD_EXPORT int bitdelta_cache_release(bitdelta_cache* c, int32_t variant, void* s
   if (!c) return BITDELTA_ERR_NULL;
   std::lock_guard<std::mutex> lock(c->mu);
   if (!valid_variant(c, variant) || c->users[variant] <= 0) return BITDELTA_ERR_CACHE;
-  if (c->attached) {
-    const int32_t s = c->slot[variant];
-    if (hipEventRecord(c->free_ev[s], static_cast<hipStream_t>(stream)) != hipSuccess)
-      return BITDELTA_ERR_HIP;
-    c->free_recorded[s] = 1;
-  }
-  c->users[variant] -= 1;
-  return BITDELTA_OK;
+  return release_locked(c, variant, static_cast<hipStream_t>(stream));
 }
 
 BD_EXPORT int bitdelta_cache_state(bitdelta_cache* c, int32_t variant, int32_t* state,
@@ -291,34 +327,131 @@ BD_EXPORT int bitdelta_cache_acquire(bitdelta_cache* c, int32_t variant, void* c
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return BITDELTA_ERR_HIP;
   if (dev != c->device) return BITDELTA_ERR_DEVICE;
-  const int st = poll_locked(c, nullptr);
+  int st = poll_locked(c, nullptr);
   if (st != BITDELTA_OK) return st;
   int32_t s = -1;
-  request_locked(c, variant, action, &s, evicted);
-  if (*action == BITDELTA_CACHE_FULL) return BITDELTA_OK;
-  hipStream_t cs = static_cast<hipStream_t>(copy_stream);
-  hipStream_t us = static_cast<hipStream_t>(use_stream);
-  if (*action == BITDELTA_CACHE_LOAD) {
-    hipError_t e = hipSuccess;
-    if (c->free_recorded[s]) e = hipStreamWaitEvent(cs, c->free_ev[s], 0);
-    if (e == hipSuccess)
-      e = hipMemcpyAsync(c->slot_dev[s], c->src[variant], c->src_bytes[variant],
-                         hipMemcpyHostToDevice, cs);
-    if (e == hipSuccess) e = hipEventRecord(c->load_ev[variant], cs);
-    if (e != hipSuccess) {
-      // the variant is not loading after all; the evicted one stays evicted
-      c->state[variant] = BITDELTA_CACHE_ABSENT;
-      c->slot[variant] = -1;
-      c->owner[s] = -1;
-      c->users[variant] -= 1;
-      return BITDELTA_ERR_HIP;
+  st = acquire_locked(c, variant, static_cast<hipStream_t>(copy_stream), true,
+                      static_cast<hipStream_t>(use_stream), action, &s, evicted);
+  if (st != BITDELTA_OK || *action == BITDELTA_CACHE_FULL) return st;
+  *slot_ptr = c->slot_dev[s];
+  return BITDELTA_OK;
+}
+
+// ------------------------------------------------------------------ router
+// Decode batches fed from a request queue over a cache (section "Altyapı
+// ayrıntıları", the routing paragraph: requests are tracked per variant and
+// nothing is blocked behind a variant whose delta is loading).  A request
+// registers with the cache once, at the first batch formed after it arrived
+// (a FULL refusal leaves it unregistered until the next batch); it is ready
+// once its variant is resident (a base-only request at once); a batch takes
+// ready requests in arrival order.  With memory attached the registration
+// starts the loads on the copy stream and no stream waits on them: a request
+// joins a batch only after its load has completed.
+
+struct bitdelta_router {
+  std::mutex mu;
+  bitdelta_cache* cache = nullptr;
+  struct Req {
+    int64_t id;
+    int32_t v, state, slot;
+  };
+  std::deque<Req> q;
+};
+
+namespace {
+constexpr int32_t kReqNew = 0, kReqWaiting = 1, kReqReady = 2;
+}
+
+BD_EXPORT int bitdelta_router_create(bitdelta_cache* cache, bitdelta_router** out) {
+  if (!cache || !out) return BITDELTA_ERR_NULL;
+  *out = nullptr;
+  bitdelta_router* r = new (std::nothrow) bitdelta_router;
+  if (!r) return BITDELTA_ERR_CACHE;
+  r->cache = cache;
+  *out = r;
+  return BITDELTA_OK;
+}
+
+BD_EXPORT void bitdelta_router_destroy(bitdelta_router* r) { delete r; }
+
+BD_EXPORT int bitdelta_router_submit(bitdelta_router* r, int64_t request_id, int32_t variant) {
+  if (!r) return BITDELTA_ERR_NULL;
+  std::lock_guard<std::mutex> lock(r->mu);
+  if (variant < -1 || variant >= r->cache->V) return BITDELTA_ERR_CACHE;
+  r->q.push_back({request_id, variant, variant < 0 ? kReqReady : kReqNew, -1});
+  return BITDELTA_OK;
+}
+
+BD_EXPORT int bitdelta_router_next_batch(bitdelta_router* r, int32_t max_batch, void* copy_stream,
+                                         int64_t* ids, int32_t* variants, int32_t* slots,
+                                         int32_t* n) {
+  if (!r || !ids || !variants || !slots || !n) return BITDELTA_ERR_NULL;
+  *n = 0;
+  if (max_batch < 1) return BITDELTA_ERR_CACHE;
+  std::lock_guard<std::mutex> lock(r->mu);
+  bitdelta_cache* c = r->cache;
+  std::lock_guard<std::mutex> clock(c->mu);
+  if (c->attached) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return BITDELTA_ERR_HIP;
+    if (dev != c->device) return BITDELTA_ERR_DEVICE;
+    const int st = poll_locked(c, nullptr);
+    if (st != BITDELTA_OK) return st;
+  }
+  for (auto& q : r->q) {
+    if (q.state != kReqNew) continue;
+    int32_t act = 0, slot = -1, ev = -1;
+    if (c->attached) {
+      const int st = acquire_locked(c, q.v, static_cast<hipStream_t>(copy_stream), false,
+                                    nullptr, &act, &slot, &ev);
+      if (st != BITDELTA_OK) return st;
+    } else {
+      request_locked(c, q.v, &act, &slot, &ev);
+    }
+    if (act == BITDELTA_CACHE_FULL) continue;
+    q.state = act == BITDELTA_CACHE_HIT ? kReqReady : kReqWaiting;
+    q.slot = slot;
+  }
+  for (auto& q : r->q)
+    if (q.state == kReqWaiting && c->state[q.v] == BITDELTA_CACHE_RESIDENT) q.state = kReqReady;
+  std::deque<bitdelta_router::Req> rest;
+  int32_t k = 0;
+  for (const auto& q : r->q) {
+    if (q.state == kReqReady && k < max_batch) {
+      ids[k] = q.id;
+      variants[k] = q.v;
+      slots[k] = q.slot;
+      ++k;
+    } else {
+      rest.push_back(q);
     }
   }
-  if (*action != BITDELTA_CACHE_HIT &&
-      hipStreamWaitEvent(us, c->load_ev[variant], 0) != hipSuccess) {
-    c->users[variant] -= 1;  // the caller gets no slot and releases nothing
-    return BITDELTA_ERR_HIP;
+  r->q.swap(rest);
+  *n = k;
+  return BITDELTA_OK;
+}
+
+BD_EXPORT int bitdelta_router_complete(bitdelta_router* r, int32_t n, const int32_t* variants,
+                                       void* use_stream) {
+  if (!r || (n > 0 && !variants)) return BITDELTA_ERR_NULL;
+  std::lock_guard<std::mutex> lock(r->mu);
+  bitdelta_cache* c = r->cache;
+  std::lock_guard<std::mutex> clock(c->mu);
+  for (int32_t i = 0; i < n; ++i)
+    if (variants[i] >= c->V || variants[i] < -1 ||
+        (variants[i] >= 0 && c->users[variants[i]] <= 0))
+      return BITDELTA_ERR_CACHE;
+  for (int32_t i = 0; i < n; ++i) {
+    if (variants[i] < 0) continue;
+    const int st = release_locked(c, variants[i], static_cast<hipStream_t>(use_stream));
+    if (st != BITDELTA_OK) return st;
   }
-  *slot_ptr = c->slot_dev[s];
+  return BITDELTA_OK;
+}
+
+BD_EXPORT int bitdelta_router_pending(bitdelta_router* r, int32_t* n) {
+  if (!r || !n) return BITDELTA_ERR_NULL;
+  std::lock_guard<std::mutex> lock(r->mu);
+  *n = (int32_t)r->q.size();
   return BITDELTA_OK;
 }

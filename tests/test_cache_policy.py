@@ -16,12 +16,17 @@ ACTIONS = {"HIT": CP.HIT, "QUEUED": CP.QUEUED, "LOAD": CP.LOAD, "FULL": CP.FULL}
 
 
 def read_traces():
-    traces, cur = [], None
+    """The policy traces ("trace" blocks; "router" blocks are skipped)."""
+    traces, cur, skip = [], None, False
     for raw in open(GOLDEN):
         line = raw.split("#", 1)[0].split()
         if not line:
             continue
-        if line[0] == "trace":
+        if line[0] == "router":
+            skip = True
+        elif skip:
+            skip = line[0] != "end"
+        elif line[0] == "trace":
             cur = (tuple(int(t) for t in line[1:5]), [])
         elif line[0] == "end":
             traces.append(cur)
@@ -380,3 +385,60 @@ def test_router_oracle_properties_on_zipf_traffic():
             r.complete(b)
     flat = [i for chunk in served for i in chunk]
     assert flat == list(range(37)) and all(len(ch) == 8 for ch in served[:-1])
+
+
+def test_router_library_golden_traces():
+    import tenant_linear_layers_amd as T
+    for (V, S, P, H), steps in read_router_traces():
+        def make():
+            c = T.DeltaCache(V, S, P, H)
+            return c, T.Router(c)
+        run_router_trace(make, steps)
+
+
+@pytest.mark.parametrize("V,S,P,H", [(14, 8, 6, 0), (14, 4, 2, 16), (6, 2, 0, 0), (30, 10, 3, 50)])
+def test_router_library_matches_oracle(V, S, P, H):
+    """Batch by batch, the native router equals the oracle's on Zipf(1.1)
+    traffic with base-only requests, random batch sizes, loads that finish
+    at random and batches completed out of order."""
+    import tenant_linear_layers_amd as T
+    rng = np.random.default_rng(V * 100 + S)
+    lc = T.DeltaCache(V, S, P, H)
+    lr = T.Router(lc)
+    oc = CP.CachePolicy(V, S, P, H)
+    orr = CP.Router(oc)
+    open_b = []
+    rid = 0
+    for step in range(600):
+        for _ in range(int(rng.integers(0, 4))):
+            v = int(zipf_trace(1, V, 7 * step + rid)[0]) if rng.random() > 0.1 else -1
+            lr.submit(rid, v)
+            orr.submit(rid, v)
+            rid += 1
+        for u in range(V):
+            if oc.state[u] == CP.LOADING and rng.random() < 0.4:
+                lc.loaded(u)
+                oc.loaded(u)
+        mb = int(rng.integers(1, 9))
+        got = lr.next_batch(mb)
+        want = orr.next_batch(mb)
+        assert got == [tuple(w) for w in want], step
+        open_b.append(got)
+        while open_b and rng.random() < 0.6:
+            b = open_b.pop(int(rng.integers(len(open_b))))
+            lr.complete(b)
+            orr.complete(b)
+        assert lr.pending() == len(orr.queue)
+    for u in range(V):
+        assert lc.state(u) == (oc.state[u], oc.slot[u], oc.rate[u])
+
+
+def test_router_library_rejects_bad_calls():
+    import tenant_linear_layers_amd as T
+    c = T.DeltaCache(4, 2, 0, 0)
+    r = T.Router(c)
+    for call in (lambda: r.submit(0, 4), lambda: r.submit(0, -2), lambda: r.next_batch(0),
+                 lambda: r.complete([(0, 1, 0)])):
+        with pytest.raises(T.BitDeltaError) as e:
+            call()
+        assert e.value.status == 10

@@ -204,3 +204,60 @@ def test_cache_eviction_waits_for_released_work():
     for k, y in enumerate(ys0):
         assert torch.equal(y.view(torch.int16), want[0].view(torch.int16)), k
     assert torch.equal(y1.view(torch.int16), want[1].view(torch.int16))
+
+
+def test_router_feeds_mixed_batches():
+    """Requests over 8 variants (Zipf, one in ten base-only) through the
+    router and a 3-slot cache into bitdelta_linear_multi: every request is
+    served once, each batch's output equals the same call on the variants'
+    own tensors bit for bit (and the oracle on some batches); nothing waits
+    on the host except when no request is ready."""
+    shapes = [(256, 1024)]
+    mode = T.ALPHA_PER_ROW
+    V, Sl, P = 8, 3, 1
+    bases, packs, alphas, blobs = make_variants(shapes, V, mode, 81)
+    cache, slots = make_cache(V, Sl, P, 0, blobs)
+    router = T.Router(cache)
+    copy = torch.cuda.Stream()
+    g = S.generator(82)
+    rng = np.random.default_rng(83)
+    n_req = 120
+    xs = S.draw_activations(n_req, shapes[0][1], g).to(DEV)
+    variant_of = [int(v) if rng.random() > 0.1 else -1 for v in S.zipf_ids(n_req, V, 84)]
+    submitted, served, outs = 0, [], []
+    for it in range(2000):
+        for _ in range(int(rng.integers(0, 6))):
+            if submitted < n_req:
+                router.submit(submitted, variant_of[submitted])
+                submitted += 1
+        batch = router.next_batch(16, copy)
+        if not batch:
+            if submitted == n_req and router.pending() == 0:
+                break
+            copy.synchronize()   # only loads are outstanding
+            continue
+        rids = [b[0] for b in batch]
+        local = sorted({b[1] for b in batch if b[1] >= 0})
+        slot_of = {b[1]: b[2] for b in batch if b[1] >= 0}
+        ids = torch.tensor([local.index(b[1]) if b[1] >= 0 else -1 for b in batch],
+                           dtype=torch.int32, device=DEV)
+        x = xs[torch.as_tensor(rids, device=DEV)].contiguous()
+        if local:
+            views = [T.delta_views(slots[slot_of[v]], shapes, mode)[0] for v in local]
+            y = T.linear_multi(x, ids, bases[0], [p for p, _ in views], [a for _, a in views], mode)
+            y_direct = T.linear_multi(x, ids, bases[0], [packs[v][0] for v in local],
+                                      [alphas[v][0] for v in local], mode)
+        else:
+            y = y_direct = T.linear_multi(x, ids, bases[0], [packs[0][0]], [alphas[0][0]], mode)
+        outs.append((y, y_direct, x, ids, local))
+        served.extend(rids)
+        router.complete(batch)
+    torch.cuda.synchronize()
+    assert sorted(served) == list(range(n_req))
+    for k, (y, y_direct, x, ids, local) in enumerate(outs):
+        assert torch.equal(y.view(torch.int16), y_direct.view(torch.int16)), k
+        if k % 10 == 0 and local:
+            ref = O.linear_multi(bits16(x), ids.cpu().numpy(), bits16(bases[0]),
+                                 [packed_u64(packs[v][0]) for v in local],
+                                 [alphas[v][0].cpu().numpy() for v in local], mode)
+            assert_y_close(y, ref, f"router batch {k}")
