@@ -548,6 +548,114 @@ class StackWorkload(LayerWorkload):
         return rep
 
 
+def serve_layer70b(args, dev):
+    """The serving loop around the path on one 70B-shaped layer: the 14
+    variants' deltas of the layer (QKV, O, gate, up, down; per-row alpha;
+    Laplace b_v log-uniform in [2e-4, 2e-3], as layer70b_multi) live in
+    page-locked host blobs; a delta cache of 8 device slots with the top 6
+    variants pinned (the page's split of 14) loads them on demand; a router
+    forms decode batches of up to 64 ready requests from a Zipf(1.1) request
+    stream arriving 64 per batch slot; every batch runs the layer's five
+    mixed-variant linears on the cached slots.  Two passes over 4096
+    requests each: cold (empty cache) and warm (the cache as the first left
+    it).  value is the linears' algorithmic HBM bytes over the pass's wall
+    time; tokens_per_s is requests served per second through the layer."""
+    wl = S.WORKLOADS["layer70b_multi"]
+    mode = wl.alpha_mode
+    g = S.generator(wl.seed, dev)
+    bases = S.draw_layer_bases(wl, g, dev)
+    shapes = [(d_out, d_in) for _, d_out, d_in in wl.matrices]
+    _, total = T.delta_layout(shapes, mode)
+    V = wl.n_variants
+    packs = [[None] * len(shapes) for _ in range(V)]
+    alphas = [[None] * len(shapes) for _ in range(V)]
+    for v, i, wf in S.iter_finetuned(bases, S.variant_scales(wl), g):
+        packs[v][i], alphas[v][i] = T.compress(wf, bases[i], mode)
+        del wf
+    blobs = [torch.empty(total, dtype=torch.uint8, pin_memory=True) for _ in range(V)]
+    for v in range(V):
+        for (hp, ha), p, a in zip(T.delta_views(blobs[v], shapes, mode), packs[v], alphas[v]):
+            hp.copy_(p.cpu())
+            ha.copy_(a.cpu())
+    n_slots, n_pinned, max_m, n_req = 8, 6, 64, 4096
+    cache = T.DeltaCache(V, n_slots, n_pinned, 0)
+    slots = [torch.empty(total, dtype=torch.uint8, device=dev) for _ in range(n_slots)]
+    cache.attach(slots, blobs)
+    router = T.Router(cache)
+    copy = torch.cuda.Stream()
+    xs = S.draw_layer_inputs(wl, max_m, g, dev)
+    ys = [torch.empty(max_m, d_out, dtype=torch.bfloat16, device=dev) for d_out, _ in shapes]
+    slot_views = [T.delta_views(t, shapes, mode) for t in slots]
+    torch.cuda.synchronize()
+    print(f"[bench] serve_layer70b: {V} variants, {n_slots} slots ({n_pinned} pinned), "
+          f"delta {total:,} B per variant", file=sys.stderr, flush=True)
+
+    def one_pass(seed, rid0, checks):
+        ids_all = S.zipf_ids(n_req, V, seed)
+        submitted = served = batches = 0
+        nbytes = 0
+        distinct = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while served < n_req:
+            for _ in range(max_m):
+                if submitted < n_req:
+                    router.submit(rid0 + submitted, int(ids_all[submitted]))
+                    submitted += 1
+            batch = router.next_batch(max_m, copy)
+            if not batch:
+                copy.synchronize()   # every queued request waits for a load
+                continue
+            m = len(batch)
+            local = sorted({b[1] for b in batch})
+            slot_of = {b[1]: b[2] for b in batch}
+            ids = torch.tensor([local.index(b[1]) for b in batch], dtype=torch.int32,
+                               device=dev)
+            for i, (d_out, d_in) in enumerate(shapes):
+                pl = [slot_views[slot_of[v]][i][0] for v in local]
+                al = [slot_views[slot_of[v]][i][1] for v in local]
+                T.linear_multi(xs[i][:m], ids, bases[i], pl, al, mode, y=ys[i][:m])
+                n = d_out * d_in
+                nbytes += (2 * n + len(local) * (n // 8 + 4 * d_out) + 2 * m * d_in
+                           + 2 * m * d_out + 4 * m)
+            if batches in checks:
+                # the cached slots against the variants' own tensors, bit for bit
+                i = 2
+                y_ref = T.linear_multi(xs[i][:m], ids, bases[i], [packs[v][i] for v in local],
+                                       [alphas[v][i] for v in local], mode)
+                torch.cuda.synchronize()
+                if not torch.equal(ys[i][:m].view(torch.int16), y_ref.view(torch.int16)):
+                    raise RuntimeError("served batch differs from the direct call")
+            router.complete(batch)
+            served += m
+            batches += 1
+            distinct.append(len(local))
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return {"requests": n_req, "batches": batches, "mean_batch": round(n_req / batches, 2),
+                "mean_distinct_variants": round(sum(distinct) / len(distinct), 2),
+                "wall_ms": round(wall * 1e3, 3), "tokens_per_s": round(n_req / wall, 1),
+                "linears_gbs": round(nbytes / wall / 1e9, 2)}
+
+    cold = one_pass(101, 0, {0, 5})
+    warm = one_pass(102, n_req, {0, 7, 30})
+    print(f"[bench] cold {cold['wall_ms']} ms, warm {warm['wall_ms']} ms", file=sys.stderr,
+          flush=True)
+    out = {"metric": METRIC, "value": warm["linears_gbs"], "unit": "GB/s", "n_gpus": 1,
+           "steps": 1, "warmup": 1, "ms_per_step": warm["wall_ms"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": "serve_layer70b: one 70B-shaped layer, 14 variants' deltas "
+                                  "in pinned host memory, delta cache of 8 slots (top 6 "
+                                  "pinned), router batches of up to 64 Zipf(1.1) requests "
+                                  "through the layer's five mixed-variant linears",
+                      "variants": V, "slots": n_slots, "pinned": n_pinned, "max_batch": max_m,
+                      "delta_bytes_per_variant": total},
+           "cold": cold, "warm": warm,
+           "roofline": roofline_entry("hbm", warm["linears_gbs"], HBM_PEAK_GBS, "GB/s", None),
+           "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------ CPU oracle
 def cpu_baseline(w: ProjWorkload, budget_s: float):
     """The oracle, as it stands, on a bounded sample of the same workload:
@@ -795,7 +903,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="proj_4096",
                     choices=["proj_4096", "layer70b_prefill", "layer70b_multi",
-                             "layer70b_decode", "stack70b_multi"])
+                             "layer70b_decode", "stack70b_multi", "serve_layer70b"])
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
     ap.add_argument("--counter-pass", action="store_true",
@@ -822,6 +930,9 @@ def main():
     torch.cuda.set_device(dev)
     T.lib()
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
+    if args.workload == "serve_layer70b":
+        serve_layer70b(args, dev)
+        return
     if args.workload == "proj_4096":
         w = ProjWorkload(dev)
     elif args.workload == "stack70b_multi":
