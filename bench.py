@@ -914,7 +914,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the kernels shard by output rows, see DESIGN.md); run with --gpus 1.",
+              "(the kernels would shard by output rows); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
     if args.summarize_counters:

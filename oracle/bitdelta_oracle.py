@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).  Plain numpy, float64
 for the floating-point products, Python integers for the exact scale.
 
-Readings of the page taken here (each is listed in the design doc as well):
+Readings of the page taken here:
 
 * Delta is formed in float32: both bf16 operands widen exactly, one IEEE
   float32 subtraction with round-to-nearest-even, subnormals kept.

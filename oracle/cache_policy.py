@@ -18,7 +18,7 @@ routing paragraphs:
   loading, further requests for it queue behind that load instead of each
   starting a load of its own.
 
-Readings taken where the page leaves the rule open (listed in the design doc):
+Readings taken where the page leaves the rule open:
 
 * Request rate is an integer request count per variant that is halved
   (shift right by one, all variants at once) after every `halve_every`-th
@@ -139,7 +139,7 @@ class Router:
     Page section "Altyapı ayrıntıları", the routing paragraph: the router
     keeps track of the requests in flight per variant and avoids head-of-line
     blocking; requests for a variant whose delta is loading wait for that one
-    load.  Reading taken (listed in the design doc):
+    load.  Reading taken:
 
     * a request registers with the cache once, the first time a batch is
       formed after it arrived (so the cache counts it once); a FULL refusal
