@@ -913,7 +913,7 @@ def main():
     ap.add_argument("--counter-launches", type=int, default=8)
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the kernels would shard by output rows); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
