@@ -63,6 +63,10 @@ WORKLOADS = {
 }
 
 
+# Smallest u of the Laplace inverse CDF: -1/2 plus one float32 step there.
+U_MIN = -0.5 + 2.0 ** -25
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """uint16 bit patterns of a bf16 tensor, as a host numpy array."""
     if t.dtype != torch.bfloat16:
@@ -90,6 +94,9 @@ def draw_finetuned(w_base: torch.Tensor, b: float, gen: torch.Generator) -> torc
     u = torch.rand(w_base.shape, generator=gen, device=w_base.device,
                    dtype=torch.float32)
     u.sub_(0.5)
+    # rand can return exactly 0: keep u inside (-1/2, 1/2), where the inverse
+    # CDF is finite (the clamped end is a draw of about 16.6 b)
+    u.clamp_(min=U_MIN)
     lap = torch.log1p(u.abs().mul_(-2.0)).mul_(-b).mul_(torch.sign(u))
     del u
     lap.add_(w_base.to(torch.float32))
@@ -183,3 +190,29 @@ def draw_stack_inputs(wl: Workload, m: int, gen: torch.Generator, device) -> lis
     """Per-layer activations (x ~ N(0, 1) for every layer, as the layer
     inputs are drawn for one layer)."""
     return [draw_layer_inputs(wl, m, gen, device) for _ in range(wl.layers)]
+
+
+# ----------------------------------------------------------------- merges
+def draw_gaussian(rows: int, cols: int, gen: torch.Generator, device="cpu") -> torch.Tensor:
+    """float32 [rows, cols] ~ N(0, 1) (the start of an orthogonal iteration)."""
+    return torch.randn(rows, cols, generator=gen, device=device, dtype=torch.float32)
+
+
+def draw_lowrank_checkpoint(w_base: torch.Tensor, rank: int, scale: float, b_noise: float,
+                            gen: torch.Generator) -> torch.Tensor:
+    """A fine-tuned checkpoint whose task vector is a planted rank-`rank`
+    part plus Laplace(0, b_noise) noise: sum_j s_j a_j b_j^T with a_j, b_j
+    ~ N(0, 1) and s_j = scale * (1 - j / (2 rank)) / sqrt(rank), j = 0..rank-1
+    (so its element rms is about `scale` and its singular values stand well
+    above the noise's), drawn in float32 and added to the base, then rounded
+    to bf16.  The draw order is a, b, noise."""
+    d_out, d_in = w_base.shape
+    dev = w_base.device
+    a = torch.randn(d_out, rank, generator=gen, device=dev, dtype=torch.float32)
+    b = torch.randn(d_in, rank, generator=gen, device=dev, dtype=torch.float32)
+    s = torch.tensor([scale * (1.0 - j / (2.0 * rank)) / rank ** 0.5 for j in range(rank)],
+                     device=dev, dtype=torch.float32)
+    u = (torch.rand(d_out, d_in, generator=gen, device=dev, dtype=torch.float32) - 0.5).clamp_(
+        min=U_MIN)
+    noise = -b_noise * torch.sign(u) * torch.log1p(-2.0 * u.abs())
+    return (w_base.float() + (a * s) @ b.T + noise).to(torch.bfloat16)

@@ -42,7 +42,11 @@ def y_error(y_dev: torch.Tensor, y_ref: np.ndarray):
     return float(np.linalg.norm(err)) / nref, float(np.max(np.abs(err))) / rms
 
 
-def assert_y_close(y_dev, y_ref, what=""):
+def assert_y_close(y_dev, y_ref, what="", min_finite=0.5):
+    """Within the tolerance, and the comparison is not vacuous: at least
+    min_finite of the reference values are finite."""
+    frac = float(np.mean(np.isfinite(y_ref)))
+    assert frac >= min_finite, f"{what}: only {frac:.1%} of the reference outputs are finite"
     rel, mx = y_error(y_dev, y_ref)
     assert rel <= REL_FRO_TOL and mx <= MAX_ABS_OVER_RMS_TOL, (
         f"{what}: rel_fro={rel:.3e} (tol {REL_FRO_TOL}), max_abs/rms={mx:.3e} "

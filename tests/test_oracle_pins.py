@@ -474,3 +474,19 @@ def test_reconstruct_rounds_twice_float32_then_bf16():
     # bf16 holds exactly (0x3F7F)
     r = O.reconstruct(wb, O.pack_sign_bits(np.zeros((1, 64), bool)), alpha, 0)
     assert np.all(r == 0x3F7F)
+
+
+def test_laplace_draw_stays_finite():
+    """The Laplace inverse CDF is infinite at u = -1/2, which torch.rand's
+    exact zeros would reach (about one draw in 2^24 on the device): the draw
+    clamps u to one float32 step inside, so no delta is infinite and the
+    largest magnitude is about 16.6 b."""
+    import torch
+    import synthetic as S
+    g = S.generator(123)
+    base = torch.zeros(2048, 4096, dtype=torch.bfloat16)
+    wf = S.draw_finetuned(base, 1.0, g).float()
+    assert torch.isfinite(wf).all()
+    assert wf.abs().max().item() <= 16.7
+    u = torch.tensor([0.0]) - 0.5                      # the value torch.rand's zero gives
+    assert u.clamp(min=S.workloads.U_MIN).item() > -0.5
