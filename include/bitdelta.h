@@ -348,6 +348,46 @@ int bitdelta_router_complete(bitdelta_router* router, int32_t n, const int32_t* 
 /* Requests still queued (submitted, not yet in a batch). */
 int bitdelta_router_pending(bitdelta_router* router, int32_t* n);
 
+/*
+ * MonoSoup merge - k fine-tuned checkpoints of one base merged through
+ * rank-r truncations of their task vectors (section "MonoSoup": each
+ * Delta_i = W_i - W_base is replaced by its rank-r truncated SVD tau_i and
+ * W_merged = W_base + (1/k) sum_i tau_i).
+ *
+ * tau_i = Q_i (Delta_i^T Q_i)^T, where Q_i (orthonormal columns) comes from
+ * orthogonal iteration started at omega: Q = orth(Delta omega), then
+ * power_iters times Q = orth(Delta orth(Delta^T Q)).  This is the rank-r
+ * truncation whenever sigma_r(Delta_i) > sigma_{r+1}(Delta_i), to within
+ * about (sigma_{r+1}/sigma_r)^(2 power_iters + 1) relative; with no gap at r
+ * the result is a rank-r approximation of the top subspace found.  Delta is
+ * formed per element as one float32 subtraction of the bf16 values; sums are
+ * float32 in a fixed order (deterministic).  Directions that vanish (a
+ * Delta of rank below r, e.g. a checkpoint equal to the base) are dropped.
+ *
+ *   w_ft         HOST array of k device pointers, bf16 [d_out, d_in] each
+ *   k            1 .. BITDELTA_MONOSOUP_MAX_CHECKPOINTS
+ *   w_base       device, bf16 [d_out, d_in]
+ *   rank         1 .. min(BITDELTA_MONOSOUP_MAX_RANK, d_out, d_in)
+ *   power_iters  0 .. BITDELTA_MONOSOUP_MAX_POWER_ITERS
+ *   omega        device, float32 [d_in, rank], the caller's Gaussian start
+ *                (the same start is used for every checkpoint)
+ *   w_merged     device, bf16 [d_out, d_in], written: W_base + the mean,
+ *                rounded to nearest even
+ *   tau_mean     device, float32 [d_out, d_in], written, or NULL
+ *   workspace    device, >= bitdelta_monosoup_workspace_size(...) bytes,
+ *                16-byte aligned; contents are scratch
+ * Returns BITDELTA_OK or an error status; nothing is enqueued on error.
+ */
+#define BITDELTA_MONOSOUP_MAX_RANK 32
+#define BITDELTA_MONOSOUP_MAX_CHECKPOINTS 64
+#define BITDELTA_MONOSOUP_MAX_POWER_ITERS 64
+
+size_t bitdelta_monosoup_workspace_size(int64_t d_out, int64_t d_in, int32_t k, int32_t rank);
+int bitdelta_monosoup_merge(const uint16_t* const* w_ft, int32_t k, const uint16_t* w_base,
+                            int64_t d_out, int64_t d_in, int32_t rank, int32_t power_iters,
+                            const float* omega, uint16_t* w_merged, float* tau_mean,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* bitdelta_status_string(int status);
 

@@ -31,7 +31,13 @@ def truncated_svd(d: np.ndarray, rank: int) -> np.ndarray:
     """Best rank-`rank` approximation of a float64 matrix (U_r S_r V_r^T)."""
     if rank <= 0:
         return np.zeros_like(d)
-    u, s, vt = np.linalg.svd(d, full_matrices=False)
+    try:
+        u, s, vt = np.linalg.svd(d, full_matrices=False)
+    except np.linalg.LinAlgError:
+        # LAPACK's divide-and-conquer driver can fail to converge on large
+        # matrices; the QR-iteration driver computes the same decomposition
+        import scipy.linalg
+        u, s, vt = scipy.linalg.svd(d, full_matrices=False, lapack_driver="gesvd")
     r = min(rank, s.size)
     return (u[:, :r] * s[:r]) @ vt[:r]
 

@@ -14,7 +14,10 @@ Recipe (the page models a fine-tuning delta as Laplace(0, b); section
 * W_ft = bf16(float32(W_base) + Delta);
 * x ~ N(0, 1), rounded to bf16;
 * variant ids: truncated Zipf(1.1) over the variants, P(v) ~ (v+1)^-1.1,
-  drawn with numpy's Generator.choice.
+  drawn with numpy's Generator.choice;
+* checkpoints for a merge: a planted rank-r task vector (Gaussian factors,
+  decreasing scales) plus Laplace noise added to the base, rounded to bf16;
+  the orthogonal iteration's start ~ N(0, 1) in float32.
 """
 
 from .workloads import (  # noqa: F401
@@ -25,8 +28,10 @@ from .workloads import (  # noqa: F401
     draw_activations,
     draw_base,
     draw_finetuned,
+    draw_gaussian,
     draw_layer_bases,
     draw_layer_inputs,
+    draw_lowrank_checkpoint,
     draw_stack_bases,
     draw_stack_inputs,
     iter_finetuned,

@@ -27,6 +27,8 @@ from .bitdelta import (  # noqa: F401
     lib,
     linear,
     linear_multi,
+    monosoup_merge,
+    monosoup_workspace_size,
     Router,
     ratio_to_f32_bits,
     reconstruct,

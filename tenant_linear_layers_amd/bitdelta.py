@@ -61,7 +61,13 @@ EXPORTS = (
     "bitdelta_router_next_batch",
     "bitdelta_router_complete",
     "bitdelta_router_pending",
+    "bitdelta_monosoup_workspace_size",
+    "bitdelta_monosoup_merge",
 )
+
+MONOSOUP_MAX_RANK = 32
+MONOSOUP_MAX_CHECKPOINTS = 64
+MONOSOUP_MAX_POWER_ITERS = 64
 
 
 class BitDeltaError(RuntimeError):
@@ -132,6 +138,11 @@ def lib() -> ctypes.CDLL:
     L.bitdelta_router_complete.restype = i32
     L.bitdelta_router_pending.argtypes = [vp, pi32]
     L.bitdelta_router_pending.restype = i32
+    L.bitdelta_monosoup_workspace_size.argtypes = [i64, i64, ctypes.c_int32, ctypes.c_int32]
+    L.bitdelta_monosoup_workspace_size.restype = sz
+    L.bitdelta_monosoup_merge.argtypes = [vp, ctypes.c_int32, vp, i64, i64, ctypes.c_int32,
+                                          ctypes.c_int32, vp, vp, vp, vp, sz, vp]
+    L.bitdelta_monosoup_merge.restype = i32
     _lib = L
     return L
 
@@ -485,3 +496,44 @@ class Router:
         n = ctypes.c_int32()
         _check(lib().bitdelta_router_pending(self._h, ctypes.byref(n)), "bitdelta_router_pending")
         return n.value
+
+
+# ------------------------------------------------------------------ MonoSoup
+def monosoup_workspace_size(d_out: int, d_in: int, k: int, rank: int) -> int:
+    return int(lib().bitdelta_monosoup_workspace_size(d_out, d_in, k, rank))
+
+
+def monosoup_merge(w_fts, w_base: torch.Tensor, rank: int, power_iters: int,
+                   omega: torch.Tensor, want_tau: bool = False, out=None, workspace=None,
+                   stream=None):
+    """(merged bf16 [d_out, d_in], mean of the rank-r truncations float32 or
+    None) for k checkpoints w_fts of the base w_base; omega float32
+    [d_in, rank] is the Gaussian start of the orthogonal iteration."""
+    _need(w_base, "w_base", torch.bfloat16)
+    dev = w_base.device
+    if w_base.dim() != 2:
+        raise ValueError("w_base must be 2-D")
+    d_out, d_in = w_base.shape
+    for w in w_fts:
+        _need(w, "w_ft", torch.bfloat16, dev)
+        if w.shape != w_base.shape:
+            raise ValueError("every checkpoint must have the base's shape")
+    _need(omega, "omega", torch.float32, dev)
+    _size(omega, "omega", d_in * rank)
+    k = len(w_fts)
+    if out is None:
+        out = torch.empty_like(w_base)
+    _need(out, "out", torch.bfloat16, dev)
+    _size(out, "out", d_out * d_in)
+    tau = torch.empty((d_out, d_in), dtype=torch.float32, device=dev) if want_tau else None
+    need = monosoup_workspace_size(d_out, d_in, k, rank)
+    if workspace is None:
+        workspace = torch.empty((max(need, 16),), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    arr = (ctypes.c_void_p * max(k, 1))(*[w.data_ptr() for w in w_fts])
+    with _on(dev):
+        st = lib().bitdelta_monosoup_merge(ctypes.cast(arr, ctypes.c_void_p), k, _ptr(w_base),
+                                           d_out, d_in, rank, power_iters, _ptr(omega), _ptr(out),
+                                           _ptr(tau), _ptr(workspace), ws_bytes, _stream(stream))
+    _check(st, "bitdelta_monosoup_merge")
+    return out, tau

@@ -227,3 +227,51 @@ BD_EXPORT int bitdelta_reconstruct(const uint16_t* w_base, const uint64_t* packe
                                           alpha_mode == BITDELTA_ALPHA_PER_ROW, (int)d_out,
                                           (int)d_in, w_eff, static_cast<hipStream_t>(stream)));
 }
+
+BD_EXPORT size_t bitdelta_monosoup_workspace_size(int64_t d_out, int64_t d_in, int32_t k,
+                                                  int32_t rank) {
+  if (!shape_ok(d_out, d_in) || k < 1 || k > BITDELTA_MONOSOUP_MAX_CHECKPOINTS || rank < 1 ||
+      rank > BITDELTA_MONOSOUP_MAX_RANK || rank > d_out || rank > d_in)
+    return 0;
+  return bd::monosoup_workspace_bytes(d_out, d_in, k, rank);
+}
+
+BD_EXPORT int bitdelta_monosoup_merge(const uint16_t* const* w_ft, int32_t k,
+                                      const uint16_t* w_base, int64_t d_out, int64_t d_in,
+                                      int32_t rank, int32_t power_iters, const float* omega,
+                                      uint16_t* w_merged, float* tau_mean, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if (!w_ft || !w_base || !omega || !w_merged || !workspace) return BITDELTA_ERR_NULL;
+  if (!shape_ok(d_out, d_in) || k < 1 || k > BITDELTA_MONOSOUP_MAX_CHECKPOINTS || rank < 1 ||
+      rank > BITDELTA_MONOSOUP_MAX_RANK || rank > d_out || rank > d_in || power_iters < 0 ||
+      power_iters > BITDELTA_MONOSOUP_MAX_POWER_ITERS || d_out * d_in >= kMaxElems / 4)
+    return BITDELTA_ERR_SHAPE;
+  for (int i = 0; i < k; ++i)
+    if (!w_ft[i]) return BITDELTA_ERR_NULL;
+  for (int i = 0; i < k; ++i)
+    if (!aligned16(w_ft[i])) return BITDELTA_ERR_ALIGN;
+  if (!aligned16(w_base) || !aligned16(w_merged) || !aligned16(workspace) ||
+      (tau_mean && !aligned16(tau_mean)) || (reinterpret_cast<uintptr_t>(omega) & 3u))
+    return BITDELTA_ERR_ALIGN;
+  const size_t need = bd::monosoup_workspace_bytes(d_out, d_in, k, rank);
+  if (workspace_bytes < need) return BITDELTA_ERR_WORKSPACE;
+  const size_t wbytes = (size_t)d_out * (size_t)d_in * 2u;
+  const size_t tbytes = wbytes * 2u;
+  const size_t obytes = (size_t)d_in * (size_t)rank * 4u;
+  const void* outs[3] = {w_merged, tau_mean, workspace};
+  const size_t outn[3] = {wbytes, tbytes, need};
+  for (int a = 0; a < 3; ++a) {
+    if (!outs[a]) continue;
+    if (overlap(outs[a], outn[a], w_base, wbytes) || overlap(outs[a], outn[a], omega, obytes))
+      return BITDELTA_ERR_OVERLAP;
+    for (int i = 0; i < k; ++i)
+      if (overlap(outs[a], outn[a], w_ft[i], wbytes)) return BITDELTA_ERR_OVERLAP;
+    for (int b = a + 1; b < 3; ++b)
+      if (outs[b] && overlap(outs[a], outn[a], outs[b], outn[b])) return BITDELTA_ERR_OVERLAP;
+  }
+  const int dev = check_device();
+  if (dev != BITDELTA_OK) return dev;
+  return status_of(bd::launch_monosoup(w_ft, k, w_base, (int)d_out, (int)d_in, rank, power_iters,
+                                       omega, w_merged, tau_mean, workspace,
+                                       static_cast<hipStream_t>(stream)));
+}

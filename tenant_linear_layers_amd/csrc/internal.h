@@ -46,4 +46,13 @@ hipError_t launch_reconstruct(const uint16_t* w, const uint8_t* packed_bytes, co
                               int per_row, int d_out, int d_in, uint16_t* out,
                               hipStream_t stream);
 
+// MonoSoup merge (rank-r truncations by orthogonal iteration, the mean
+// added to the base).  The working width is the rank rounded up to 8, 16 or
+// 32; the workspace holds the per-checkpoint bases and partial sums.
+int monosoup_width(int rank);
+size_t monosoup_workspace_bytes(int64_t d_out, int64_t d_in, int k, int rank);
+hipError_t launch_monosoup(const uint16_t* const* w_ft, int k, const uint16_t* w_base, int d_out,
+                           int d_in, int rank, int power_iters, const float* omega, uint16_t* out,
+                           float* tau, void* workspace, hipStream_t stream);
+
 }  // namespace bd

@@ -136,3 +136,29 @@ def test_reconstruct_argument_errors():
     assert _c(f(A, C, D, 1, 8, 64, A + 16, None)) == 9     # w_eff overlaps w_base
     assert _c(f(A, C, D, 1, 8, 64, C, None)) == 9          # ... the packed signs
     assert _c(f(A, C, E + 4, 1, 8, 64, E, None)) == 9      # ... per-row alpha
+
+
+def test_monosoup_argument_checks():
+    """bitdelta_monosoup_merge rejects bad arguments before any HIP call
+    (the addresses are never dereferenced)."""
+    L = T.lib()
+    arr = (ctypes.c_void_p * 2)(A, B)
+    cast = lambda a: ctypes.cast(a, ctypes.c_void_p)  # noqa: E731
+    ws = T.monosoup_workspace_size(256, 512, 2, 8)
+    assert ws > 0
+    assert T.monosoup_workspace_size(256, 512, 2, 33) == 0
+    assert T.monosoup_workspace_size(256, 100, 2, 8) == 0
+
+    def call(k=2, rank=8, q=3, d_out=256, d_in=512, omega=C, out=D, tau=None, wsp=E, wsb=ws,
+             w=arr):
+        return L.bitdelta_monosoup_merge(cast(w), k, ctypes.c_void_p(0x600000), d_out, d_in,
+                                         rank, q, ctypes.c_void_p(omega), ctypes.c_void_p(out),
+                                         ctypes.c_void_p(tau), ctypes.c_void_p(wsp), wsb, None)
+    assert call(rank=0) == 2 and call(rank=33) == 2 and call(k=0) == 2 and call(k=65) == 2
+    assert call(q=-1) == 2 and call(q=65) == 2 and call(d_in=100) == 2 and call(d_out=4, rank=8) == 2
+    assert call(omega=0) == 1 and call(out=0) == 1 and call(wsp=0) == 1
+    assert call(out=D + 8) == 3 and call(omega=C + 2) == 3
+    assert call(wsb=ws - 1) == 6
+    assert call(out=B) == 9                               # output over a checkpoint
+    nul = (ctypes.c_void_p * 2)(A, None)
+    assert call(w=nul) == 1

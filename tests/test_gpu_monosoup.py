@@ -1,0 +1,93 @@
+"""GPU parity of the MonoSoup merge (bitdelta_monosoup_merge) against the
+oracle's exact truncated SVDs, on checkpoints whose task vectors have a
+planted spectral gap at the rank (where the truncation is unique and the
+orthogonal iteration converges to it).
+
+Bars: the float32 mean of the truncations within 1e-4 relative Frobenius
+error of the float64 one and every element within 1e-3 of its rms (float32
+sums over at most a few thousand terms stay near 1e-5 relative); each merged
+bf16 weight within one bf16 unit of the exact value plus that element's error
+in the mean (near zero a bf16 unit is smaller than the float32 error), and
+at most 1% of them different from the oracle's rounding."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.monosoup as M
+import synthetic as S
+import tenant_linear_layers_amd as T
+from helpers import bits16
+from oracle.bitdelta_oracle import bf16_bits_to_f32
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    T.lib()
+
+
+def checkpoints(d_out, d_in, k, rank, seed, scale=2e-3, b_noise=2e-4):
+    g = S.generator(seed, DEV)
+    wb = S.draw_base(d_out, d_in, 0.02, g, DEV)
+    wf = [S.draw_lowrank_checkpoint(wb, rank, scale, b_noise, g) for _ in range(k)]
+    omega = S.draw_gaussian(d_in, rank, g, DEV)
+    return wb, wf, omega
+
+
+def check(wb, wf, omega, rank, q, rows=None):
+    merged, tau = T.monosoup_merge(wf, wb, rank, q, omega, want_tau=True)
+    torch.cuda.synchronize()
+    m_ref, t_ref = M.merge([bits16(w) for w in wf], bits16(wb), rank)
+    t = tau.cpu().numpy().astype(np.float64)
+    rel = np.linalg.norm(t - t_ref) / max(np.linalg.norm(t_ref), 1e-300)
+    assert rel <= 1e-4, f"tau_mean rel_fro {rel:.2e}"
+    rms = np.sqrt(np.mean(t_ref * t_ref))
+    terr = np.abs(t - t_ref)
+    assert terr.max() <= 1e-3 * rms, f"tau_mean max error {terr.max() / rms:.2e} of rms"
+    exact = bf16_bits_to_f32(bits16(wb)).astype(np.float64) + t_ref
+    got = bf16_bits_to_f32(bits16(merged)).astype(np.float64)
+    _, e = np.frexp(exact)
+    unit = np.ldexp(1.0, e - 8)           # one bf16 unit at the exact value
+    assert np.all(np.abs(got - exact) <= unit + terr), "merged weight off by more than a unit"
+    assert np.mean(bits16(merged) != m_ref) <= 0.01
+    return merged, tau
+
+
+@pytest.mark.parametrize("shape,k,rank", [((256, 512), 3, 8), ((320, 192), 2, 5),
+                                          ((12, 640), 2, 4), ((200, 320), 4, 16),
+                                          ((512, 256), 2, 32)])
+def test_monosoup_matches_exact_truncation(shape, k, rank):
+    wb, wf, omega = checkpoints(*shape, k, rank, seed=shape[0] + 7 * rank)
+    check(wb, wf, omega, rank, 4)
+
+
+def test_monosoup_checkpoint_equal_to_base():
+    """A task vector of zero has no directions: its truncation is zero, and a
+    merge of the base with itself returns the base bit for bit."""
+    wb, wf, omega = checkpoints(128, 256, 1, 8, seed=11)
+    merged, tau = T.monosoup_merge([wb.clone()], wb, 8, 3, omega, want_tau=True)
+    torch.cuda.synchronize()
+    assert torch.equal(merged.view(torch.int16), wb.view(torch.int16))
+    assert not tau.any()
+    check(wb, [wb.clone(), wf[0]], omega, 8, 4)
+
+
+def test_monosoup_is_deterministic():
+    wb, wf, omega = checkpoints(256, 512, 2, 8, seed=13)
+    a, ta = T.monosoup_merge(wf, wb, 8, 3, omega, want_tau=True)
+    b, tb = T.monosoup_merge(wf, wb, 8, 3, omega, want_tau=True)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16)) and torch.equal(ta, tb)
+
+
+def test_monosoup_4096_as_benchmarked():
+    """The benchmark's configuration at full size (4096 x 4096, rank 16, four
+    power iterations), with two of its four checkpoints (the oracle's two
+    4096 x 4096 SVDs take seconds on the host)."""
+    wb, wf, omega = checkpoints(4096, 4096, 2, 16, seed=17)
+    check(wb, wf, omega, 16, 4)
