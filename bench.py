@@ -656,6 +656,56 @@ def serve_layer70b(args, dev):
     print(json.dumps(out), flush=True)
 
 
+def monosoup_4096(args, dev):
+    """MonoSoup merge of 4 fine-tuned checkpoints of a 4096x4096 matrix at
+    rank 16 with 4 power iterations (task vectors with a planted rank-16
+    part plus Laplace noise).  The merge is captured in a HIP graph and timed
+    with HIP events.  Algorithmic bytes per merge: each checkpoint's task
+    vector is streamed from its two bf16 matrices (4 bytes per element) once
+    per product, 2 * (power_iters + 1) products, and the merge reads the base
+    and writes the merged weights (4 bytes per element)."""
+    d, k, rank, q = 4096, 4, 16, 4
+    g = S.generator(31, dev)
+    wb = S.draw_base(d, d, 0.02, g, dev)
+    wf = [S.draw_lowrank_checkpoint(wb, rank, 2e-3, 2e-4, g) for _ in range(k)]
+    omega = S.draw_gaussian(d, rank, g, dev)
+    out = torch.empty_like(wb)
+    ws = torch.empty(T.monosoup_workspace_size(d, d, k, rank), dtype=torch.uint8, device=dev)
+    T.monosoup_merge(wf, wb, rank, q, omega, out=out, workspace=ws)
+    ref = out.clone()
+    graph = capture(lambda: T.monosoup_merge(wf, wb, rank, q, omega, out=out, workspace=ws))
+    for _ in range(args.warmup):
+        graph.replay()
+    ms = time_replays(graph, max(3, args.steps))
+    if not torch.equal(out.view(torch.int16), ref.view(torch.int16)):
+        raise RuntimeError("graph replays of the merge differ from the eager call")
+    nbytes = k * 2 * (q + 1) * 4 * d * d + 4 * d * d
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    cpu = None
+    if args.cpu_budget > 0:
+        import oracle.monosoup as M
+        t0 = time.perf_counter()
+        M.merge([S.bf16_bits(w) for w in wf[:1]], S.bf16_bits(wb), rank)
+        t1 = time.perf_counter() - t0
+        cpu = {"value": round(nbytes / k / t1 / 1e9, 3), "unit": "GB/s", "cores":
+               len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"oracle merge of one of the {k} checkpoints (exact float64 SVD of the "
+                         f"4096x4096 task vector), {t1:.1f} s; value is that merge's share of "
+                         f"the bytes over its time"}
+    out_line = {"metric": "monosoup merge effective HBM GB/s, 1 GPU", "value": round(gbs, 2),
+                "unit": "GB/s", "n_gpus": 1, "steps": max(3, args.steps), "warmup": args.warmup,
+                "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+                "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+                "config": {"workload": "monosoup_4096: 4 checkpoints of a 4096x4096 matrix, "
+                                       "rank 16, 4 power iterations, planted rank-16 task "
+                                       "vectors plus Laplace(0, 2e-4) noise",
+                           "d_out": d, "d_in": d, "checkpoints": k, "rank": rank,
+                           "power_iters": q, "bytes_per_merge": nbytes},
+                "roofline": roofline_entry("hbm", gbs, HBM_PEAK_GBS, "GB/s", None),
+                "cpu_baseline": cpu}
+    print(json.dumps(out_line), flush=True)
+
+
 # ------------------------------------------------------------------ CPU oracle
 def cpu_baseline(w: ProjWorkload, budget_s: float):
     """The oracle, as it stands, on a bounded sample of the same workload:
@@ -903,7 +953,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="proj_4096",
                     choices=["proj_4096", "layer70b_prefill", "layer70b_multi",
-                             "layer70b_decode", "stack70b_multi", "serve_layer70b"])
+                             "layer70b_decode", "stack70b_multi", "serve_layer70b",
+                             "monosoup_4096"])
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
     ap.add_argument("--counter-pass", action="store_true",
@@ -932,6 +983,9 @@ def main():
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     if args.workload == "serve_layer70b":
         serve_layer70b(args, dev)
+        return
+    if args.workload == "monosoup_4096":
+        monosoup_4096(args, dev)
         return
     if args.workload == "proj_4096":
         w = ProjWorkload(dev)

@@ -23,9 +23,10 @@
 // Kernels: mul (Y = Delta X: four rows per wave, lanes across d_in, a
 // butterfly sum per output), tmul (partial Z = Delta^T Y over row chunks,
 // lanes across d_in) and its fixed-order reduction, gram (partial A^T A over
-// row chunks), chol (sum of the partials, Cholesky with dropped pivots and
-// the triangular inverse, one workgroup), scale (A <- A R^-1, one row per
-// thread), merge (W_base + mean of Q_i Z_i^T, rounded to bf16, LDS tiles).
+// row chunks), chol (sum of the partials and the Cholesky factor with
+// dropped pivots, one workgroup), scale (A <- A U^-1 by substitution, one row
+// per thread), merge (W_base + mean of Q_i Z_i^T, rounded to bf16, LDS
+// tiles).
 #include "common.h"
 #include "internal.h"
 
@@ -33,7 +34,7 @@ namespace bd {
 namespace {
 
 constexpr int kTmulChunks = 64;   // row chunks of the Delta^T Y partials
-constexpr int kGramChunks = 256;  // row chunks of the Gram partials
+constexpr int kGramChunks = 64;   // row chunks of the Gram partials
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -122,6 +123,7 @@ __global__ __launch_bounds__(64) void ms_tmul_kernel(const uint16_t* __restrict_
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int j = 0; j < R; ++j) acc[h][j] = 0.f;
+#pragma unroll 4
   for (int o = r0; o < r1; ++o) {
     const size_t base = (size_t)o * d_in + cc;
     const uint32_t a = ld32(wf + base);
@@ -153,6 +155,7 @@ __global__ __launch_bounds__(256) void ms_reduce_kernel(const float* __restrict_
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float s = 0.f;
+#pragma unroll 16
   for (int p = 0; p < kTmulChunks; ++p) s += Zp[(int64_t)p * n + i];
   Z[i] = s;
 }
@@ -168,81 +171,69 @@ __global__ __launch_bounds__(R * R) void ms_gram_kernel(const float* __restrict_
   const int r0 = p * rows;
   const int r1 = min(r0 + rows, n);
   float s = 0.f;
+#pragma unroll 8
   for (int o = r0; o < r1; ++o) s += A[(size_t)o * R + a] * A[(size_t)o * R + b];
   Gp[((size_t)p * R + a) * R + b] = s;
 }
 
-// G = sum_p Gp[p] (chunk order); upper Cholesky factor U (G = U^T U) with
-// pivots at or below 1e-6 of the largest diagonal dropped (their rows of U and
-// their rows and columns of the inverse are zero); Rinv = U^-1 on the kept
-// indices.
+// G = sum_p Gp[p] (chunk order) and its upper Cholesky factor U (G = U^T U),
+// written to Uf [R][R].  Thread (a, b) keeps G[a][b] (b >= a) in a register
+// and the factorisation runs one pivot per step: the step's row of U from the
+// updated row of G, then the trailing update.  A pivot at or below 1e-6 of
+// the largest diagonal of G is dropped: its row of U is zero, its diagonal
+// 0 marks it for the substitution.
 template <int R>
 __global__ __launch_bounds__(R * R) void ms_chol_kernel(const float* __restrict__ Gp,
-                                                        float* __restrict__ Rinv) {
-  __shared__ float G[R][R];
+                                                        float* __restrict__ Uf) {
   __shared__ float U[R][R];
-  __shared__ float V[R][R];
-  __shared__ int keep[R];
+  __shared__ float diag[R];
+  __shared__ float piv;
   const int a = threadIdx.x / R;
   const int b = threadIdx.x % R;
-  float s = 0.f;
-  for (int p = 0; p < kGramChunks; ++p) s += Gp[((size_t)p * R + a) * R + b];
-  G[a][b] = s;
+  float g = 0.f;
+#pragma unroll
+  for (int p = 0; p < kGramChunks; ++p) g += Gp[((size_t)p * R + a) * R + b];
   U[a][b] = 0.f;
-  V[a][b] = 0.f;
+  if (a == b) diag[a] = g;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float gmax = 0.f;
-    for (int k = 0; k < R; ++k) gmax = fmaxf(gmax, G[k][k]);
-    const float thr = 1e-6f * gmax;
-    for (int k = 0; k < R; ++k) {
-      float dkk = G[k][k];
-      for (int m = 0; m < k; ++m) dkk -= U[m][k] * U[m][k];
-      keep[k] = (gmax > 0.f && dkk > thr) ? 1 : 0;
-      if (!keep[k]) continue;
-      const float ukk = sqrtf(dkk);
-      U[k][k] = ukk;
-      for (int j = k + 1; j < R; ++j) {
-        float v = G[k][j];
-        for (int m = 0; m < k; ++m) v -= U[m][k] * U[m][j];
-        U[k][j] = v / ukk;
-      }
-    }
-    // inverse of the upper triangle on the kept indices, column by column
-    for (int j = 0; j < R; ++j) {
-      if (!keep[j]) continue;
-      V[j][j] = 1.f / U[j][j];
-      for (int i = j - 1; i >= 0; --i) {
-        if (!keep[i]) continue;
-        float v = 0.f;
-        for (int m = i + 1; m <= j; ++m) v += U[i][m] * V[m][j];
-        V[i][j] = -v / U[i][i];
-      }
-    }
+  float gmax = 0.f;
+  for (int k = 0; k < R; ++k) gmax = fmaxf(gmax, diag[k]);
+  const float thr = 1e-6f * gmax;
+  for (int k = 0; k < R; ++k) {
+    if (a == k && b == k) piv = g;
+    __syncthreads();
+    const float pk = piv;
+    const bool keep = gmax > 0.f && pk > thr;
+    if (a == k && b >= k) U[k][b] = keep ? g / sqrtf(pk) : 0.f;
+    __syncthreads();
+    if (a > k && b >= a) g -= U[k][a] * U[k][b];
   }
-  __syncthreads();
-  Rinv[a * R + b] = V[a][b];
+  Uf[a * R + b] = U[a][b];
 }
 
-// A[row][:] <- A[row][:] Rinv; one row per thread.
+// A[row][:] <- A[row][:] U^-1 on the kept indices, by forward substitution
+// (z U = x, z_j = 0 where U[j][j] = 0); one row per thread.
 template <int R>
 __global__ __launch_bounds__(256) void ms_scale_kernel(float* __restrict__ A, int n,
-                                                       const float* __restrict__ Rinv) {
+                                                       const float* __restrict__ Uf) {
   __shared__ float M[R * R];
-  for (int t = threadIdx.x; t < R * R; t += 256) M[t] = Rinv[t];
+  for (int t = threadIdx.x; t < R * R; t += 256) M[t] = Uf[t];
   __syncthreads();
   const int row = blockIdx.x * 256 + threadIdx.x;
   if (row >= n) return;
-  float x[R];
+  float z[R];
 #pragma unroll
-  for (int j = 0; j < R; ++j) x[j] = A[(size_t)row * R + j];
+  for (int j = 0; j < R; ++j) z[j] = A[(size_t)row * R + j];
 #pragma unroll
   for (int j = 0; j < R; ++j) {
-    float v = 0.f;
+    float v = z[j];
 #pragma unroll
-    for (int m = 0; m < R; ++m) v += x[m] * M[m * R + j];
-    A[(size_t)row * R + j] = v;
+    for (int m = 0; m < j; ++m) v -= z[m] * M[m * R + j];
+    const float ujj = M[j * R + j];
+    z[j] = ujj > 0.f ? v / ujj : 0.f;
   }
+#pragma unroll
+  for (int j = 0; j < R; ++j) A[(size_t)row * R + j] = z[j];
 }
 
 // Omega [d_in][rank] into X [d_in][R], zero columns past the rank.
@@ -319,14 +310,14 @@ __global__ __launch_bounds__(256) void ms_merge_kernel(const uint16_t* __restric
 template <int R>
 struct Plan {
   int d_out, d_in, k;
-  float *Y, *Z, *X0, *Zp, *Gp, *Rinv;
+  float *Y, *Z, *X0, *Zp, *Gp, *Uf;
   hipStream_t s;
 
   hipError_t orth(float* A, int n) const {
     for (int pass = 0; pass < 2; ++pass) {
       hipLaunchKernelGGL(ms_gram_kernel<R>, dim3(kGramChunks), dim3(R * R), 0, s, A, n, Gp);
-      hipLaunchKernelGGL(ms_chol_kernel<R>, dim3(1), dim3(R * R), 0, s, Gp, Rinv);
-      hipLaunchKernelGGL(ms_scale_kernel<R>, dim3((n + 255) / 256), dim3(256), 0, s, A, n, Rinv);
+      hipLaunchKernelGGL(ms_chol_kernel<R>, dim3(1), dim3(R * R), 0, s, Gp, Uf);
+      hipLaunchKernelGGL(ms_scale_kernel<R>, dim3((n + 255) / 256), dim3(256), 0, s, A, n, Uf);
     }
     return hipGetLastError();
   }
@@ -361,7 +352,7 @@ hipError_t run_monosoup(const uint16_t* const* w_ft, int k, const uint16_t* w_ba
   P.X0 = P.Z + nZ;
   P.Zp = P.X0 + (size_t)d_in * R;
   P.Gp = P.Zp + (size_t)kTmulChunks * d_in * R;
-  P.Rinv = P.Gp + (size_t)kGramChunks * R * R;
+  P.Uf = P.Gp + (size_t)kGramChunks * R * R;
   hipLaunchKernelGGL(ms_pad_kernel, dim3((unsigned)(((size_t)d_in * R + 255) / 256)), dim3(256), 0,
                      s, omega, d_in, rank, R, P.X0);
   hipError_t e = hipGetLastError();
