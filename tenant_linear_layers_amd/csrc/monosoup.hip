@@ -20,7 +20,7 @@
 // rounded up to 8, 16 or 32; columns past the rank start as zeros and stay
 // zero (their Cholesky pivots are dropped).
 //
-// Kernels: mul (Y = Delta X: four rows per wave, lanes across d_in, a
+// Kernels: mul (Y = Delta X: 8 rows per wave (4 at width 32), lanes across d_in, a
 // butterfly sum per output), tmul (partial Z = Delta^T Y over row chunks,
 // lanes across d_in) and its fixed-order reduction, gram (partial A^T A over
 // row chunks), chol (sum of the partials and the Cholesky factor with
@@ -48,23 +48,24 @@ __device__ __forceinline__ void delta8(const u32x4& a, const u32x4& b, float (&d
   }
 }
 
-// Y[o][j] = sum_c Delta[o][c] X[c][j]; X [d_in][R], Y [d_out][R].
-template <int R>
-__global__ __launch_bounds__(256) void ms_mul_kernel(const uint16_t* __restrict__ wf,
-                                                     const uint16_t* __restrict__ wb, int d_out,
-                                                     int d_in, const float* __restrict__ X,
-                                                     float* __restrict__ Y) {
+// Y[o][j] = sum_c Delta[o][c] X[c][j]; X [d_in][R], Y [d_out][R].  A wave
+// owns RW rows, which share every read of X; one wave per workgroup.
+template <int R, int RW>
+__global__ __launch_bounds__(64) void ms_mul_kernel(const uint16_t* __restrict__ wf,
+                                                    const uint16_t* __restrict__ wb, int d_out,
+                                                    int d_in, const float* __restrict__ X,
+                                                    float* __restrict__ Y) {
   const int lane = threadIdx.x & 63;
-  const int o0 = blockIdx.x * 16 + (threadIdx.x >> 6) * 4;
-  float acc[4][R];
+  const int o0 = blockIdx.x * RW;
+  float acc[RW][R];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RW; ++i)
 #pragma unroll
     for (int j = 0; j < R; ++j) acc[i][j] = 0.f;
   for (int c0 = lane * 8; c0 < d_in; c0 += 512) {
-    float d[4][8];
+    float d[RW][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < RW; ++i) {
       const size_t base = (size_t)min(o0 + i, d_out - 1) * d_in + c0;
       delta8(ld128(wf + base), ld128(wb + base), d[i]);
     }
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256) void ms_mul_kernel(const uint16_t* __restrict_
       for (int j4 = 0; j4 < R / 4; ++j4) {
         const float4 x = *reinterpret_cast<const float4*>(xr + 4 * j4);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < RW; ++i) {
           acc[i][4 * j4] += d[i][e] * x.x;
           acc[i][4 * j4 + 1] += d[i][e] * x.y;
           acc[i][4 * j4 + 2] += d[i][e] * x.z;
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(256) void ms_mul_kernel(const uint16_t* __restrict_
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < RW; ++i)
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       float v = acc[i][j];
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(256) void ms_mul_kernel(const uint16_t* __restrict_
     }
   if (lane == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < RW; ++i) {
       if (o0 + i >= d_out) continue;
 #pragma unroll
       for (int j = 0; j < R; ++j) Y[(size_t)(o0 + i) * R + j] = acc[i][j];
@@ -322,8 +323,9 @@ struct Plan {
     return hipGetLastError();
   }
   hipError_t mul(const uint16_t* wf, const uint16_t* wb, const float* X, float* Yo) const {
-    hipLaunchKernelGGL(ms_mul_kernel<R>, dim3((d_out + 15) / 16), dim3(256), 0, s, wf, wb, d_out,
-                       d_in, X, Yo);
+    constexpr int RW = R <= 16 ? 8 : 4;
+    hipLaunchKernelGGL((ms_mul_kernel<R, RW>), dim3((d_out + RW - 1) / RW), dim3(64), 0, s, wf, wb,
+                       d_out, d_in, X, Yo);
     return hipGetLastError();
   }
   hipError_t tmul(const uint16_t* wf, const uint16_t* wb, const float* Yi, float* Zo) const {
