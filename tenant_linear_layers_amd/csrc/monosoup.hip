@@ -9,7 +9,8 @@
 // tau_i = Q_i Q_i^T Delta_i for Q_i with orthonormal columns spanning that
 // subspace.  Q_i comes from orthogonal (subspace) iteration started from a
 // caller-drawn Gaussian Omega [d_in, r]: Y = Delta Omega, then q times
-// Y <- Delta (Delta^T Y), each product re-orthonormalised (CholeskyQR, twice).
+// Y <- Delta (Delta^T Y), each product re-orthonormalised (CholeskyQR; twice
+// for the final basis).
 // It converges to the top-r subspace when sigma_r > sigma_{r+1}, with error
 // falling like (sigma_{r+1} / sigma_r)^(2q+1); then Z_i = Delta_i^T Q_i and
 // tau_i = Q_i Z_i^T.  No small SVD is needed.
@@ -314,8 +315,10 @@ struct Plan {
   float *Y, *Z, *X0, *Zp, *Gp, *Uf;
   hipStream_t s;
 
-  hipError_t orth(float* A, int n) const {
-    for (int pass = 0; pass < 2; ++pass) {
+  // passes = 2 (CholeskyQR2) for the final basis; inside the iteration one
+  // pass is enough, since every step re-orthonormalises what it multiplies.
+  hipError_t orth(float* A, int n, int passes) const {
+    for (int pass = 0; pass < passes; ++pass) {
       hipLaunchKernelGGL(ms_gram_kernel<R>, dim3(kGramChunks), dim3(R * R), 0, s, A, n, Gp);
       hipLaunchKernelGGL(ms_chol_kernel<R>, dim3(1), dim3(R * R), 0, s, Gp, Uf);
       hipLaunchKernelGGL(ms_scale_kernel<R>, dim3((n + 255) / 256), dim3(256), 0, s, A, n, Uf);
@@ -362,12 +365,12 @@ hipError_t run_monosoup(const uint16_t* const* w_ft, int k, const uint16_t* w_ba
     float* Yi = P.Y + (size_t)i * d_out * R;
     float* Zi = P.Z + (size_t)i * d_in * R;
     e = P.mul(w_ft[i], w_base, P.X0, Yi);
-    if (e == hipSuccess) e = P.orth(Yi, d_out);
+    if (e == hipSuccess) e = P.orth(Yi, d_out, q == 0 ? 2 : 1);
     for (int it = 0; it < q && e == hipSuccess; ++it) {
       e = P.tmul(w_ft[i], w_base, Yi, Zi);
-      if (e == hipSuccess) e = P.orth(Zi, d_in);
+      if (e == hipSuccess) e = P.orth(Zi, d_in, 1);
       if (e == hipSuccess) e = P.mul(w_ft[i], w_base, Zi, Yi);
-      if (e == hipSuccess) e = P.orth(Yi, d_out);
+      if (e == hipSuccess) e = P.orth(Yi, d_out, it == q - 1 ? 2 : 1);
     }
     if (e == hipSuccess) e = P.tmul(w_ft[i], w_base, Yi, Zi);
   }
