@@ -15,6 +15,9 @@ namespace {
 
 constexpr int64_t kInt32Max = 2147483647;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
+// The MonoSoup merge kernel's grid takes 16 rows per workgroup in its y
+// dimension (at most 65535 workgroups).
+constexpr int64_t kMonosoupMaxRows = 65535 * 16;
 
 bool shape_ok(int64_t d_out, int64_t d_in) {
   return d_out >= 1 && d_in >= 64 && d_in % 64 == 0 && d_out <= kInt32Max && d_in <= kInt32Max &&
@@ -231,7 +234,8 @@ BD_EXPORT int bitdelta_reconstruct(const uint16_t* w_base, const uint64_t* packe
 BD_EXPORT size_t bitdelta_monosoup_workspace_size(int64_t d_out, int64_t d_in, int32_t k,
                                                   int32_t rank) {
   if (!shape_ok(d_out, d_in) || k < 1 || k > BITDELTA_MONOSOUP_MAX_CHECKPOINTS || rank < 1 ||
-      rank > BITDELTA_MONOSOUP_MAX_RANK || rank > d_out || rank > d_in)
+      rank > BITDELTA_MONOSOUP_MAX_RANK || rank > d_out || rank > d_in ||
+      d_out > kMonosoupMaxRows)
     return 0;
   return bd::monosoup_workspace_bytes(d_out, d_in, k, rank);
 }
@@ -244,7 +248,8 @@ BD_EXPORT int bitdelta_monosoup_merge(const uint16_t* const* w_ft, int32_t k,
   if (!w_ft || !w_base || !omega || !w_merged || !workspace) return BITDELTA_ERR_NULL;
   if (!shape_ok(d_out, d_in) || k < 1 || k > BITDELTA_MONOSOUP_MAX_CHECKPOINTS || rank < 1 ||
       rank > BITDELTA_MONOSOUP_MAX_RANK || rank > d_out || rank > d_in || power_iters < 0 ||
-      power_iters > BITDELTA_MONOSOUP_MAX_POWER_ITERS || d_out * d_in >= kMaxElems / 4)
+      power_iters > BITDELTA_MONOSOUP_MAX_POWER_ITERS || d_out * d_in >= kMaxElems / 4 ||
+      d_out > kMonosoupMaxRows)
     return BITDELTA_ERR_SHAPE;
   for (int i = 0; i < k; ++i)
     if (!w_ft[i]) return BITDELTA_ERR_NULL;
