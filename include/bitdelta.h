@@ -358,7 +358,8 @@ int bitdelta_router_pending(bitdelta_router* router, int32_t* n);
  * orthogonal iteration started at omega: Q = orth(Delta omega), then
  * power_iters times Q = orth(Delta orth(Delta^T Q)).  This is the rank-r
  * truncation whenever sigma_r(Delta_i) > sigma_{r+1}(Delta_i), to within
- * about (sigma_{r+1}/sigma_r)^(2 power_iters + 1) relative; with no gap at r
+ * about (sigma_{r+1}/sigma_r)^(2 power_iters + 1) relative times a factor
+ * from the random start that grows like sqrt(r (d_out - r)); with no gap at r
  * the result is a rank-r approximation of the top subspace found.  Delta is
  * formed per element as one float32 subtraction of the bf16 values; sums are
  * float32 in a fixed order (deterministic).  Directions that vanish (a

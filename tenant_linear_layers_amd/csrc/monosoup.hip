@@ -12,7 +12,8 @@
 // Y <- Delta (Delta^T Y), each product re-orthonormalised (CholeskyQR; twice
 // for the final basis).
 // It converges to the top-r subspace when sigma_r > sigma_{r+1}, with error
-// falling like (sigma_{r+1} / sigma_r)^(2q+1); then Z_i = Delta_i^T Q_i and
+// falling like (sigma_{r+1} / sigma_r)^(2q+1) times a factor from the random
+// start (growing like sqrt(r (d_out - r))); then Z_i = Delta_i^T Q_i and
 // tau_i = Q_i Z_i^T.  No small SVD is needed.
 //
 // Every product streams Delta straight from the two bf16 matrices (one

@@ -67,6 +67,17 @@ def test_monosoup_matches_exact_truncation(shape, k, rank):
     check(wb, wf, omega, rank, 4)
 
 
+@pytest.mark.parametrize("rank,q", [(20, 4), (1, 2), (12, 6)])
+def test_monosoup_ranks_and_iterations(rank, q):
+    """Ranks off the working widths (20 at width 32, 1 and 12 padded with
+    zero columns) and other iteration counts.  The iteration's error falls
+    like (sigma_{r+1}/sigma_r)^(2q+1) times a factor from the random start
+    that grows like sqrt(r (n - r)): with the planted gap (about 9-11x) four
+    iterations meet the bar at rank 20 (two gave 2.3e-4), two at rank 1."""
+    wb, wf, omega = checkpoints(384, 640, 2, rank, seed=100 + rank)
+    check(wb, wf, omega, rank, q)
+
+
 def test_monosoup_checkpoint_equal_to_base():
     """A task vector of zero has no directions: its truncation is zero, and a
     merge of the base with itself returns the base bit for bit."""
