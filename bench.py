@@ -758,6 +758,27 @@ BLOCK_KERNEL = {"compress": "compress_rows_kernel", "decode_m1": "linear_decode_
                 "reconstruct": "reconstruct_kernel"}
 
 
+def clock_pass(dev, n: int = 6):
+    """For a GRBM_GUI_ACTIVE counter run: n fused prefills (M = 2048) of a
+    gate-shaped 28672x8192 matrix with finite weights and per-matrix alpha,
+    then n library GEMMs (torch.mm) of the same shape on W_base."""
+    g = S.generator(45, dev)
+    M, d_out, d_in = 2048, 28672, 8192
+    wb = S.draw_base(d_out, d_in, 0.015, g, dev)
+    wf = S.draw_finetuned(wb, 1e-3, g)
+    p, a = T.compress(wf, wb, 0)
+    del wf
+    x = S.draw_activations(M, d_in, g, dev)
+    y = torch.empty(M, d_out, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(n):
+        T.linear(x, wb, p, a, 0, y=y)
+    torch.cuda.synchronize()
+    for _ in range(n):
+        torch.mm(x, wb.t(), out=y)
+    torch.cuda.synchronize()
+
+
 def counter_pass(w: ProjWorkload, n: int):
     """n eager launches of each kernel of the step, block by block, each on its
     own rotation copy; then n launches of the calibration kernel."""
@@ -962,6 +983,9 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/*_proj_4096_pmc.json from two --pmc runs, then exit")
     ap.add_argument("--counter-launches", type=int, default=8)
+    ap.add_argument("--clock-pass", action="store_true",
+                    help="six fused gate-shaped prefills then six library GEMMs, for a "
+                         "rocprofv3 --pmc GRBM_GUI_ACTIVE run, then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -980,6 +1004,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     T.lib()
+    if args.clock_pass:
+        clock_pass(dev)
+        print("[bench] clock pass done", file=sys.stderr, flush=True)
+        return
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     if args.workload == "serve_layer70b":
         serve_layer70b(args, dev)
