@@ -260,7 +260,8 @@ __global__ __launch_bounds__(256) void ms_merge_kernel(const uint16_t* __restric
                                                        uint16_t* __restrict__ out,
                                                        float* __restrict__ tau) {
   __shared__ float Ys[16][R];
-  __shared__ float Zs[128][R + 1];
+  __shared__ __attribute__((aligned(16))) float Zs[R][128];  // transposed: a thread's 8
+                                                              // columns are 32 contiguous bytes
   const int t = threadIdx.x;
   const int o0 = blockIdx.y * 16;
   const int c0 = blockIdx.x * 128;
@@ -279,14 +280,22 @@ __global__ __launch_bounds__(256) void ms_merge_kernel(const uint16_t* __restric
     }
     for (int u = t; u < 128 * R; u += 256) {
       const int cc = u / R, j = u % R;
-      Zs[cc][j] = Zi[(size_t)min(c0 + cc, d_in - 1) * R + j];
+      Zs[j][cc] = Zi[(size_t)min(c0 + cc, d_in - 1) * R + j];
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < R; ++j) {
       const float y = Ys[lr][j];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += y * Zs[lc + e][j];
+      const float4 z0 = *reinterpret_cast<const float4*>(&Zs[j][lc]);
+      const float4 z1 = *reinterpret_cast<const float4*>(&Zs[j][lc + 4]);
+      acc[0] += y * z0.x;
+      acc[1] += y * z0.y;
+      acc[2] += y * z0.z;
+      acc[3] += y * z0.w;
+      acc[4] += y * z1.x;
+      acc[5] += y * z1.y;
+      acc[6] += y * z1.z;
+      acc[7] += y * z1.w;
     }
   }
   const int o = o0 + lr;
