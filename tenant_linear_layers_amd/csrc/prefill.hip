@@ -305,7 +305,7 @@ template <bool XPF, int TBM, int WM, int WN>
 __global__ __launch_bounds__(64 * (WM * WN + 4), 1) void prefill_pc_kernel(
     const uint16_t* __restrict__ x, int M, const uint16_t* __restrict__ w,
     const uint8_t* __restrict__ bits8, const float* __restrict__ alpha, int per_row, int d_out,
-    int d_in, uint16_t* __restrict__ y, int ldy, int ntm, int ntn, int chunk) {
+    int d_in, uint16_t* __restrict__ y, int ldy, int ntm, int ntn, int chunk, int xg) {
   constexpr int NMW = WM * WN;          // MFMA waves; 4 producer waves follow
   constexpr int TMW = TBM / WM / 32;    // 32-row MFMA tiles per wave
   constexpr int TNW = PC_BN / WN / 32;  // 32-column MFMA tiles per wave
@@ -319,11 +319,27 @@ __global__ __launch_bounds__(64 * (WM * WN + 4), 1) void prefill_pc_kernel(
   __shared__ __attribute__((aligned(16))) unsigned char W0[PC_WSTAGE];
   __shared__ __attribute__((aligned(16))) unsigned char W1[PC_WSTAGE];
 
-  // contiguous tile ranges per XCD, token tile fastest (as in prefill_kernel)
-  const int tile = (blockIdx.x & 7) * chunk + (blockIdx.x >> 3);
-  if (tile >= ntm * ntn) return;
-  const int m0 = (tile % ntm) * TBM;
-  const int n0 = (tile / ntm) * PC_BN;
+  // Workgroups are dealt round-robin to the 8 XCDs.  With xg == 1 each XCD
+  // takes a contiguous range of tiles, token tile fastest (as in
+  // prefill_kernel); with xg > 1 the token tiles form xg groups and the
+  // weight tiles 8 / xg groups (the host checks both divide evenly) and each
+  // XCD takes one (token group, weight group) block, so that it fetches a
+  // 1/xg share of x into its L2 instead of all of it.
+  const int xcd = blockIdx.x & 7;
+  const int local = blockIdx.x >> 3;
+  int tm, tn;
+  if (xg == 1) {
+    const int tile = xcd * chunk + local;
+    if (tile >= ntm * ntn) return;
+    tm = tile % ntm;
+    tn = tile / ntm;
+  } else {
+    const int tmg = ntm / xg;
+    tm = (xcd % xg) * tmg + local % tmg;
+    tn = (xcd / xg) * (ntn / (8 / xg)) + local / tmg;
+  }
+  const int m0 = tm * TBM;
+  const int n0 = tn * PC_BN;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   const int nk = d_in / BK;
@@ -499,9 +515,17 @@ hipError_t launch_pc_cfg(const uint16_t* x, int M, const uint16_t* w, const uint
   const int ntn = (d_out + PC_BN - 1) / PC_BN;
   const int tiles = ntm * ntn;
   const int chunk = (tiles + 7) / 8;
+  // XCD blocks (see the kernel): xg token groups times 8 / xg weight groups
+  // where both divide evenly, xg minimising what the 8 L2s fetch between
+  // them, 8/xg copies of x plus xg copies of W (ties keep the smaller xg).
+  int xg = 1;
+  for (int g = 2; g <= 8; g *= 2) {
+    if (ntm % g != 0 || ntn % (8 / g) != 0) continue;
+    if ((8 / g) * (int64_t)M + g * (int64_t)d_out < (8 / xg) * (int64_t)M + xg * (int64_t)d_out) xg = g;
+  }
   hipLaunchKernelGGL((prefill_pc_kernel<XPF, TBM, WM, WN>), dim3(8 * chunk),
                      dim3(64 * (WM * WN + 4)), 0, stream, x, M, w, packed_bytes, alpha, per_row,
-                     d_out, d_in, y, ldy, ntm, ntn, chunk);
+                     d_out, d_in, y, ldy, ntm, ntn, chunk, xg);
   return hipGetLastError();
 }
 
