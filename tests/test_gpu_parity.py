@@ -229,6 +229,31 @@ def test_linear_prefill_tile_paths(case):
                    oracle_y(x, wb, packed, alpha, mode, rows=rows), f"prefill path {case}")
 
 
+# Products whose producer/consumer tiles are dealt to the 8 XCDs in blocks
+# of g token-tile groups times 8/g weight-tile groups (the launcher picks g
+# by what the L2s fetch): g = 4 and g = 8 on 256 x 128 tiles, g = 2 on
+# 512 x 128 tiles.  A tile dealt twice or never would leave part of y
+# unwritten (y is allocated empty), so every output is compared.
+# (M, d_out, d_in, mode)
+PREFILL_XCD_BLOCKS = [
+    (4096, 2048, 256, 0),
+    (8192, 1024, 256, 1),
+    (4096, 4096, 192, 0),
+]
+
+
+@pytest.mark.parametrize("case", PREFILL_XCD_BLOCKS, ids=lambda c: f"M{c[0]}_{c[1]}x{c[2]}")
+def test_linear_prefill_xcd_blocks_full_output(case):
+    m, d_out, d_in, mode = case
+    wb, wf = S.small_pair(d_out, d_in, 0.02, 1e-3, seed=d_out + m + 3)
+    x = S.draw_activations(m, d_in, S.generator(m + 9))
+    wb, wf, x = to_dev(wb, wf, x)
+    packed, alpha = T.compress(wf, wb, mode)
+    y = torch.full((m, d_out), float("nan"), dtype=torch.bfloat16, device=DEV)
+    T.linear(x, wb, packed, alpha, mode, y=y)
+    assert_y_close(y, oracle_y(x, wb, packed, alpha, mode), f"prefill XCD blocks {case}")
+
+
 def test_linear_prefill_large_x_prefetch():
     """x of more than 64 MiB (1024 x 32832) takes the producer/consumer tiles
     with x prefetched into L2 two steps ahead; 513 steps (odd)."""
