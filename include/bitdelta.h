@@ -390,6 +390,28 @@ int bitdelta_monosoup_merge(const uint16_t* const* w_ft, int32_t k, const uint16
                             const float* omega, uint16_t* w_merged, float* tau_mean,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Calibration probes - measured ceilings for the rooflines of the kernels
+ * above (they compute nothing of the method).
+ *
+ * bitdelta_probe_stream_read reads `bytes` (a multiple of 16) of device
+ * memory at src (16-byte aligned) once, with 16-byte loads: workgroup b of
+ * `workgroups` (256 threads each) reads the b-th contiguous chunk.  sink is
+ * device memory of 1024 bytes (4-byte aligned) that the kernel may write; its
+ * contents mean nothing.  Time it to get the sustained HBM read rate.
+ *
+ * bitdelta_probe_mfma_bf16 runs `workgroups` workgroups of 4 waves; every
+ * wave issues 8 * iters back-to-back v_mfma_f32_32x32x16_bf16 (8 independent
+ * accumulator chains), 32768 flops each: 1048576 * workgroups * iters flops
+ * in all.  sink as above.  Time it to get the sustained bf16 matrix-core rate.
+ *
+ * Both return BITDELTA_OK or an error status (BITDELTA_ERR_SHAPE for sizes
+ * out of range); nothing is enqueued on error.
+ */
+int bitdelta_probe_stream_read(const void* src, size_t bytes, int32_t workgroups, uint32_t* sink,
+                               void* stream);
+int bitdelta_probe_mfma_bf16(int32_t workgroups, int32_t iters, float* sink, void* stream);
+
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* bitdelta_status_string(int status);
 

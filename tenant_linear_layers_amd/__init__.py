@@ -29,6 +29,8 @@ from .bitdelta import (  # noqa: F401
     linear_multi,
     monosoup_merge,
     monosoup_workspace_size,
+    probe_mfma_bf16,
+    probe_stream_read,
     Router,
     ratio_to_f32_bits,
     reconstruct,

@@ -63,6 +63,8 @@ EXPORTS = (
     "bitdelta_router_pending",
     "bitdelta_monosoup_workspace_size",
     "bitdelta_monosoup_merge",
+    "bitdelta_probe_stream_read",
+    "bitdelta_probe_mfma_bf16",
 )
 
 MONOSOUP_MAX_RANK = 32
@@ -143,6 +145,10 @@ def lib() -> ctypes.CDLL:
     L.bitdelta_monosoup_merge.argtypes = [vp, ctypes.c_int32, vp, i64, i64, ctypes.c_int32,
                                           ctypes.c_int32, vp, vp, vp, vp, sz, vp]
     L.bitdelta_monosoup_merge.restype = i32
+    L.bitdelta_probe_stream_read.argtypes = [vp, sz, ctypes.c_int32, vp, vp]
+    L.bitdelta_probe_stream_read.restype = i32
+    L.bitdelta_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp]
+    L.bitdelta_probe_mfma_bf16.restype = i32
     _lib = L
     return L
 
@@ -537,3 +543,28 @@ def monosoup_merge(w_fts, w_base: torch.Tensor, rank: int, power_iters: int,
                                            _ptr(tau), _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "bitdelta_monosoup_merge")
     return out, tau
+
+
+# ------------------------------------------------------------------ calibration
+def probe_stream_read(src: torch.Tensor, workgroups: int, sink: torch.Tensor, stream=None):
+    """One plain read of every byte of src (device, 16-byte multiple) by
+    `workgroups` workgroups; sink: device tensor of at least 1024 bytes."""
+    if not src.is_cuda or not src.is_contiguous() or not sink.is_cuda:
+        raise ValueError("src and sink must be contiguous device tensors")
+    if sink.numel() * sink.element_size() < 1024:
+        raise ValueError("sink must hold at least 1024 bytes")
+    nbytes = src.numel() * src.element_size()
+    with _on(src.device):
+        st = lib().bitdelta_probe_stream_read(_ptr(src), nbytes, workgroups, _ptr(sink),
+                                              _stream(stream))
+    _check(st, "bitdelta_probe_stream_read")
+
+
+def probe_mfma_bf16(workgroups: int, iters: int, sink: torch.Tensor, stream=None) -> int:
+    """Back-to-back bf16 matrix-core instructions; returns the flops issued."""
+    if not sink.is_cuda or sink.numel() * sink.element_size() < 1024:
+        raise ValueError("sink must be a device tensor of at least 1024 bytes")
+    with _on(sink.device):
+        st = lib().bitdelta_probe_mfma_bf16(workgroups, iters, _ptr(sink), _stream(stream))
+    _check(st, "bitdelta_probe_mfma_bf16")
+    return 1048576 * workgroups * iters

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libbitdelta.so")
 
 SOURCES = ("api.hip", "compress.hip", "decode.hip", "prefill.hip", "reconstruct.hip",
-           "cache.hip", "monosoup.hip")
+           "cache.hip", "monosoup.hip", "probe.hip")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

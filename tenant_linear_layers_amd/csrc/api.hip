@@ -280,3 +280,28 @@ BD_EXPORT int bitdelta_monosoup_merge(const uint16_t* const* w_ft, int32_t k,
                                        omega, w_merged, tau_mean, workspace,
                                        static_cast<hipStream_t>(stream)));
 }
+
+BD_EXPORT int bitdelta_probe_stream_read(const void* src, size_t bytes, int32_t workgroups,
+                                         uint32_t* sink, void* stream) {
+  if (!src || !sink) return BITDELTA_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0 || workgroups < 1 || workgroups > (1 << 20))
+    return BITDELTA_ERR_SHAPE;
+  if (!aligned16(src) || (reinterpret_cast<uintptr_t>(sink) & 3u)) return BITDELTA_ERR_ALIGN;
+  if (overlap(sink, 1024, src, bytes)) return BITDELTA_ERR_OVERLAP;
+  const int dev = check_device();
+  if (dev != BITDELTA_OK) return dev;
+  return status_of(bd::launch_probe_read(src, bytes, workgroups, sink,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+BD_EXPORT int bitdelta_probe_mfma_bf16(int32_t workgroups, int32_t iters, float* sink,
+                                       void* stream) {
+  if (!sink) return BITDELTA_ERR_NULL;
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 24))
+    return BITDELTA_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(sink) & 3u) return BITDELTA_ERR_ALIGN;
+  const int dev = check_device();
+  if (dev != BITDELTA_OK) return dev;
+  return status_of(bd::launch_probe_mfma(workgroups, iters, sink,
+                                         static_cast<hipStream_t>(stream)));
+}

@@ -55,4 +55,9 @@ hipError_t launch_monosoup(const uint16_t* const* w_ft, int k, const uint16_t* w
                            int d_in, int rank, int power_iters, const float* omega, uint16_t* out,
                            float* tau, void* workspace, hipStream_t stream);
 
+// Calibration kernels (measured ceilings beside the published peaks).
+hipError_t launch_probe_read(const void* src, size_t bytes, int workgroups, uint32_t* sink,
+                             hipStream_t stream);
+hipError_t launch_probe_mfma(int workgroups, int iters, float* sink, hipStream_t stream);
+
 }  // namespace bd

@@ -163,3 +163,19 @@ def test_monosoup_argument_checks():
     assert call(out=B) == 9                               # output over a checkpoint
     nul = (ctypes.c_void_p * 2)(A, None)
     assert call(w=nul) == 1
+
+
+def test_probe_argument_checks():
+    """The calibration probes reject bad arguments before any HIP call."""
+    L = T.lib()
+    f, g = L.bitdelta_probe_stream_read, L.bitdelta_probe_mfma_bf16
+    vp = ctypes.c_void_p
+    assert f(vp(0), 1024, 8, vp(B), None) == 1
+    assert f(vp(A), 1024, 8, vp(0), None) == 1
+    assert f(vp(A), 0, 8, vp(B), None) == 2 and f(vp(A), 1000, 8, vp(B), None) == 2
+    assert f(vp(A), 1024, 0, vp(B), None) == 2 and f(vp(A), 1024, (1 << 20) + 1, vp(B), None) == 2
+    assert f(vp(A + 8), 1024, 8, vp(B), None) == 3 and f(vp(A), 1024, 8, vp(B + 2), None) == 3
+    assert f(vp(A), 4096, 8, vp(A + 512), None) == 9       # sink inside the source
+    assert g(8, 16, vp(0), None) == 1
+    assert g(0, 16, vp(B), None) == 2 and g(8, 0, vp(B), None) == 2
+    assert g(8, (1 << 24) + 1, vp(B), None) == 2 and g(8, 16, vp(B + 1), None) == 3
