@@ -108,6 +108,26 @@ int bitdelta_compress(const uint16_t* w_ft, const uint16_t* w_base, int64_t d_ou
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * bitdelta_compress_noalloc - bitdelta_compress for callers that cannot
+ * allocate memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same computation and results, with
+ * no workspace argument and no allocation of any kind.  In per-matrix mode
+ * the per-row partial sums live in a scratch array of 4 MiB that the library
+ * keeps on each GPU it runs on until the process ends, so d_out is limited to
+ * 262144 rows there (BITDELTA_ERR_WORKSPACE beyond); per-row mode needs no
+ * scratch and takes any shape bitdelta_compress takes.  All calls on one GPU
+ * share that GPU's scratch: per-matrix calls that may overlap in time on one
+ * GPU (different streams, or concurrent graph replays) race and must be
+ * ordered by the caller.  Every partial sum a call reads was written by that
+ * call, so nothing needs clearing between calls.
+ * Arguments, layout, ownership and errors otherwise as bitdelta_compress;
+ * BITDELTA_ERR_HIP if the scratch's device address cannot be obtained.
+ */
+int bitdelta_compress_noalloc(const uint16_t* w_ft, const uint16_t* w_base, int64_t d_out,
+                              int64_t d_in, int alpha_mode, uint64_t* packed, float* alpha,
+                              void* stream);
+
+/*
  * bitdelta_linear - fused BitDelta linear for one variant:
  *   y[m, o] = sum_i x[m, i] * (W_base[o, i] + alpha_o * s[o, i]),   no bias
  * (section "Sunum mimarisi", the conceptual fused kernel; s from the packed

@@ -21,6 +21,7 @@ from .bitdelta import (  # noqa: F401
     BitDeltaError,
     DeltaCache,
     compress,
+    compress_noalloc,
     compress_workspace_size,
     delta_layout,
     delta_views,

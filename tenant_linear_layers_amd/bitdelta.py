@@ -41,6 +41,7 @@ CACHE_ABSENT, CACHE_LOADING, CACHE_RESIDENT = 0, 1, 2
 EXPORTS = (
     "bitdelta_compress_workspace_size",
     "bitdelta_compress",
+    "bitdelta_compress_noalloc",
     "bitdelta_linear",
     "bitdelta_linear_multi",
     "bitdelta_reconstruct",
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.bitdelta_compress_workspace_size.restype = sz
     L.bitdelta_compress.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp, sz, vp]
     L.bitdelta_compress.restype = i32
+    L.bitdelta_compress_noalloc.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp]
+    L.bitdelta_compress_noalloc.restype = i32
     L.bitdelta_linear.argtypes = [vp, i64, vp, vp, vp, i32, i64, i64, vp, vp]
     L.bitdelta_linear.restype = i32
     L.bitdelta_linear_multi.argtypes = [vp, i64, vp, vp, ctypes.c_int32, vp, vp, i32, i64, i64,
@@ -243,6 +246,26 @@ def compress(w_ft: torch.Tensor, w_base: torch.Tensor, alpha_mode: int, packed=N
                                      _ptr(packed), _ptr(alpha), _ptr(workspace), ws_bytes,
                                      _stream(stream))
     _check(st, "bitdelta_compress")
+    return packed, alpha
+
+
+def compress_noalloc(w_ft: torch.Tensor, w_base: torch.Tensor, alpha_mode: int, packed: torch.Tensor,
+                     alpha: torch.Tensor, stream=None):
+    """compress into caller tensors through bitdelta_compress_noalloc (no
+    workspace, nothing allocated by the library or here)."""
+    _need(w_base, "w_base", torch.bfloat16)
+    dev = w_base.device
+    _need(w_ft, "w_ft", torch.bfloat16, dev)
+    if w_base.dim() != 2 or w_ft.shape != w_base.shape:
+        raise ValueError("w_ft and w_base must be 2-D and of one shape")
+    d_out, d_in = w_base.shape
+    _need(packed, "packed", torch.int64, dev)
+    _need(alpha, "alpha", torch.float32, dev)
+    _signs_and_scale(packed, alpha, d_out, d_in, alpha_mode)
+    with _on(dev):
+        st = lib().bitdelta_compress_noalloc(_ptr(w_ft), _ptr(w_base), d_out, d_in, alpha_mode,
+                                             _ptr(packed), _ptr(alpha), _stream(stream))
+    _check(st, "bitdelta_compress_noalloc")
     return packed, alpha
 
 

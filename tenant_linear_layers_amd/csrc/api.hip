@@ -3,6 +3,7 @@
 // include/bitdelta.h for the contract of each entry point.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "bitdelta.h"
 #include "common.h"
@@ -111,6 +112,73 @@ BD_EXPORT int bitdelta_compress(const uint16_t* w_ft, const uint16_t* w_base, in
                                        alpha_mode == BITDELTA_ALPHA_PER_ROW, packed, alpha,
                                        static_cast<uint64_t*>(workspace),
                                        static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------ no-alloc
+// Scratch of bitdelta_compress_noalloc: the per-row integer partial sums of a
+// per-matrix scale (16 bytes per row), in a file-scope device array instead
+// of a caller workspace.  Each GPU holds its own copy for the life of the
+// process.  Host code never uses the array's name as an address: the device
+// address is looked up once per device, with that device current, and kept.
+constexpr int64_t kNoAllocMaxRows = 262144;  // 4 MiB of scratch
+static __device__ __align__(256) uint64_t scratch[2 * kNoAllocMaxRows];
+
+namespace {
+void* g_scratch_ptr[64];
+hipError_t g_scratch_err[64];
+std::once_flag g_scratch_once[64];
+
+// Device address of this device's scratch (nullptr on failure, with *err set).
+void* scratch_on_current_device(hipError_t* err) {
+  int dev = 0;
+  *err = hipGetDevice(&dev);
+  if (*err != hipSuccess) return nullptr;
+  if (dev < 0 || dev >= 64) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress((void**)&p, HIP_SYMBOL(scratch));
+    g_scratch_err[dev] = e;
+    g_scratch_ptr[dev] = e == hipSuccess ? p : nullptr;
+  });
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+BD_EXPORT int bitdelta_compress_noalloc(const uint16_t* w_ft, const uint16_t* w_base,
+                                        int64_t d_out, int64_t d_in, int alpha_mode,
+                                        uint64_t* packed, float* alpha, void* stream) {
+  if (!w_ft || !w_base || !packed || !alpha) return BITDELTA_ERR_NULL;
+  if (!shape_ok(d_out, d_in)) return BITDELTA_ERR_SHAPE;
+  if (alpha_mode != BITDELTA_ALPHA_PER_MATRIX && alpha_mode != BITDELTA_ALPHA_PER_ROW)
+    return BITDELTA_ERR_MODE;
+  if (alpha_mode == BITDELTA_ALPHA_PER_MATRIX && d_out > kNoAllocMaxRows)
+    return BITDELTA_ERR_WORKSPACE;
+  if (!aligned16(w_ft) || !aligned16(w_base) || !aligned16(packed) || !aligned16(alpha))
+    return BITDELTA_ERR_ALIGN;
+  const size_t wbytes = (size_t)d_out * (size_t)d_in * 2u;
+  const size_t pbytes = wbytes / 16u;
+  const size_t abytes = alpha_mode == BITDELTA_ALPHA_PER_ROW ? (size_t)d_out * 4u : 4u;
+  if (overlap(packed, pbytes, w_ft, wbytes) || overlap(packed, pbytes, w_base, wbytes) ||
+      overlap(alpha, abytes, w_ft, wbytes) || overlap(alpha, abytes, w_base, wbytes) ||
+      overlap(alpha, abytes, packed, pbytes))
+    return BITDELTA_ERR_OVERLAP;
+  const int dev = check_device();
+  if (dev != BITDELTA_OK) return dev;
+  uint64_t* partial = nullptr;
+  if (alpha_mode == BITDELTA_ALPHA_PER_MATRIX) {
+    hipError_t e = hipSuccess;
+    partial = static_cast<uint64_t*>(scratch_on_current_device(&e));
+    if (e != hipSuccess || !partial) return BITDELTA_ERR_HIP;
+  }
+  // The row pass writes both limbs of every row 0..d_out-1 before the
+  // finalize reads them, so nothing left by an earlier call is ever read.
+  return status_of(bd::launch_compress(w_ft, w_base, (int)d_out, (int)d_in,
+                                       alpha_mode == BITDELTA_ALPHA_PER_ROW, packed, alpha,
+                                       partial, static_cast<hipStream_t>(stream)));
 }
 
 BD_EXPORT int bitdelta_linear(const uint16_t* x, int64_t M, const uint16_t* w_base,

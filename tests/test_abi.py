@@ -179,3 +179,16 @@ def test_probe_argument_checks():
     assert g(8, 16, vp(0), None) == 1
     assert g(0, 16, vp(B), None) == 2 and g(8, 0, vp(B), None) == 2
     assert g(8, (1 << 24) + 1, vp(B), None) == 2 and g(8, 16, vp(B + 1), None) == 3
+
+
+def test_compress_noalloc_argument_checks():
+    """bitdelta_compress_noalloc rejects bad arguments, and per-matrix shapes
+    past its 262144-row scratch, before any HIP call."""
+    f = T.lib().bitdelta_compress_noalloc
+    vp = ctypes.c_void_p
+    assert f(vp(0), vp(B), 16, 64, 0, vp(C), vp(D), None) == 1
+    assert f(vp(A), vp(B), 16, 100, 0, vp(C), vp(D), None) == 2
+    assert f(vp(A), vp(B), 16, 64, 2, vp(C), vp(D), None) == 4
+    assert f(vp(A), vp(B), 262145, 64, 0, vp(C), vp(D), None) == 6
+    assert f(vp(A + 8), vp(B), 16, 64, 0, vp(C), vp(D), None) == 3
+    assert f(vp(A), vp(B), 16, 64, 1, vp(A + 64), vp(D), None) == 9
