@@ -618,8 +618,10 @@ hipError_t launch_linear_prefill(const uint16_t* x, int M, const uint16_t* w,
   if (d_in <= kPcMaxDin && 10 * ntm_pc * PC_BM <= 11 * ntm * BM) {
     const long tiles = ntm_pc * ((d_out + PC_BN - 1) / PC_BN);
     const long full = tiles / kCUs;
-    if (full >= 1) {
-      const long rows = tiles % kCUs == 0 ? d_out : (full * kCUs / ntm_pc) * PC_BN;
+    // rows is 0 when the whole rounds hold fewer tiles than one weight tile's
+    // column of token tiles (tall x over few rows): then 256-token tiles only.
+    const long rows = full < 1 ? 0 : tiles % kCUs == 0 ? d_out : (full * kCUs / ntm_pc) * PC_BN;
+    if (rows > 0) {
       if (rows >= d_out)
         return launch_pc(x, M, w, packed_bytes, alpha, per_row, d_out, d_in, y, d_out, stream);
       hipError_t e =

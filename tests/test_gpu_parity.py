@@ -254,6 +254,21 @@ def test_linear_prefill_xcd_blocks_full_output(case):
     assert_y_close(y, oracle_y(x, wb, packed, alpha, mode), f"prefill XCD blocks {case}")
 
 
+def test_linear_prefill_tall_x_few_rows():
+    """M = 200000 tokens over 128 rows: the whole rounds of producer/consumer
+    tiles hold fewer tiles than one weight tile's column of token tiles, so
+    the launcher takes 256-token tiles for the whole product (a zero-row
+    producer/consumer launch before the guard).  Every output is compared."""
+    m, d_out, d_in = 200000, 128, 64
+    wb, wf = S.small_pair(d_out, d_in, 0.02, 1e-3, seed=77)
+    x = S.draw_activations(m, d_in, S.generator(78))
+    wb, wf, x = to_dev(wb, wf, x)
+    packed, alpha = T.compress(wf, wb, 0)
+    y = torch.full((m, d_out), float("nan"), dtype=torch.bfloat16, device=DEV)
+    T.linear(x, wb, packed, alpha, 0, y=y)
+    assert_y_close(y, oracle_y(x, wb, packed, alpha, 0), "prefill tall x, few rows")
+
+
 def test_linear_prefill_large_x_prefetch():
     """x of more than 64 MiB (1024 x 32832) takes the producer/consumer tiles
     with x prefetched into L2 two steps ahead; 513 steps (odd)."""
