@@ -120,9 +120,9 @@ def capture(fn) -> torch.cuda.CUDAGraph:
     return g
 
 
-def time_replays(graph, reps: int) -> float:
-    """Mean milliseconds per replay, from HIP events recorded on the stream
-    the graph runs on, around each replay."""
+def time_replays(graph, reps: int) -> list:
+    """Milliseconds of each of `reps` replays, from HIP events recorded on the
+    stream the graph runs on, around each replay."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(reps)]
     for s, e in evs:
@@ -130,7 +130,13 @@ def time_replays(graph, reps: int) -> float:
         graph.replay()
         e.record()
     torch.cuda.synchronize()
-    return sum(s.elapsed_time(e) for s, e in evs) / reps
+    return [s.elapsed_time(e) for s, e in evs]
+
+
+def median(xs) -> float:
+    v = sorted(xs)
+    n = len(v)
+    return v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
 
 
 # ------------------------------------------------------------------ workload
@@ -676,7 +682,7 @@ def monosoup_4096(args, dev):
     graph = capture(lambda: T.monosoup_merge(wf, wb, rank, q, omega, out=out, workspace=ws))
     for _ in range(args.warmup):
         graph.replay()
-    ms = time_replays(graph, max(3, args.steps))
+    ms = median(time_replays(graph, max(REPS, args.steps)))
     if not torch.equal(out.view(torch.int16), ref.view(torch.int16)):
         raise RuntimeError("graph replays of the merge differ from the eager call")
     nbytes = k * 2 * (q + 1) * 4 * d * d + 4 * d * d
@@ -712,11 +718,6 @@ def cpu_baseline(w: ProjWorkload, budget_s: float):
     compression of the projection and the three decode products (all 4096 rows),
     repeated while the time budget lasts.  Reported in the metric's unit."""
     import oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        threads = 1
     wb = S.bf16_bits(w.host["wb"])
     wf = S.bf16_bits(w.host["wf"])
     xs = {m: S.bf16_bits(x) for m, x in w.host["xs"].items()}
@@ -733,16 +734,11 @@ def cpu_baseline(w: ProjWorkload, budget_s: float):
         passes += 1
         if t_dec + t_comp > budget_s or passes >= 200:
             break
-    return {
-        "value": round(nbytes / t_dec / 1e9, 4),
-        "unit": "GB/s",
-        "cores": int(threads),
-        "kind": "oracle",
-        "sample": (f"oracle decode products M={list(w.decode_ms)} on the full 4096x4096 "
-                   f"projection, {passes} pass(es), {t_dec:.1f} s; oracle compression of the "
-                   f"same matrix {t_comp:.1f} s ({w.compress_bytes() / t_comp / 1e9:.3f} GB/s)"),
-        "host_cores_available": len(os.sched_getaffinity(0)),
-    }
+    return _cpu_record(
+        round(nbytes / t_dec / 1e9, 4), "GB/s",
+        f"oracle decode products M={list(w.decode_ms)} on the full 4096x4096 projection, "
+        f"{passes} pass(es), {t_dec:.1f} s; oracle compression of the same matrix "
+        f"{t_comp:.1f} s ({w.compress_bytes() / t_comp / 1e9:.3f} GB/s)")
 
 
 # ------------------------------------------------------------------ counters
@@ -962,9 +958,370 @@ def measure_delta_loads(decode_graph, n_decode: int, decode_alone_us: float):
     }
 
 
-def roofline_entry(bound, achieved, peak, unit, traffic=None):
-    return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": traffic}
+REPS = 50                      # replays per timing graph; the median is reported
+
+
+def roofline_entry(bound, achieved, peak, unit, traffic=None, measured=None):
+    """Roofline of one kernel: achieved against the published peak, and
+    against the ceiling measured on this GPU by the calibration probes."""
+    e = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+         "frac": round(achieved / peak, 4), "traffic": traffic}
+    if measured:
+        e["measured_peak"] = round(measured, 2)
+        e["frac_vs_measured"] = round(achieved / measured, 4)
+    return e
+
+
+# ------------------------------------------------------------------ ceilings
+def measure_ceilings(dev):
+    """What this GPU reaches on plain work: a stream read of 1 GiB (the best
+    of several workgroup counts), the same read as 32 MiB launches cycling
+    over 32 distinct buffers (the size of one decode launch on the
+    projection), and back-to-back bf16 MFMA (the best of two grid sizes)."""
+    sink = torch.zeros(256, dtype=torch.int32, device=dev)
+    big = torch.zeros(2**30 // 2, dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+    res = {}
+    best = (0.0, 0)
+    for wg in (1024, 2048, 4096, 8192):
+        g = capture(lambda wg=wg: [T.probe_stream_read(big, wg, sink) for _ in range(4)])
+        ms = median(time_replays(g, 20)) / 4
+        best = max(best, (2**30 / (ms * 1e-3) / 1e9, wg))
+    res["hbm_read_gbs"] = round(best[0], 1)
+    res["hbm_read_workgroups"] = best[1]
+    chunks = [big[i * 2**24:(i + 1) * 2**24] for i in range(32)]
+    best32 = (0.0, 0)
+    for wg in (256, 512, 1024, 2048):
+        g = capture(lambda wg=wg: [T.probe_stream_read(c, wg, sink) for _ in range(4)
+                                   for c in chunks])
+        ms = median(time_replays(g, 20)) / 128
+        best32 = max(best32, (2**25 / (ms * 1e-3) / 1e9, wg))
+    res["hbm_read_32mib_gbs"] = round(best32[0], 1)
+    res["hbm_read_32mib_workgroups"] = best32[1]
+    del big, chunks
+    bestm = (0.0, 0)
+    for wg in (512, 1024):
+        iters = 2048
+        flops = [0]
+        g = capture(lambda wg=wg: flops.__setitem__(0, sum(T.probe_mfma_bf16(wg, iters, sink)
+                                                          for _ in range(4))))
+        ms = median(time_replays(g, 10))
+        bestm = max(bestm, (flops[0] / (ms * 1e-3) / 1e12, wg))
+    res["bf16_mfma_tflops"] = round(bestm[0], 1)
+    res["bf16_mfma_workgroups"] = bestm[1]
+    res["bf16_mfma_implied_ghz"] = round(2.4 * bestm[0] / BF16_PEAK_TFLOPS, 3)
+    torch.cuda.synchronize()
+    return res
+
+
+# ------------------------------------------------------------------ timing
+def time_workload(w, args, n_pass=1, check=None):
+    """Graphs of one pass of the path (the steps) and of each kernel range;
+    K timed steps (HIP events around each replay, between synchronisations),
+    then REPS timed replays of each range: the median replay divided by its
+    launches is the kernel's launch duration.  check(name) runs after a
+    range's replays (the graphs must reproduce eager results)."""
+    passes = [capture(lambda j=j: w.one_pass(j)) for j in range(n_pass)]
+    range_graphs = {name: (n, capture(fn)) for name, (n, fn) in w.ranges().items()}
+    for i in range(args.warmup):
+        passes[i % n_pass].replay()
+    torch.cuda.synchronize()
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step_ev[i][0].record()
+        passes[i % n_pass].replay()
+        step_ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_list = [s.elapsed_time(e) for s, e in step_ev]
+    avg_us = {}
+    for name, (n, g) in range_graphs.items():
+        g.replay()
+        avg_us[name] = 1e3 * median(time_replays(g, REPS)) / n
+        if check:
+            check(name)
+    print(f"[bench] {w.name}: timed {args.steps} steps in {wall:.3f} s "
+          f"(GPU {sum(step_list) / len(step_list):.3f} ms per step)", file=sys.stderr, flush=True)
+    return {"step_ms": sum(step_list) / len(step_list), "step_ms_median": median(step_list),
+            "wall_s": wall, "avg_us": avg_us, "range_graphs": range_graphs}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def _cpu_record(value, unit, sample):
+    return {"value": value, "unit": unit, "cores": int(_blas_threads()), "kind": "oracle",
+            "sample": sample, "host_cores_available": len(os.sched_getaffinity(0)),
+            "cores_note": "cores = numpy BLAS threads the oracle's float64 products ran on; "
+                          "host_cores_available = CPUs this process may use"}
+
+
+# ------------------------------------------------------------------ proj_4096
+def bench_proj(args, dev, ceil):
+    """The 4096x4096 projection (the metric's decode configuration): the
+    whole path per step, each kernel's launch duration, the unfused A/B and
+    the delta loads.  Returns (record, workload)."""
+    w = ProjWorkload(dev)
+    torch.cuda.synchronize()
+    print(f"[bench] proj_4096: rotation copies R={w.R}, distinct variants in the mixed batch "
+          f"D={w.distinct}", file=sys.stderr, flush=True)
+    n_pass = max(1, w.R // 6)
+    # eager references of the unfused A/B outputs, checked after each range
+    eager_ref = {}
+    for m in list(w.decode_ms) + [w.prefill_m]:
+        w.run_dense(m, 0)
+        eager_ref[f"dense_m{m}"] = (w.ys_dense[m], w.ys_dense[m].clone())
+    w.run_reconstruct(0)
+    eager_ref["reconstruct"] = (w.w_eff, w.w_eff.clone())
+    w.run_decode(16, 0)
+    eager_ref["decode_m16"] = (w.ys[16], w.ys[16].clone())
+    torch.cuda.synchronize()
+
+    def check(name):
+        if name in eager_ref:
+            buf, ref = eager_ref[name]
+            assert torch.equal(buf.view(torch.int16), ref.view(torch.int16)), (
+                f"graph replays of {name} differ from the eager launch")
+
+    t = time_workload(w, args, n_pass, check)
+    avg_us = t["avg_us"]
+    dec_bytes = sum(w.decode_bytes(m) for m in w.decode_ms)
+    dec_us = sum(avg_us[f"decode_m{m}"] for m in w.decode_ms)
+    dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
+    pre_tflops = w.prefill_flops() / (avg_us["prefill"] * 1e-6) / 1e12
+    hbm = ceil.get("hbm_read_32mib_gbs")
+    mfma = ceil.get("bf16_mfma_tflops")
+    rooflines = {
+        "decode": roofline_entry("hbm", dec_gbs, HBM_PEAK_GBS, "GB/s",
+                                 counter_traffic("decode", w.name), hbm),
+        "compress": roofline_entry("hbm", w.compress_bytes() / (avg_us["compress"] * 1e-6) / 1e9,
+                                   HBM_PEAK_GBS, "GB/s", counter_traffic("compress", w.name),
+                                   ceil.get("hbm_read_gbs")),
+        "multi": roofline_entry("hbm", w.multi_bytes() / (avg_us["multi"] * 1e-6) / 1e9,
+                                HBM_PEAK_GBS, "GB/s", counter_traffic("multi", w.name), hbm),
+        "prefill": roofline_entry("mfma", pre_tflops, BF16_PEAK_TFLOPS, "TFLOP/s",
+                                  counter_traffic("prefill", w.name), mfma),
+        "reconstruct": roofline_entry("hbm", w.reconstruct_bytes() / (avg_us["reconstruct"] * 1e-6)
+                                      / 1e9, HBM_PEAK_GBS, "GB/s",
+                                      counter_traffic("reconstruct", w.name),
+                                      ceil.get("hbm_read_gbs")),
+    }
+    # Unfused A/B: the fused call against W_eff materialised by
+    # bitdelta_reconstruct and multiplied by the library GEMM (torch.mm on
+    # hipBLASLt), and against that GEMM alone on a stored W_eff.
+    rec_us = avg_us["reconstruct"]
+    unfused = {}
+    for m in list(w.decode_ms) + [w.prefill_m]:
+        key = f"decode_m{m}" if m in w.decode_ms else "prefill"
+        dense = avg_us[f"dense_m{m}"]
+        unfused[key] = {"tokens": m, "fused_us": round(avg_us[key], 3),
+                        "reconstruct_plus_gemm_us": round(rec_us + dense, 3),
+                        "gemm_on_stored_weff_us": round(dense, 3)}
+    print("[bench] proj_4096: delta-cache loads", file=sys.stderr, flush=True)
+    n16, g16 = t["range_graphs"]["decode_m16"]
+    delta_load = measure_delta_loads(g16, n16, avg_us["decode_m16"])
+    rec = {
+        "value": round(dec_gbs, 2), "unit": "GB/s",
+        "ms_per_step": round(t["step_ms"], 4), "ms_per_step_median": round(t["step_ms_median"], 4),
+        "config": {
+            "workload": "proj_4096: Llama-style 4096x4096 projection, bf16 W_base~N(0,0.02), "
+                        "Laplace(0,5e-4) delta, per-row alpha; step = compress W_ft + decode "
+                        "M=1,4,16 + 14-variant Zipf(1.1) decode M=16 + prefill M=2048",
+            "d_out": 4096, "d_in": 4096, "decode_tokens": list(w.decode_ms),
+            "multi_tokens": w.multi_m, "multi_variants": w.n_variants,
+            "multi_distinct_variants": w.distinct, "prefill_tokens": w.prefill_m,
+            "alpha_mode": "per_row", "rotation_copies": w.R,
+        },
+        "prefill_tflops": round(pre_tflops, 2),
+        "roofline": rooflines["decode"],
+        "roofline_by_kernel": rooflines,
+        "unfused_ab": unfused,
+        "kernel_us": {k: round(v, 3) for k, v in avg_us.items()},
+        "delta_load": delta_load,
+    }
+    return rec, w
+
+
+# ------------------------------------------------------------------ layers
+def sample_rows(d_out: int, k: int, seed: int) -> np.ndarray:
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return np.sort(rng.choice(d_out, size=min(k, d_out), replace=False))
+
+
+def _host_rows(t: torch.Tensor, rows):
+    return t[torch.as_tensor(rows, device=t.device)].cpu()
+
+
+def layer_samples(w, layer_ops, k: int, seed: int):
+    """Host copies of what the oracle needs for k sampled output rows of each
+    matrix (every output row depends on its weight row only): x, the rows of
+    W_base, their packed signs and alpha.  layer_ops: per matrix (x, W_base,
+    [packed per variant], [alpha per variant])."""
+    out = []
+    for i, (x, wb, packs, alphas) in enumerate(layer_ops):
+        d_out = wb.shape[0]
+        rows = sample_rows(d_out, k, seed + i)
+        out.append({
+            "x": S.bf16_bits(x), "wb": S.bf16_bits(_host_rows(wb, rows)),
+            "packs": [_host_rows(p, rows).numpy().view(np.uint64) for p in packs],
+            "alphas": [(_host_rows(a, rows) if w.mode == 1 else a.cpu()).numpy()
+                       for a in alphas],
+            "rows": len(rows), "d_in": wb.shape[1], "d_out": d_out})
+    return out
+
+
+def cpu_layer(kind, samples, mode, ids, budget_s: float, what: str):
+    """The oracle on the sampled rows, repeated while the budget lasts: prefill
+    in TFLOP/s (2*M*rows*d_in per matrix), mixed decode in GB/s (the rows'
+    share of the algorithmic bytes: W_base, the signs and alpha of every
+    variant present, x and y)."""
+    import oracle as O
+    work, t_all, passes = 0.0, 0.0, 0
+    distinct = len(set(int(v) for v in ids)) if ids is not None else 1
+    while True:
+        t0 = time.perf_counter()
+        for smp in samples:
+            r, d_in = smp["rows"], smp["d_in"]
+            m = smp["x"].shape[0]
+            if kind == "prefill":
+                O.linear(smp["x"], smp["wb"], smp["packs"][0], smp["alphas"][0], mode)
+                work += 2.0 * m * r * d_in
+            else:
+                O.linear_multi(smp["x"], ids, smp["wb"], smp["packs"], smp["alphas"], mode)
+                alpha = 4 * (r if mode == 1 else 1)
+                work += (2 * r * d_in + distinct * (r * d_in // 8 + alpha) + 2 * m * d_in
+                         + 2 * m * r + 4 * m)
+        t_all += time.perf_counter() - t0
+        passes += 1
+        if t_all > budget_s or passes >= 50:
+            break
+    scale, unit = (1e12, "TFLOP/s") if kind == "prefill" else (1e9, "GB/s")
+    rows = samples[0]["rows"]
+    return _cpu_record(round(work / t_all / scale, 5), unit,
+                       f"{what}: oracle on {rows} sampled output rows of each matrix, "
+                       f"{passes} pass(es), {t_all:.1f} s")
+
+
+def bench_layer(name, args, dev, ceil):
+    """One of the layer configurations (70B-shaped layer prefill, layer
+    mixed decode, the 80-layer stack's mixed decode): steps, each matrix's
+    launch duration, the roofline, and host samples for the oracle."""
+    t0 = time.perf_counter()
+    if name == "stack70b_multi":
+        w = StackWorkload(name, dev)
+    else:
+        w = LayerWorkload(name, dev)
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+    print(f"[bench] {name}: set up in {setup_s:.1f} s, distinct variants D={w.distinct}",
+          file=sys.stderr, flush=True)
+    t = time_workload(w, args)
+    rep = w.report(t["avg_us"], args, t["step_ms"])
+    measured = ceil.get("bf16_mfma_tflops") if w.kind == "prefill" else ceil.get("hbm_read_gbs")
+    rep["roofline"] = roofline_entry(rep["roofline"]["bound"], rep["value"],
+                                     rep["roofline"]["peak"], rep["roofline"]["unit"],
+                                     rep["roofline"]["traffic"], measured)
+    rep["ms_per_step"] = round(t["step_ms"], 4)
+    rep["ms_per_step_median"] = round(t["step_ms_median"], 4)
+    rep["kernel_us"] = {k: round(v, 3) for k, v in t["avg_us"].items()}
+    rep["setup_s"] = round(setup_s, 1)
+    # host samples for the oracle, taken before the device memory is freed
+    if name == "stack70b_multi":
+        layers = (0, w.wl.layers // 2, w.wl.layers - 1)
+        samples = []
+        for l in layers:
+            ops = [(w.xs[l][i], w.stack[l][i], [w.packs[l][v][i] for v in range(len(w.packs[l]))],
+                    [w.alphas[l][v][i] for v in range(len(w.alphas[l]))])
+                   for i in range(len(w.wl.matrices))]
+            samples += layer_samples(w, ops, 32, 1000 + 10 * l)
+        what = f"layers {list(layers)} of the 80-layer stack, M={w.m}"
+    else:
+        ops = [w.rot[i][0] for i in range(len(w.bases))]
+        samples = layer_samples(w, ops, 64 if w.kind == "prefill" else 128, 1000)
+        what = f"one 70B-shaped layer, M={w.m}"
+    ids = w.ids.cpu().numpy() if w.kind == "multi" else None
+    meta = {"kind": w.kind, "mode": w.mode, "ids": ids, "samples": samples, "what": what}
+    return rep, meta
+
+
+def free_device():
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+DEFAULT_CONFIGS = ("proj_4096", "layer70b_prefill", "layer70b_multi", "stack70b_multi")
+
+
+def run_default(args, dev):
+    """The default line: value is the decode figure of the projection (the
+    metric's decode configuration); the 70B-shaped layer's prefill gives the
+    metric's TFLOP/s; the layer's and the 80-layer stack's mixed-variant
+    decode are reported beside them, each with its roofline and the oracle on
+    a bounded sample."""
+    configs = [c for c in args.configs.split(",") if c]
+    for c in configs:
+        if c not in DEFAULT_CONFIGS:
+            raise SystemExit(f"unknown configuration {c}")
+    print("[bench] measuring ceilings", file=sys.stderr, flush=True)
+    ceil = measure_ceilings(dev)
+    print(f"[bench] ceilings {ceil}", file=sys.stderr, flush=True)
+    free_device()
+    recs, metas, proj_w = {}, {}, None
+    for c in configs:
+        print(f"[bench] setting up {c}", file=sys.stderr, flush=True)
+        if c == "proj_4096":
+            recs[c], proj_w = bench_proj(args, dev, ceil)
+            proj_host = proj_w.host
+            proj_meta = {"mode": proj_w.mode, "decode_ms": proj_w.decode_ms}
+            proj_w = None
+        else:
+            recs[c], metas[c] = bench_layer(c, args, dev, ceil)
+        free_device()
+    if args.cpu_budget > 0:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        if "proj_4096" in recs:
+            shell = ProjWorkload.__new__(ProjWorkload)
+            shell.host, shell.mode, shell.decode_ms = proj_host, proj_meta["mode"], \
+                proj_meta["decode_ms"]
+            shell.d_out = shell.d_in = 4096
+            recs["proj_4096"]["cpu_baseline"] = cpu_baseline(shell, args.cpu_budget)
+        for c, m in metas.items():
+            recs[c]["cpu_baseline"] = cpu_layer(m["kind"], m["samples"], m["mode"], m["ids"],
+                                                args.cpu_budget / 2, m["what"])
+    head = recs.get("proj_4096") or next(iter(recs.values()))
+    out = {
+        "metric": METRIC, "value": head["value"], "unit": head["unit"], "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic", "config": head["config"],
+        "roofline": head["roofline"], "cpu_baseline": head.get("cpu_baseline"),
+    }
+    if "layer70b_prefill" in recs:
+        r = recs["layer70b_prefill"]
+        out["prefill_tflops"] = r["value"]
+        out["prefill_roofline"] = r["roofline"]
+    if "layer70b_multi" in recs:
+        out["multi_layer_gbs"] = recs["layer70b_multi"]["value"]
+        out["multi_layer_roofline"] = recs["layer70b_multi"]["roofline"]
+    if "stack70b_multi" in recs:
+        out["multi_stack_gbs"] = recs["stack70b_multi"]["value"]
+        out["multi_stack_roofline"] = recs["stack70b_multi"]["roofline"]
+    out["ceilings"] = ceil
+    out["timing"] = (f"medians of {REPS} HIP-event-timed graph replays per kernel range "
+                     f"(each replay = back-to-back launches over distinct operand copies); "
+                     f"ms_per_step = mean of the K timed steps")
+    out["configs"] = recs
+    print(json.dumps(out), flush=True)
 
 
 def main():
@@ -972,12 +1329,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="proj_4096",
-                    choices=["proj_4096", "layer70b_prefill", "layer70b_multi",
+    ap.add_argument("--workload", default="default",
+                    choices=["default", "proj_4096", "layer70b_prefill", "layer70b_multi",
                              "layer70b_decode", "stack70b_multi", "serve_layer70b",
                              "monosoup_4096"])
-    ap.add_argument("--cpu-budget", type=float, default=12.0,
-                    help="seconds of oracle work for the cpu_baseline leg (0 skips it)")
+    ap.add_argument("--configs", default=",".join(DEFAULT_CONFIGS),
+                    help="configurations of the default line (comma-separated)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work for the projection's cpu_baseline leg (half "
+                         "that for each layer configuration; 0 skips them)")
     ap.add_argument("--counter-pass", action="store_true",
                     help="eager launches for a rocprofv3 --pmc run (proj_4096), then exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -1008,6 +1368,16 @@ def main():
         clock_pass(dev)
         print("[bench] clock pass done", file=sys.stderr, flush=True)
         return
+    if args.counter_pass:
+        w = ProjWorkload(dev)
+        torch.cuda.synchronize()
+        counter_pass(w, args.counter_launches)
+        print(f"[bench] counter pass done ({args.counter_launches} launches per kernel, "
+              f"D={w.distinct})", file=sys.stderr, flush=True)
+        return
+    if args.workload == "default":
+        run_default(args, dev)
+        return
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     if args.workload == "serve_layer70b":
         serve_layer70b(args, dev)
@@ -1015,170 +1385,21 @@ def main():
     if args.workload == "monosoup_4096":
         monosoup_4096(args, dev)
         return
-    if args.workload == "proj_4096":
-        w = ProjWorkload(dev)
-    elif args.workload == "stack70b_multi":
-        w = StackWorkload(args.workload, dev)
-    elif args.workload == "layer70b_decode":
+    if args.workload == "layer70b_decode":
         w = DecodeLayerWorkload(args.workload, dev)
-    else:
-        w = LayerWorkload(args.workload, dev)
-    torch.cuda.synchronize()
-    if args.counter_pass:
-        if not isinstance(w, ProjWorkload):
-            raise SystemExit("--counter-pass covers the proj_4096 workload")
-        counter_pass(w, args.counter_launches)
-        print(f"[bench] counter pass done ({args.counter_launches} launches per kernel, "
-              f"D={w.distinct})", file=sys.stderr, flush=True)
-        return
-    print(f"[bench] rotation copies R={w.R}, distinct variants in the mixed batch "
-          f"D={w.distinct}", file=sys.stderr, flush=True)
-
-    # Graphs: one per pass over distinct rotation copies (the steps), and
-    # one per kernel range holding back-to-back launches over the copies.
-    n_pass = max(1, w.R // 6)
-    passes = [capture(lambda j=j: w.one_pass(j)) for j in range(n_pass)]
-    range_graphs = {name: (n, capture(fn)) for name, (n, fn) in w.ranges().items()}
-    if isinstance(w, ProjWorkload):
-        # the graphs must reproduce eager results
-        w.run_decode(16, 0)
-        y_eager = w.ys[16].clone()
-        range_graphs["decode_m16"][1].replay()
         torch.cuda.synchronize()
-        w.run_decode(16, 0)
-        torch.cuda.synchronize()
-        assert torch.equal(w.ys[16], y_eager), "graph replay differs from eager launch"
-        # eager references of the unfused A/B outputs, checked again after
-        # every timed replay below
-        eager_ref = {}
-        for m in list(w.decode_ms) + [w.prefill_m]:
-            w.run_dense(m, 0)
-            eager_ref[f"dense_m{m}"] = (w.ys_dense[m], w.ys_dense[m].clone())
-        w.run_reconstruct(0)
-        eager_ref["reconstruct"] = (w.w_eff, w.w_eff.clone())
-        torch.cuda.synchronize()
-    for _ in range(args.warmup):
-        passes[_ % n_pass].replay()
-    torch.cuda.synchronize()
-    print(f"[bench] graphs captured ({n_pass} passes, {len(range_graphs)} ranges)",
-          file=sys.stderr, flush=True)
-
-    # Timed region 1: K steps, each one pass of the path.
-    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step_ev[i][0].record()
-        passes[i % n_pass].replay()
-        step_ev[i][1].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    step_ms = sum(s.elapsed_time(e) for s, e in step_ev) / args.steps
-    # Timed region 2: each kernel range, back-to-back launches, HIP events
-    # around each replay -> average launch duration per kernel.
-    avg_us = {}
-    for name, (n, g) in range_graphs.items():
-        g.replay()
-        avg_us[name] = 1e3 * time_replays(g, max(3, args.steps // 4)) / n
-        if isinstance(w, ProjWorkload) and name in eager_ref:
-            buf, ref = eager_ref[name]
-            assert torch.equal(buf.view(torch.int16), ref.view(torch.int16)), (
-                f"graph replays of {name} differ from the eager launch")
-    print(f"[bench] timed {args.steps} steps in {wall:.3f} s "
-          f"(GPU {step_ms:.3f} ms per step)", file=sys.stderr, flush=True)
-
-    if not isinstance(w, ProjWorkload):
-        rep = w.report(avg_us, args, step_ms)
-        out = {"metric": METRIC, "value": rep["value"], "unit": rep["unit"], "n_gpus": 1,
-               "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_ms, 4),
-               "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-               "dtype": "bf16", "data": "synthetic", "config": rep["config"],
-               "per_matrix": rep["per_matrix"], "layer_us": rep["layer_us"],
-               **({"dense_base_ab": rep["dense_base_ab"]} if "dense_base_ab" in rep else {}),
-               "value_per_step": rep.get("value_per_step"),
-               **({"stack_ms": rep["stack_ms"]} if "stack_ms" in rep else {}),
-               "roofline": rep["roofline"],
-               "kernel_avg_us": {k: round(v, 3) for k, v in avg_us.items()},
-               "cpu_baseline": None}
+        t = time_workload(w, args)
+        rep = w.report(t["avg_us"], args, t["step_ms"])
+        rep["kernel_us"] = {k: round(v, 3) for k, v in t["avg_us"].items()}
+        out = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+               "ms_per_step": round(t["step_ms"], 4), "higher_is_better": True,
+               "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+               **rep, "cpu_baseline": None}
         print(json.dumps(out), flush=True)
         return
-
-    dec_bytes = sum(w.decode_bytes(m) for m in w.decode_ms)
-    dec_us = sum(avg_us[f"decode_m{m}"] for m in w.decode_ms)
-    dec_gbs = dec_bytes / (dec_us * 1e-6) / 1e9
-    pre_us = avg_us["prefill"]
-    pre_tflops = w.prefill_flops() / (pre_us * 1e-6) / 1e12
-    comp_us = avg_us["compress"]
-    multi_us = avg_us["multi"]
-
-    rooflines = {
-        "decode": roofline_entry("hbm", dec_gbs, HBM_PEAK_GBS, "GB/s",
-                                 counter_traffic("decode", w.name)),
-        "compress": roofline_entry("hbm", w.compress_bytes() / (comp_us * 1e-6) / 1e9,
-                                   HBM_PEAK_GBS, "GB/s", counter_traffic("compress", w.name)),
-        "multi": roofline_entry("hbm", w.multi_bytes() / (multi_us * 1e-6) / 1e9,
-                                HBM_PEAK_GBS, "GB/s", counter_traffic("multi", w.name)),
-        "prefill": roofline_entry("mfma", pre_tflops, BF16_PEAK_TFLOPS, "TFLOP/s",
-                                  counter_traffic("prefill", w.name)),
-        "reconstruct": roofline_entry("hbm", w.reconstruct_bytes() / (avg_us["reconstruct"] * 1e-6)
-                                      / 1e9, HBM_PEAK_GBS, "GB/s",
-                                      counter_traffic("reconstruct", w.name)),
-    }
-    # Unfused A/B: the fused call against W_eff materialised by
-    # bitdelta_reconstruct and multiplied by the library GEMM (torch.mm on
-    # hipBLASLt), and against that GEMM alone on a stored W_eff (a dense bf16
-    # layer of the same shape, no BitDelta at all).
-    rec_us = avg_us["reconstruct"]
-    unfused = {}
-    for m in list(w.decode_ms) + [w.prefill_m]:
-        key = f"decode_m{m}" if m in w.decode_ms else "prefill"
-        dense = avg_us[f"dense_m{m}"]
-        unfused[key] = {"tokens": m, "fused_us": round(avg_us[key], 3),
-                        "reconstruct_plus_gemm_us": round(rec_us + dense, 3),
-                        "gemm_on_stored_weff_us": round(dense, 3)}
-    kernel_us = {name: round(v, 3) for name, v in avg_us.items()}
-
-    print("[bench] delta-cache loads", file=sys.stderr, flush=True)
-    n16, g16 = range_graphs["decode_m16"]
-    delta_load = measure_delta_loads(g16, n16, avg_us["decode_m16"])
-
-    cpu = None
-    if args.cpu_budget > 0:
-        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(w, args.cpu_budget)
-
-    out = {
-        "metric": METRIC,
-        "value": round(dec_gbs, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(step_ms, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": "proj_4096: Llama-style 4096x4096 projection, bf16 W_base~N(0,0.02), "
-                        "Laplace(0,5e-4) delta, per-row alpha; step = compress W_ft + decode "
-                        "M=1,4,16 + 14-variant Zipf(1.1) decode M=16 + prefill M=2048",
-            "d_out": 4096, "d_in": 4096, "decode_tokens": list(w.decode_ms),
-            "multi_tokens": w.multi_m, "multi_variants": w.n_variants,
-            "multi_distinct_variants": w.distinct, "prefill_tokens": w.prefill_m,
-            "alpha_mode": "per_row", "rotation_copies": w.R,
-        },
-        "prefill_tflops": round(pre_tflops, 2),
-        "roofline": rooflines["decode"],
-        "roofline_by_kernel": rooflines,
-        "unfused_ab": unfused,
-        "kernel_avg_us": kernel_us,
-        "delta_load": delta_load,
-        "cpu_baseline": cpu,
-    }
-    print(json.dumps(out), flush=True)
+    # one configuration of the default line alone
+    args.configs = args.workload
+    run_default(args, dev)
 
 
 if __name__ == "__main__":
