@@ -29,6 +29,9 @@
 // block past a wave's range re-reads the wave's last block and is skipped;
 // lanes of a final 64-wide block that fall past d_in re-read valid data whose
 // x is then zeroed.
+#include <cstdlib>
+#include <cstring>
+
 #include "common.h"
 #include "internal.h"
 
@@ -52,6 +55,29 @@ __device__ __forceinline__ void sign_pairs(uint32_t bits, uint32_t (&s)[16]) {
     s[i] = __builtin_amdgcn_bitop3_b32(zl << (15 - 2 * i), 0x80008000u, 0x3F803F80u, 0xEA);
     s[i + 8] = __builtin_amdgcn_bitop3_b32(zh << (15 - 2 * i), 0x80008000u, 0x3F803F80u, 0xEA);
   }
+}
+
+// The same operand built one MFMA step at a time: spread_signs gives the two
+// spread words, step_signs the four dwords of step q (elements 8q..8q+7).
+struct Spread {
+  uint32_t zl, zh;
+};
+
+__device__ __forceinline__ Spread spread_signs(uint32_t bits) {
+  Spread z;
+  z.zl = __builtin_amdgcn_bitop3_b32(bits, bits << 15, 0x00005555u, 0x1B);
+  z.zh = __builtin_amdgcn_bitop3_b32(bits >> 16, bits >> 1, 0x00005555u, 0x1B);
+  return z;
+}
+
+__device__ __forceinline__ u32x4 step_signs(const Spread& z, int q) {
+  const uint32_t w = q < 2 ? z.zl : z.zh;
+  const int i0 = 4 * (q & 1);
+  u32x4 v;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    v[k] = __builtin_amdgcn_bitop3_b32(w << (15 - 2 * (i0 + k)), 0x80008000u, 0x3F803F80u, 0xEA);
+  return v;
 }
 
 __device__ __forceinline__ u32x4 quad(const uint32_t (&s)[16], int q) {
@@ -468,6 +494,391 @@ __global__ __launch_bounds__(NW * kWave) void linear_multi_kernel(const SkinnyAr
   }
 }
 
+// ---------------------------------------------------------------- mixed batch, pairs
+// Grouping of a mixed batch by (tile, variant) pairs, built once per
+// workgroup in LDS.  Tokens are ordered by variant id (stable): slot s holds
+// token perm[s] of variant slotv[s] (-1 base only, -2 invalid id), and the
+// slots form 16-token tiles (slot s in tile s / 16).  var[0..nvar) are the
+// distinct valid variants present, in increasing order.  A pair is one
+// variant present in one tile: pair p covers the slots of tile pt[p] that
+// hold variant var[pj[p]].  Pairs are listed in slot order, so from one pair
+// to the next the tile and the variant index never decrease.
+template <int NS>  // slots: M <= NS
+struct PairGroups {
+  int perm[NS];
+  int slotv[NS];
+  int key[NS];
+  int flag[NS];
+  int var[NS];
+  int pt[NS];
+  int pj[NS];
+  int nvar, npair;
+};
+
+template <int NS>
+__device__ void build_pairs(PairGroups<NS>& G, const int32_t* ids, int M, int n_variants) {
+  const int t = threadIdx.x;
+  if (t < M) {
+    const int v = ids[t];
+    // order: variants 0..V-1, then base-only tokens, then invalid ids
+    G.key[t] = (v >= 0 && v < n_variants) ? v : (v == -1 ? n_variants : n_variants + 1);
+  }
+  __syncthreads();
+  if (t < M) {
+    const int k = G.key[t];
+    int rank = 0;
+    for (int u = 0; u < M; ++u) {
+      const int ku = G.key[u];
+      rank += (ku < k || (ku == k && u < t)) ? 1 : 0;
+    }
+    G.perm[rank] = t;
+    G.slotv[rank] = k < n_variants ? k : (k == n_variants ? -1 : -2);
+  }
+  __syncthreads();
+  // key[s] = 1 where slot s starts a variant's run, flag[s] = 1 where it
+  // starts a pair (the start of a run, or a tile boundary inside one)
+  int v = -3;
+  if (t < M) {
+    v = G.slotv[t];
+    const bool prev_same = t > 0 && G.slotv[t - 1] == v;
+    G.key[t] = (v >= 0 && !prev_same) ? 1 : 0;
+    G.flag[t] = (v >= 0 && (!prev_same || (t & 15) == 0)) ? 1 : 0;
+  }
+  __syncthreads();
+  if (t < M && v >= 0) {
+    int j = -1, p = 0;
+    for (int u = 0; u <= t; ++u) j += G.key[u];
+    for (int u = 0; u < t; ++u) p += G.flag[u];
+    if (G.key[t]) G.var[j] = v;
+    if (G.flag[t]) {
+      G.pt[p] = t >> 4;
+      G.pj[p] = j;
+    }
+  }
+  if (t == 0) {
+    int nv = 0, np = 0;
+    for (int u = 0; u < M; ++u) {
+      nv += G.key[u];
+      np += G.flag[u];
+    }
+    G.nvar = nv;
+    G.npair = np;
+  }
+  __syncthreads();
+}
+
+// The base product runs once for all tokens on 16-token tiles; the sign
+// product once per pair: x of the pair's tile times the +-1 operand of the
+// pair's variant, into the pair's own accumulator.  Rows of a tile that
+// belong to other variants get products that are never read.  The tile's x
+// operand is read from LDS once per tile change and the +-1 operand is built
+// once per variant change (both only move forward along the pair list).
+// Pairs are taken KP at a time; a batch after the first re-streams x and the
+// sign words of its pairs but not W_base.
+//
+// Work split: a workgroup owns 16 output rows; its NW waves take the
+// 128-wide blocks of d_in round-robin and their partial sums are added in
+// LDS in a fixed order.  Lane (n, g) holds elements 32g..32g+31 of the block
+// of row n (W_base and sign bits) and of token n of each tile (x).  Per
+// block, a wave stages its block of x for the MT*16 slots in its own LDS
+// region (buffer loads straight to LDS, 4 rows of 256 bytes per
+// instruction; chunk c of row r at c ^ (r % 16), so operand reads of 16
+// consecutive rows at one chunk hit distinct banks), and the weights and
+// sign words of its next block are requested before the current block is
+// multiplied.  The sign rows of the pairs' variants are looked up once per
+// batch, outside the loop over blocks.
+template <int MT, int NW, int KP, bool WLDS, int WPE>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void
+linear_multi_pairs_kernel(const SkinnyArgs a) {
+  constexpr int kXRows = MT * 16;
+  constexpr int kXRowB = 256;                  // bytes per staged row (128 bf16)
+  constexpr int kXWave = (kXRows + (WLDS ? 16 : 0)) * kXRowB;  // x rows, then 16 W_base rows
+  constexpr int kXBytes = NW * kXWave;
+  constexpr int kRedChunk = 8;                 // f32x4 per lane and wave reduced at once
+  constexpr int kRedBytes = NW * kRedChunk * 4 * kWave * 4;
+  constexpr int kDma = MT * 4;                 // 4-row staging instructions per block
+  constexpr int kSmem = kRedBytes > kXBytes ? kRedBytes : kXBytes;
+  static_assert(MT <= kRedChunk, "base tiles reduce in one chunk");
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  __shared__ PairGroups<kXRows> G;
+  __shared__ float sw_slot[kXRows][16];
+  __shared__ float ss_slot[kXRows][16];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int d_in = a.d_in;
+  const int M = a.M;
+  char* xs = smem + wv * kXWave;
+  char* ws = xs + kXRows * kXRowB;  // the wave's 16 rows of W_base for one block
+  float* red = reinterpret_cast<float*>(smem);
+
+  build_pairs(G, a.ids, M, a.n_variants);
+  const int npair = G.npair;
+  const int nbatch = max((npair + KP - 1) / KP, 1);  // one pass at least, for the base
+  // Pair and variant tables, lane p holding entry p.
+  const int pt_l = lane < npair ? G.pt[lane] : 0;
+  const int pj_l = lane < npair ? G.pj[lane] : -1;
+
+  // Staging: instruction j writes slot rows 4j..4j+3; lane (lane/16,
+  // c = lane%16) fetches chunk c ^ (row % 16) of the row's token (slots past
+  // M re-read the last token; their outputs are never stored).  Byte offsets
+  // into x at the first block.
+  const int xbytes = M * d_in * 2;
+  int xoff[kDma];
+#pragma unroll
+  for (int j = 0; j < kDma; ++j) {
+    const int r = 4 * j + (lane >> 4);
+    xoff[j] = G.perm[min(r, M - 1)] * d_in * 2 + (((lane & 15) ^ (r & 15)) << 4);
+  }
+  // Operand reads: tile t, k-step q, lane (n, g) reads chunk 4g+q of slot
+  // row 16t+n (whose swizzle key is n).
+  int foff[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) foff[q] = (((4 * g + q) ^ n) << 4);
+
+  const int row0 = blockIdx.x * 16;
+  const int nrows = min(16, a.d_out - row0);
+  const uint16_t* wblk = a.w + (size_t)row0 * d_in;
+  const int wbytes = nrows * d_in * 2;
+  // W_base staging (WLDS), like x: instruction j writes rows 4j..4j+3 of
+  // the block, lane (lane/16, c = lane%16) fetching chunk c ^ row of its row
+  // (rows past d_out re-read the last row).  Byte offsets at the first
+  // block.  Without WLDS the lane loads its own 64 bytes in operand layout.
+  const int woff = (min(n, nrows - 1) * d_in + (g << 5)) * 2;  // + 2*k0 per block
+  int wdoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * j + (lane >> 4);
+    wdoff[j] = min(r, nrows - 1) * d_in * 2 + (((lane & 15) ^ r) << 4);
+  }
+  // Sign words are loaded with four lanes per row (lane 4r + j reads dword
+  // j of row r's 16 bytes of the block: every quad of lanes reads one
+  // contiguous piece, which the address unit serves four times faster than
+  // the operand layout), then moved to the operand layout (lane n + 16g
+  // holds dword g of row n) by one cross-lane permute.
+  const uint32_t srow = min(lane >> 2, nrows - 1) * (d_in >> 3);
+  const int sj = (lane & 3) << 2;
+  const int perm_src = ((n << 2) + g) << 2;            // byte address of the source lane
+  const size_t prow = (size_t)row0 * (d_in >> 3);      // this workgroup's rows in a packed matrix
+
+  const int nblk = (d_in + 127) >> 7;
+  const int nmine = blocks_of_wave(wv, nblk, NW);
+  const bool half_tail = (d_in & 127) != 0;
+
+  f32x4 accw[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) accw[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int batch = 0; batch < nbatch; ++batch) {
+    const int p0 = batch * KP;
+    const int np = min(KP, npair - p0);  // pairs in the batch (<= 0: none)
+    // Lane u: the sign rows (this workgroup's) of pair p0+u's variant.
+    const uint8_t* stab = nullptr;
+    if (lane < np) {
+      const int vv = G.var[G.pj[p0 + lane]];
+      stab = reinterpret_cast<const uint8_t*>(a.packed[vv]) + prow;
+    }
+    const uint64_t stab_u = reinterpret_cast<uint64_t>(stab);
+    const uint32_t stab_lo = (uint32_t)stab_u, stab_hi = (uint32_t)(stab_u >> 32);
+    // Pair u builds a +-1 operand (and so needs its sign words) when it
+    // starts a new variant; otherwise it reuses the previous pair's.
+    const int jprev_l = __shfl_up(pj_l, 1, kWave);
+    const uint64_t builds = __builtin_amdgcn_ballot_w64(
+        lane >= p0 && lane < p0 + np && (lane == p0 || pj_l != jprev_l));
+
+    f32x4 acc[KP];
+#pragma unroll
+    for (int u = 0; u < KP; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    uint32_t sc[KP];
+    u32x4 wc[4];
+    auto stage_w = [&](int i) {
+      const int k0 = (wv + NW * i) << 7;
+      if (WLDS) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) lds_bload16(wblk, wbytes, wdoff[j], 2 * k0, ws + j * 1024);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wc[q] = bload128(wblk, wbytes, woff + 16 * q, 2 * k0);
+      }
+    };
+    auto load_s1 = [&](int i, int u) {
+      // dword sj/4 of the row's 16 sign bytes of block wv + NW*i; in a final
+      // 64-wide block dwords 2 and 3 re-read the row's last 4 bytes (never
+      // past the row)
+      const uint32_t off = srow + min(((wv + NW * i) << 4) + sj, (d_in >> 3) - 4);
+      const uint64_t b = ((uint64_t)__builtin_amdgcn_readlane(stab_hi, u) << 32) |
+                         (uint32_t)__builtin_amdgcn_readlane(stab_lo, u);
+      sc[u] = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(b + off);
+    };
+    auto stage_x = [&](int i) {
+      const int k0 = (wv + NW * i) << 7;
+#pragma unroll
+      for (int j = 0; j < kDma; ++j) lds_bload16(a.x, xbytes, xoff[j], 2 * k0, xs + j * 1024);
+    };
+    if (nmine > 0) {
+      stage_x(0);
+      if (batch == 0) stage_w(0);
+#pragma unroll
+      for (int u = 0; u < KP; ++u)
+        if ((builds >> (p0 + u)) & 1) load_s1(0, u);
+    }
+    for (int i = 0; i < nmine; ++i) {
+      __builtin_amdgcn_s_waitcnt(0);  // x staged, weights and sign words of block i
+      const bool more = i + 1 < nmine;
+      if (half_tail && wv + NW * i == nblk - 1) {
+        // a final 64-wide block: its columns 64..127 do not exist (the
+        // staging read other bytes there): zero them in every slot row, so
+        // that they add nothing whatever the weights and signs read there
+        for (int e = lane; e < kXRows * 8; e += kWave) {
+          const int r = e >> 3;
+          const int cg = 8 + (e & 7);
+          *reinterpret_cast<u32x4*>(xs + r * kXRowB + ((cg ^ (r & 15)) << 4)) =
+              u32x4{0u, 0u, 0u, 0u};
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      }
+      u32x4 xw[4];
+      auto read_x = [&](int t) {
+        const char* src = xs + (16 * t + n) * kXRowB;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) xw[q] = *reinterpret_cast<const u32x4*>(src + foff[q]);
+      };
+      // The next block's W_base goes into the W stage once this block's has
+      // been read, and each sign word into its register right after its last
+      // use (the last block re-reads itself: no register load depends on a
+      // condition, which would make the compiler wait for it before the
+      // merge).
+      const int inext = more ? i + 1 : i;
+      // this block's sign words into the operand layout
+#pragma unroll
+      for (int u = 0; u < KP; ++u)
+        if ((builds >> (p0 + u)) & 1) sc[u] = __builtin_amdgcn_ds_bpermute(perm_src, sc[u]);
+      int tcur = -1;
+      if (batch == 0) {
+        u32x4 wf[4];
+        if (WLDS) {
+          const char* src = ws + n * kXRowB;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) wf[q] = *reinterpret_cast<const u32x4*>(src + foff[q]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) wf[q] = wc[q];
+        }
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          read_x(t);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) accw[t] = mfma16(xw[q], wf[q], accw[t]);
+        }
+        tcur = MT - 1;
+        if (WLDS) {
+          if (more) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the W stage has been read
+            stage_w(inext);
+          }
+        } else {
+          stage_w(inext);  // wc is free again
+        }
+      }
+      Spread sz;
+#pragma unroll
+      for (int u = 0; u < KP; ++u) {
+        if (u < np) {
+          const int t = __builtin_amdgcn_readlane(pt_l, p0 + u);
+          if (t != tcur) {
+            tcur = t;
+            read_x(t);
+          }
+          if ((builds >> (p0 + u)) & 1) {
+            sz = spread_signs(sc[u]);
+            // keep the reload of sc[u] after its last read, so that it lands
+            // in the same register with no copy (and no wait for the copy)
+            __builtin_amdgcn_sched_barrier(0);
+            load_s1(inext, u);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[u] = mfma16(xw[q], step_signs(sz, q), acc[u]);
+        }
+      }
+      if (more) {
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this block's LDS reads are done
+        stage_x(i + 1);
+      }
+    }
+
+    // Sign sums of the batch's pairs: add the waves' partials in a fixed
+    // order and file each under the slots of its tile that hold its
+    // variant.  MFMA 16x16 output layout: lane l holds tile rows
+    // 4*(l/16)+v of output column l%16.
+#pragma unroll
+    for (int c0 = 0; c0 < KP; c0 += kRedChunk) {
+      __syncthreads();  // staging (or the previous chunk) no longer read
+#pragma unroll
+      for (int c = 0; c < kRedChunk; ++c)
+        if (c0 + c < KP)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            red[((wv * kRedChunk + c) * 4 + v) * kWave + lane] = acc[min(c0 + c, KP - 1)][v];
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < kRedChunk * 4 * kWave; idx += NW * kWave) {
+        const int l = idx & (kWave - 1);
+        const int v = (idx >> 6) & 3;
+        const int c = idx >> 8;
+        const int u = c0 + c;
+        if (u < KP && u < np) {
+          float ss = 0.f;
+#pragma unroll
+          for (int k = 0; k < NW; ++k) ss += red[((k * kRedChunk + c) * 4 + v) * kWave + l];
+          const int slot = 16 * G.pt[p0 + u] + 4 * (l >> 4) + v;
+          if (slot < M && G.slotv[slot] == G.var[G.pj[p0 + u]]) ss_slot[slot][l & 15] = ss;
+        }
+      }
+    }
+    if (batch == 0) {
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) red[((wv * kRedChunk + t) * 4 + v) * kWave + lane] = accw[t][v];
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < MT * 4 * kWave; idx += NW * kWave) {
+        const int l = idx & (kWave - 1);
+        const int v = (idx >> 6) & 3;
+        const int t = idx >> 8;
+        float sw = 0.f;
+#pragma unroll
+        for (int k = 0; k < NW; ++k) sw += red[((k * kRedChunk + t) * 4 + v) * kWave + l];
+        const int slot = 16 * t + 4 * (l >> 4) + v;
+        if (slot < M) sw_slot[slot][l & 15] = sw;
+      }
+    }
+    __syncthreads();  // the reduction area is the next batch's staging
+  }
+
+  const int per_row = a.per_row;
+  for (int idx = threadIdx.x; idx < M * 16; idx += NW * kWave) {
+    const int slot = idx >> 4;
+    const int ol = idx & 15;
+    const int o = row0 + ol;
+    if (o < a.d_out) {
+      const int m = G.perm[slot];
+      const int vv = G.slotv[slot];
+      const float sw = sw_slot[slot][ol];
+      float yv;
+      if (vv >= 0) {
+        const float* ap = a.alpha[vv];
+        yv = sw + (per_row ? ap[o] : ap[0]) * ss_slot[slot][ol];
+      } else {
+        yv = vv == -1 ? sw : __builtin_nanf("");
+      }
+      a.y[(size_t)m * a.d_out + o] = f32_to_bf16_bits(yv);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- launchers
 constexpr int kNW = 8;
 
@@ -485,6 +896,23 @@ hipError_t launch_multi(const SkinnyArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int MT, int NW, int KP, bool WLDS, int WPE>
+hipError_t launch_multi_pairs(const SkinnyArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((linear_multi_pairs_kernel<MT, NW, KP, WLDS, WPE>), dim3((a.d_out + 15) / 16),
+                     dim3(NW * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+// Which mixed-batch kernel runs: pairs (default) or windows, from
+// BITDELTA_MULTI_KERNEL, read once (for A/B measurements).
+bool multi_use_windows() {
+  static const bool w = [] {
+    const char* e = std::getenv("BITDELTA_MULTI_KERNEL");
+    return e != nullptr && std::strcmp(e, "windows") == 0;
+  }();
+  return w;
+}
+
 }  // namespace
 
 hipError_t launch_linear_skinny(const SkinnyArgs& a, hipStream_t stream) {
@@ -497,9 +925,23 @@ hipError_t launch_linear_skinny(const SkinnyArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_linear_multi(const SkinnyArgs& a, hipStream_t stream) {
-  if (a.M <= 16) return launch_multi<1>(a, stream);
-  if (a.M <= 32) return launch_multi<2>(a, stream);
-  return launch_multi<4>(a, stream);
+  if (multi_use_windows()) {
+    if (a.M <= 16) return launch_multi<1>(a, stream);
+    if (a.M <= 32) return launch_multi<2>(a, stream);
+    return launch_multi<4>(a, stream);
+  }
+  // Four waves per workgroup (three workgroups per CU) where there are
+  // enough 16-row groups to fill the CUs that way (at least 1.5 per CU);
+  // eight otherwise (measured: 28672 x 8192 at 32 tokens 246 against 265 us,
+  // 8192 x 8192 76 us; 4096 x 4096 at 16 tokens 25.0 against 21.8 us).
+  const bool wide = (a.d_out + 15) / 16 >= 384;
+  if (a.M <= 16)
+    return wide ? launch_multi_pairs<1, 4, 12, true, 3>(a, stream)
+                : launch_multi_pairs<1, 8, 12, true, 2>(a, stream);
+  if (a.M <= 32)
+    return wide ? launch_multi_pairs<2, 4, 12, true, 3>(a, stream)
+                : launch_multi_pairs<2, 8, 12, true, 2>(a, stream);
+  return launch_multi_pairs<4, 8, 20, false, 2>(a, stream);
 }
 
 }  // namespace bd

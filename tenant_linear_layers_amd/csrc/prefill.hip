@@ -43,39 +43,6 @@ constexpr int ABLK = 1152;          // bytes per 8-row block of the x stage (1 K
 constexpr int A_STAGE = 32 * ABLK;  // 256 rows
 constexpr int LDK = BK + 8;         // weight stage row pitch in bf16 (144 bytes)
 
-// Buffer loads through a resource spanning [base, base + nbytes): offsets
-// past the end read as zero.
-__device__ __forceinline__ u32x4 bload128(const void* base, int nbytes, int voff, int soff) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-
-__device__ __forceinline__ uint32_t bload32(const void* base, int nbytes, int voff, int soff) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
-  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-}
-
-__device__ __forceinline__ uint32_t bload8(const void* base, int nbytes, int voff, int soff) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
-  return __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
-}
-
-// 16 bytes per lane through a buffer resource straight into LDS: lane i's
-// bytes land at lds + 16*i (lds must be the same for the whole wave).  A
-// buffer load rather than a global one: the compiler then counts these loads
-// in order with the weight loads and can wait for exactly the ones a step
-// needs (with global-to-LDS loads pending it falls back to waiting for all).
-__device__ __forceinline__ void lds_bload16(const void* base, int nbytes, int voff, int soff,
-                                            void* lds) {
-  const __amdgpu_buffer_rsrc_t r =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, nbytes, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, soff, 0, 0);
-}
-
 // Workgroup barrier without a memory fence.  Callers first wait for their
 // own loads and LDS stores, which is what makes the LDS contents visible; the
 // memory clobber keeps the compiler from moving memory accesses across the

@@ -392,6 +392,45 @@ def test_multi_more_distinct_variants_than_prefetched(shape):
     assert_y_close(y, _multi_ref(x, idt, wb, packs, alphas, 1), f"multi 40 variants {shape}")
 
 
+def _pattern_ids(kind, m):
+    """Variant-id patterns that exercise how a batch is cut into (16-token
+    tile, variant) pairs."""
+    rng = np.random.default_rng(len(kind) + m)
+    if kind == "long_run":       # one variant's run spans several tiles
+        ids = np.concatenate([np.full(40, 3), np.full(10, 0), np.full(6, -1),
+                              np.arange(4, 12)])[:m]
+    elif kind == "base_tile":    # a whole tile of base-only tokens between variants
+        ids = np.concatenate([np.full(8, 1), np.full(16, -1), np.arange(2, 10), np.full(16, 5),
+                              np.arange(6, 22)])[:m]
+    elif kind == "all_base":
+        ids = np.full(m, -1)
+    elif kind == "all_invalid":
+        ids = np.full(m, 99)
+    elif kind == "distinct":     # every token its own variant (one pair per token)
+        ids = np.arange(m) % 20
+    else:
+        raise ValueError(kind)
+    ids = ids.astype(np.int32)
+    rng.shuffle(ids)
+    return ids
+
+
+@pytest.mark.parametrize("kind", ["long_run", "base_tile", "all_base", "all_invalid", "distinct"])
+@pytest.mark.parametrize("m", [48, 64])
+def test_multi_pair_patterns(kind, m):
+    mode = m % 2
+    wb, packs, alphas = _variants(300, 320, 20, seed=90 + m, mode=mode)
+    ids = _pattern_ids(kind, m)
+    x = S.draw_activations(m, 320, S.generator(91 + m)).to(DEV)
+    idt = torch.from_numpy(ids).to(DEV)
+    y = T.linear_multi(x, idt, wb, packs, alphas, mode)
+    ref = _multi_ref(x, idt, wb, packs, alphas, mode)
+    if kind == "all_invalid":
+        assert bool(torch.isnan(y.float()).all())
+        return
+    assert_y_close(y, ref, f"multi pairs {kind} M={m}")
+
+
 # ---------------------------------------------------------------- workloads 3, 4
 def _sample_rows(d_out, k, seed):
     rng = np.random.default_rng(seed)
