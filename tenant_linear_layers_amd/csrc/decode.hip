@@ -208,6 +208,249 @@ __global__ __launch_bounds__(NW * kWave) void linear_decode_kernel(const SkinnyA
                            });
 }
 
+// ---------------------------------------------------------------- one variant, LDS ring
+// The same product for M <= 16 with every load coalesced: the address unit
+// serves a load whose lanes read contiguous 64-byte pieces four at a time
+// (each quad of lanes in one piece) about four times faster than one in the
+// MFMA operand layout, where every quad of lanes spans four rows.  So
+// W_base and x reach LDS by buffer loads to LDS (4 rows of 256 bytes per
+// instruction, chunk c of row r at c ^ (r % 16)) and are read back in the
+// operand layout; the sign words are loaded four lanes per row and moved to
+// the operand layout by one cross-lane permute.
+//
+// Each wave owns a ring of U stages (W_base rows of its block, then the x
+// rows); the loads of block i + U - 1 are issued before block i is
+// multiplied, with a constant count of loads per block, so one vmcnt wait
+// finds block i complete.  XD: 4-row x staging instructions per 16-token tile
+// (tokens past M re-read the last token; their outputs are never stored).
+template <int XD, int NW, int U>
+__global__ __launch_bounds__(NW * kWave) void linear_decode_ring_kernel(const SkinnyArgs a) {
+  constexpr int kXR = 4 * XD;                    // staged x rows
+  constexpr int kStage = (16 + kXR) * 256;       // W_base rows, then x rows
+  constexpr int kLoads = 4 + XD + 1;             // vector loads per block
+  constexpr int kRed = NW * 2 * 4 * kWave * 4;   // reduction area (bytes)
+  constexpr int kSmem = NW * U * kStage > kRed ? NW * U * kStage : kRed;
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int row0 = blockIdx.x * 16;
+  const int nrows = min(16, a.d_out - row0);
+  const int d_in = a.d_in;
+  const int M = a.M;
+  char* ring = smem + wv * U * kStage;
+
+  // DMA sources, byte offsets at the first block: W_base rows 4j..4j+3 and
+  // x rows 4j..4j+3 per instruction, lane (lane/16, c = lane%16) fetching
+  // chunk c ^ row.
+  const uint16_t* wblk = a.w + (size_t)row0 * d_in;
+  const int wbytes = nrows * d_in * 2;
+  const int xbytes = M * d_in * 2;
+  int wdoff[4], xdoff[XD];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * j + (lane >> 4);
+    wdoff[j] = min(r, nrows - 1) * d_in * 2 + (((lane & 15) ^ r) << 4);
+  }
+#pragma unroll
+  for (int j = 0; j < XD; ++j) {
+    const int r = 4 * j + (lane >> 4);
+    xdoff[j] = min(r, M - 1) * d_in * 2 + (((lane & 15) ^ r) << 4);
+  }
+  // Sign words: lane 4r + j loads dword j of row r's 16 bytes of the block.
+  const uint8_t* sblk = reinterpret_cast<const uint8_t*>(a.packed[0]) + (size_t)row0 * (d_in >> 3);
+  const uint32_t srow = min(lane >> 2, nrows - 1) * (d_in >> 3);
+  const int sj = (lane & 3) << 2;
+  const int perm_src = ((n << 2) + g) << 2;
+  // Operand reads: W row n, x row min(n, kXR - 1), chunk 4g + q.
+  const int xr = min(n, kXR - 1);
+  int wro[4], xro[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    wro[q] = n * 256 + (((4 * g + q) ^ n) << 4);
+    xro[q] = (16 + xr) * 256 + (((4 * g + q) ^ xr) << 4);
+  }
+
+  const int nblk = (d_in + 127) >> 7;
+  const int nmine = blocks_of_wave(wv, nblk, NW);
+  const bool half_tail = (d_in & 127) != 0;
+
+  uint32_t sreg[U];
+  auto issue = [&](int i, int u) {
+    const int k0 = (wv + NW * i) << 7;
+    char* st = ring + u * kStage;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lds_bload16(wblk, wbytes, wdoff[j], 2 * k0, st + j * 1024);
+#pragma unroll
+    for (int j = 0; j < XD; ++j) lds_bload16(a.x, xbytes, xdoff[j], 2 * k0, st + (16 + 4 * j) * 256);
+    const uint32_t off = srow + min((k0 >> 3) + sj, (d_in >> 3) - 4);
+    sreg[u] = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(
+        reinterpret_cast<uintptr_t>(sblk + off));
+  };
+
+  f32x4 accw = {0.f, 0.f, 0.f, 0.f}, accs = {0.f, 0.f, 0.f, 0.f};
+  if (nmine > 0) {
+#pragma unroll
+    for (int u = 0; u < U - 1; ++u) issue(min(u, nmine - 1), u);
+  }
+  for (int i0 = 0; i0 < nmine; i0 += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = i0 + u;
+      // past the wave's last block the issue re-reads that block into a stage
+      // nobody reads: every block issues the same number of loads
+      issue(min(i + U - 1, nmine - 1), (u + U - 1) % U);
+      __builtin_amdgcn_s_waitcnt(((kLoads * (U - 1)) & 15) | (((kLoads * (U - 1)) >> 4) << 14) |
+                                 (0x7 << 4) | (0xF << 8));  // vmcnt only
+      if (i < nmine) {  // uniform
+        char* st = ring + u * kStage;
+        if (half_tail && wv + NW * i == nblk - 1) {
+          // a final 64-wide block: zero x's columns 64..127 (read from other bytes)
+          for (int e = lane; e < kXR * 8; e += kWave) {
+            const int r = e >> 3;
+            const int cg = 8 + (e & 7);
+            *reinterpret_cast<u32x4*>(st + (16 + r) * 256 + ((cg ^ r) << 4)) =
+                u32x4{0u, 0u, 0u, 0u};
+          }
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        }
+        const uint32_t bits = __builtin_amdgcn_ds_bpermute(perm_src, sreg[u]);
+        const Spread z = spread_signs(bits);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4 wf = *reinterpret_cast<const u32x4*>(st + wro[q]);
+          const u32x4 xf = *reinterpret_cast<const u32x4*>(st + xro[q]);
+          accw = mfma16(xf, wf, accw);
+          accs = mfma16(xf, step_signs(z, q), accs);
+        }
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // the ring becomes the reduction area
+
+  float* red = reinterpret_cast<float*>(smem);
+  const f32x4 aw[1] = {accw}, as[1] = {accs};
+  const float* alpha = a.alpha[0];
+  const int per_row = a.per_row;
+  reduce_and_store<1, NW>(red, aw, as, row0, M, a.d_out, a.y,
+                          [&](int slot, int o, float sw, float ss, int& m) {
+                            m = slot;
+                            return sw + (per_row ? alpha[o] : alpha[0]) * ss;
+                          });
+}
+
+// ---------------------------------------------------------------- one variant, VALU
+// The same product for M <= MM <= 4 on the vector ALUs (no matrix cores):
+// a workgroup owns 4 output rows and its NW waves take the 128-wide blocks
+// of d_in round-robin.  Lane (r = lane/16, c = lane%16) reads 16 bytes of
+// W_base row r per block (4 rows of 256 contiguous bytes per load), the
+// sign byte of those 8 elements (its quad shares one 4-byte word) and 16
+// bytes of each token's x.  Per element: W_base widened to float32 and one
+// FMA per token for the base sum; for the sign sum x's sign bit is flipped
+// where the sign is -1 (a select by bitop3 on the shifted sign bits) and
+// added.  Partial sums are reduced over the 16 lanes of a row by DPP row
+// shifts and over the waves in LDS in a fixed order; alpha is applied once.
+template <int MM, int NW, int UB>
+__global__ __launch_bounds__(NW * kWave) void linear_decode_valu_kernel(const SkinnyArgs a) {
+  __shared__ float red[NW][2 * MM][4];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane >> 4;
+  const int c = lane & 15;
+  const int d_in = a.d_in;
+  const int M = a.M;
+  const int row0 = blockIdx.x * 4;
+  const int row = min(row0 + r, a.d_out - 1);
+  const uint16_t* wrow = a.w + (size_t)row * d_in;
+  const uint8_t* srow = reinterpret_cast<const uint8_t*>(a.packed[0]) + (size_t)row * (d_in >> 3);
+  const uint16_t* xrow[MM];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) xrow[m] = a.x + (size_t)min(m, M - 1) * d_in;
+  const int sbyte = (c & 3) << 3;  // bit offset of the lane's byte in its word
+
+  float aw[MM], as[MM];
+#pragma unroll
+  for (int m = 0; m < MM; ++m) aw[m] = as[m] = 0.f;
+
+  const int nblk = (d_in + 127) >> 7;
+  const int nmine = blocks_of_wave(wv, nblk, NW);
+  const bool half_tail = (d_in & 127) != 0;
+  for (int i0 = 0; i0 < nmine; i0 += UB) {
+    u32x4 wv4[UB], xv[UB][MM];
+    uint32_t sw[UB];
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      // loads are never predicated: past the wave's blocks, and past d_in in
+      // a final 64-wide block, they re-read valid bytes that are then skipped
+      const int b = wv + NW * min(i0 + u, nmine - 1);
+      const int e = min((b << 7) + 8 * c, d_in - 8);  // the lane's first element
+      wv4[u] = ld128(wrow + e);
+#pragma unroll
+      for (int m = 0; m < MM; ++m) xv[u][m] = ld128(xrow[m] + e);
+      sw[u] = ld32(srow + ((e >> 3) & ~3));
+    }
+#pragma unroll
+    for (int u = 0; u < UB; ++u) {
+      if (i0 + u >= nmine) continue;  // uniform
+      const int b = wv + NW * (i0 + u);
+      const bool skip = half_tail && b == nblk - 1 && 8 * c >= 64;
+      const uint32_t nb = ~(sw[u] >> sbyte);  // bit j set: element j is -1
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t wd = wv4[u][j >> 1];
+        const float w = __uint_as_float((j & 1) ? (wd & 0xFFFF0000u) : (wd << 16));
+        const uint32_t neg = nb << (31 - j);
+#pragma unroll
+        for (int m = 0; m < MM; ++m) {
+          const uint32_t xd = xv[u][m][j >> 1];
+          const uint32_t xb = (j & 1) ? (xd & 0xFFFF0000u) : (xd << 16);
+          const float x = skip ? 0.f : __uint_as_float(xb);
+          aw[m] = __builtin_fmaf(w, x, aw[m]);
+          // x with its sign bit flipped where the sign is -1 (bitop3 0x78: a ^ (b & c))
+          as[m] += __uint_as_float(
+              __builtin_amdgcn_bitop3_b32(__float_as_uint(x), neg, 0x80000000u, 0x78));
+        }
+      }
+    }
+  }
+  // reduce over the 16 lanes of each row (DPP row shifts keep within a row)
+#pragma unroll
+  for (int m = 0; m < MM; ++m) {
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) {
+      aw[m] += __shfl_xor(aw[m], off, 16);
+      as[m] += __shfl_xor(as[m], off, 16);
+    }
+  }
+  if (c == 0) {
+#pragma unroll
+    for (int m = 0; m < MM; ++m) {
+      red[wv][2 * m][r] = aw[m];
+      red[wv][2 * m + 1][r] = as[m];
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < MM * 4) {
+    const int m = threadIdx.x >> 2;
+    const int rr = threadIdx.x & 3;
+    const int o = row0 + rr;
+    if (m < M && o < a.d_out) {
+      float sw_ = 0.f, ss = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        sw_ += red[w][2 * m][rr];
+        ss += red[w][2 * m + 1][rr];
+      }
+      const float* alpha = a.alpha[0];
+      a.y[(size_t)m * a.d_out + o] = f32_to_bf16_bits(sw_ + (a.per_row ? alpha[o] : alpha[0]) * ss);
+    }
+  }
+}
+
 // ---------------------------------------------------------------- mixed batch
 // Grouping of a mixed batch by variant, built once per workgroup in LDS.
 // Tokens are ordered by variant id (stable); slot s of the sorted order holds
@@ -889,6 +1132,34 @@ hipError_t launch_decode(const SkinnyArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Environment switches for A/B measurements of alternative kernels, read at
+// every call (a lookup is far cheaper than a launch).
+bool env_is(const char* name, const char* value) {
+  const char* e = std::getenv(name);
+  return e != nullptr && std::strcmp(e, value) == 0;
+}
+
+template <int MM, int NW, int UB>
+hipError_t launch_decode_valu(const SkinnyArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((linear_decode_valu_kernel<MM, NW, UB>), dim3((a.d_out + 3) / 4),
+                     dim3(NW * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+// The vector-ALU GEMV for M <= 4 (BITDELTA_DECODE_KERNEL=valu).
+bool decode_use_valu() { return env_is("BITDELTA_DECODE_KERNEL", "valu"); }
+
+template <int XD, int NW, int U>
+hipError_t launch_decode_ring(const SkinnyArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((linear_decode_ring_kernel<XD, NW, U>), dim3((a.d_out + 15) / 16),
+                     dim3(NW * kWave), 0, stream, a);
+  return hipGetLastError();
+}
+
+// The earlier decode kernel (operand-layout loads) for every M
+// (BITDELTA_DECODE_KERNEL=operand).
+bool decode_use_old() { return env_is("BITDELTA_DECODE_KERNEL", "operand"); }
+
 template <int MT>
 hipError_t launch_multi(const SkinnyArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((linear_multi_kernel<MT, kNW>), dim3((a.d_out + 15) / 16), dim3(kNW * kWave), 0,
@@ -903,19 +1174,26 @@ hipError_t launch_multi_pairs(const SkinnyArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Which mixed-batch kernel runs: pairs (default) or windows, from
-// BITDELTA_MULTI_KERNEL, read once (for A/B measurements).
-bool multi_use_windows() {
-  static const bool w = [] {
-    const char* e = std::getenv("BITDELTA_MULTI_KERNEL");
-    return e != nullptr && std::strcmp(e, "windows") == 0;
-  }();
-  return w;
-}
+// Which mixed-batch kernel runs: pairs (default) or windows
+// (BITDELTA_MULTI_KERNEL=windows).
+bool multi_use_windows() { return env_is("BITDELTA_MULTI_KERNEL", "windows"); }
 
 }  // namespace
 
 hipError_t launch_linear_skinny(const SkinnyArgs& a, hipStream_t stream) {
+  if (decode_use_valu() && a.M <= 4) {
+    if (a.M == 1) return launch_decode_valu<1, 4, 16>(a, stream);
+    if (a.M == 2) return launch_decode_valu<2, 4, 4>(a, stream);
+    return launch_decode_valu<4, 4, 4>(a, stream);
+  }
+  // Ring stages: two up to 8 tokens (80 and 96 KB of LDS per workgroup),
+  // one for 16 (64 KB: two workgroups per CU), measured on 4096 x 4096,
+  // 28672 x 8192 and 8192 x 28672.
+  if (!decode_use_old() && a.M <= 16) {
+    if (a.M <= 4) return launch_decode_ring<1, 8, 2>(a, stream);
+    if (a.M <= 8) return launch_decode_ring<2, 8, 2>(a, stream);
+    return launch_decode_ring<4, 8, 1>(a, stream);
+  }
   // Blocks in flight per wave: 4 for a single token, 2 up to 32 tokens (the
   // x loads grow with the tiles), 1 beyond (measured on 4096x4096).
   if (a.M == 1) return launch_decode<1, 4>(a, stream);
