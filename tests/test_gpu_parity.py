@@ -392,6 +392,23 @@ def test_multi_more_distinct_variants_than_prefetched(shape):
     assert_y_close(y, _multi_ref(x, idt, wb, packs, alphas, 1), f"multi 40 variants {shape}")
 
 
+@pytest.mark.parametrize("shape", [(12345, 192), (24600, 128)])
+@pytest.mark.parametrize("m", [20, 32])
+def test_multi_many_row_groups_full_output(shape, m):
+    """More 16-row groups than the GPU holds at once (772 and 1538, the last
+    one ragged), with a base-only token: y starts as NaN and every output is
+    compared."""
+    mode = m % 2
+    wb, packs, alphas = _variants(*shape, 9, seed=95 + m, mode=mode)
+    ids = S.zipf_ids(m, 9, seed=96 + m)
+    ids[0] = -1
+    x = S.draw_activations(m, shape[1], S.generator(97 + m)).to(DEV)
+    idt = torch.from_numpy(ids).to(DEV)
+    y = torch.full((m, shape[0]), float("nan"), dtype=torch.bfloat16, device=DEV)
+    T.linear_multi(x, idt, wb, packs, alphas, mode, y=y)
+    assert_y_close(y, _multi_ref(x, idt, wb, packs, alphas, mode), f"multi rounds {shape} M={m}")
+
+
 def _pattern_ids(kind, m):
     """Variant-id patterns that exercise how a batch is cut into (16-token
     tile, variant) pairs."""
