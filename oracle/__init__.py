@@ -31,7 +31,7 @@ from .bitdelta_oracle import (  # noqa: F401
     f32_to_bf16_bits,
     fixed_point_scope_sums,
     linear,
-    linear_dense,
+    linear_by_element,
     linear_multi,
     pack_sign_bits,
     reconstruct,

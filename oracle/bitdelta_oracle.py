@@ -205,17 +205,28 @@ def linear(x_bits, w_base_bits, packed, alpha, alpha_mode: int) -> np.ndarray:
     return x @ w.T + (x @ s.T) * a[None, :]
 
 
-def linear_dense(x_bits, w_base_bits, packed, alpha, alpha_mode: int) -> np.ndarray:
-    """Same product through a materialised dense W_eff = W_base + alpha*S in
-    float64, the way the page's conceptual kernel states it.  Used as a
-    cross-check of ``linear`` on small shapes."""
+def linear_by_element(x_bits, w_base_bits, packed, alpha, alpha_mode: int) -> np.ndarray:
+    """The product straight from its definition, one output at a time:
+    y[m, o] = sum_i x[m, i] * W_eff[o, i], where W_eff[o, i] is W_base[o, i]
+    plus alpha_o when bit (i mod 64) of word i/64 of row o is set and minus
+    alpha_o when it is clear (page: section "Matematiksel temel", the
+    approximation of W_ft; section "Altyapı ayrıntıları", the bit layout).
+    Reads each sign from its packed word directly and sums in float64.  Slow
+    (Python loops over m and o): a cross-check of ``linear`` on tiny shapes."""
     x = bf16_bits_to_f32(x_bits).astype(np.float64)
     w = bf16_bits_to_f32(w_base_bits).astype(np.float64)
-    d_out, d_in = w.shape
-    s = unpack_sign_bits(packed, d_in).astype(np.float64)
+    words = np.asarray(packed, dtype=np.uint64)
+    m_rows, d_in = x.shape
+    d_out = w.shape[0]
     a = _alpha_per_output(alpha, d_out, alpha_mode)
-    w_eff = w + a[:, None] * s
-    return x @ w_eff.T
+    cols = np.arange(d_in)
+    y = np.zeros((m_rows, d_out), dtype=np.float64)
+    for o in range(d_out):
+        bit = (words[o, cols // 64] >> (cols % 64).astype(np.uint64)) & np.uint64(1)
+        w_eff = w[o] + np.where(bit == 1, a[o], -a[o])
+        for m in range(m_rows):
+            y[m, o] = float(np.sum(x[m] * w_eff))
+    return y
 
 
 def f32_to_bf16_bits(f) -> np.ndarray:

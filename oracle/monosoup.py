@@ -5,10 +5,9 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).  Plain numpy in
 float64.
 
 Page "BitDelta: Tek bir GPU kümesinden 14 Zen modeli sunmak", section
-"MonoSoup" (the merge listing and the paragraph after it): for checkpoints
-W_1 .. W_k of one base, each task vector Delta_i = W_i - W_base is replaced by
-its best rank-r approximation tau_i (a truncated SVD), and the merged weight
-is W_base + (1/k) * sum_i tau_i.
+"MonoSoup": for checkpoints W_1 .. W_k of one base, each task vector
+Delta_i = W_i - W_base is replaced by its best rank-r approximation tau_i (a
+truncated SVD), and the merged weight is W_base + (1/k) * sum_i tau_i.
 
 Readings taken:
 

@@ -262,10 +262,10 @@ def _linear_case(m, d_out, d_in, seed, mode):
 
 
 @pytest.mark.parametrize("mode", [0, 1])
-def test_split_form_equals_dense_weff(mode):
+def test_split_form_equals_sum_by_element(mode):
     x, wb, _, packed, alpha = _linear_case(5, 48, 192, 7, mode)
     y = O.linear(x, wb, packed, alpha, mode)
-    yd = O.linear_dense(x, wb, packed, alpha, mode)
+    yd = O.linear_by_element(x, wb, packed, alpha, mode)
     np.testing.assert_allclose(y, yd, rtol=1e-12, atol=1e-14)
 
 
@@ -361,7 +361,7 @@ def test_multi_rows_match_single_token_calls_and_permute():
         if v < 0:
             np.testing.assert_array_equal(y[m], base[m])
         else:
-            ref = O.linear_dense(x[m:m + 1], wb, packs[v], alphas[v], 1)[0]
+            ref = O.linear_by_element(x[m:m + 1], wb, packs[v], alphas[v], 1)[0]
             np.testing.assert_allclose(y[m], ref, rtol=1e-12, atol=1e-14)
     perm = np.array([3, 0, 6, 5, 1, 4, 2])
     yp = O.linear_multi(x[perm], ids[perm], wb, packs, alphas, 1)
