@@ -367,10 +367,29 @@ __global__ __launch_bounds__(64 * (WM * WN + 4), 1) void prefill_pc_kernel(
     // With XPF, one dword of each of the tile's 512 x rows two steps ahead
     // is loaded as well, which brings those 128-byte segments into L2 a step
     // before they are staged (for x too large to stay in the last-level
-    // cache).  The loaded values only feed a dummy sum.
+    // cache).  The loaded values only feed a dummy sum.  The S workgroups of
+    // this XCD that stream the same token tile (S a power of two, at most 8)
+    // share the work: workgroup i loads rows i, i + S, i + 2S, ... (every
+    // line is requested once per L2 instead of S times, and each scattered
+    // row costs the address unit several cycles).  Threads with no row of
+    // their own read past the end of the buffer, which touches no memory.
+    int share = 1, sidx = 0;
+    if (xg == 1) {
+      if (chunk % ntm == 0) {
+        share = chunk / ntm;
+        sidx = local / ntm;
+      }
+    } else {
+      share = ntn / (8 / xg);
+      sidx = local / (ntm / xg);
+    }
+    int S = 1;
+    while (S < 8 && 2 * S <= share) S *= 2;
+    const int npf = TBM / S;  // rows this workgroup prefetches
     uint32_t sink = 0, pf0 = 0, pf1 = 0;
-    const int pfv0 = 2 * T * d_in * 2;
-    const int pfv1 = (2 * T + 1) * d_in * 2;
+    const int pfv0 = S == 1 ? 2 * T * d_in * 2
+                            : (T < npf ? (S * T + sidx % S) * d_in * 2 : xbytes);
+    const int pfv1 = S == 1 ? (2 * T + 1) * d_in * 2 : xbytes;
     // Step kt: x of step kt+1 into the free x stage, raw weights of step
     // kt+2 into rb_load, W_eff of step kt+1 (rb_use, loaded a step earlier)
     // into the free weight stage; the barrier waits for x and the LDS
