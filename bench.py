@@ -30,18 +30,23 @@ layer of the same shape, no BitDelta at all).  Their graphs are checked
 against eager launches after each timed range.
 
 Counter runs (HBM traffic per launch, rocprofv3 FETCH_SIZE and WRITE_SIZE in
-two separate runs):
+two separate runs), for W = proj_4096, layer70b_multi or layer70b_prefill:
 
-    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT_F -o run -- python bench.py --counter-pass
-    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT_W -o run -- python bench.py --counter-pass
-    python bench.py --summarize-counters OUT_F OUT_W
+    rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT_F -o run -- python bench.py --counter-pass --workload W
+    rocprofv3 --pmc WRITE_SIZE --output-format csv -d OUT_W -o run -- python bench.py --counter-pass --workload W
+    python bench.py --summarize-counters OUT_F OUT_W --workload W
 
-`--counter-pass` launches each kernel of the proj_4096 step eagerly, in a fixed
-order, on distinct rotation copies, then a plain elementwise kernel that reads
-and writes a known 256 MiB (the calibration: the counters read a fixed fraction
-of the true bytes).  `--summarize-counters` scales the per-dispatch counters by
-that calibration and writes profiles/<kernel>_proj_4096_pmc.json (with a digest
-of the kernel's sources: a later change of the kernel voids the figure).
+`--counter-pass` launches each kernel of the workload (for a layer, each of
+its five linears) eagerly, block by block, each launch on its own rotation
+copy, then a plain elementwise kernel that reads and writes a known 256 MiB
+(the calibration: the counters read a fixed fraction of the true bytes).
+`--summarize-counters` scales the per-dispatch counters by that calibration
+and writes profiles/<kernel>_<W>_pmc.json (with a digest of the kernel's
+sources: a later change of the kernel voids the figure) and
+profiles/counters_<W>.md.  `--summarize-pmc DIR...` turns --pmc runs of the
+same pass with other counters (waves, waits, VALU/MFMA/TA busy, LDS) into
+profiles/sq_counters_<W>.md, and `--summarize-trace DIR NAME COMMAND` a
+--kernel-trace --stats run into profiles/NAME_kernel_trace.md.
 """
 
 from __future__ import annotations
@@ -356,6 +361,33 @@ class LayerWorkload:
         x, wb, _, _ = self.rot[i][c % len(self.rot[i])]
         torch.mm(x, wb.t(), out=self.ys_dense[i])
 
+    def setup_per_variant(self):
+        """The per-variant fused alternative for the mixed batch: the tokens
+        of each variant present gathered, one single-variant fused call
+        (bitdelta_linear: W_base + alpha_v sign(Delta_v) formed in the
+        kernel, W_base read again for every variant), the outputs scattered
+        back."""
+        ids = self.ids.cpu().numpy()
+        self.groups = [(v, torch.from_numpy(np.nonzero(ids == v)[0]).to(self.dev))
+                       for v in sorted(set(ids.tolist())) if v >= 0]
+        if any(v < 0 for v in ids.tolist()):
+            raise SystemExit("the per-variant comparison takes variant tokens only")
+        self.ys_pv = [torch.empty_like(y) for y in self.ys]
+        self.pv_bufs = {}
+        for i, (_, d_out, d_in) in enumerate(self.wl.matrices):
+            for v, idx in self.groups:
+                self.pv_bufs[(i, v)] = (
+                    torch.empty(len(idx), d_in, dtype=torch.bfloat16, device=self.dev),
+                    torch.empty(len(idx), d_out, dtype=torch.bfloat16, device=self.dev))
+
+    def run_per_variant(self, i, c=0):
+        x, wb, packs, alphas = self.rot[i][c % len(self.rot[i])]
+        for v, idx in self.groups:
+            xv, yv = self.pv_bufs[(i, v)]
+            torch.index_select(x, 0, idx, out=xv)
+            T.linear(xv, wb, packs[v], alphas[v], self.mode, y=yv)
+            self.ys_pv[i].index_copy_(0, idx, yv)
+
     def one_pass(self, j):
         for i in range(len(self.bases)):
             self.run(i)
@@ -366,6 +398,9 @@ class LayerWorkload:
             n = len(self.rot[i]) * RANGE_CYCLES
             out[f"{self.kind}_{nm}"] = (n, lambda i=i, n=n: [self.run(i, c) for c in range(n)])
             out[f"dense_{nm}"] = (n, lambda i=i, n=n: [self.run_dense(i, c) for c in range(n)])
+            if getattr(self, "groups", None) is not None:
+                out[f"pervar_{nm}"] = (n, lambda i=i, n=n: [self.run_per_variant(i, c)
+                                                            for c in range(n)])
         return out
 
     def work(self, i):
@@ -410,6 +445,24 @@ class LayerWorkload:
                                        "dense_base": round(dense[nm], 2)} for nm in names},
                 "layer_fused_us": round(total_us, 2), "layer_dense_base_us": round(d_tot, 2),
                 "fused_over_dense_base": round(total_us / d_tot, 4)}
+        if all(f"pervar_{nm}" in avg_us for nm in names):
+            # the per-variant fused alternative on the same batch
+            pv = {nm: avg_us[f"pervar_{nm}"] for nm in names}
+            for i in range(len(names)):
+                self.run(i)
+                self.run_per_variant(i)
+            torch.cuda.synchronize()
+            rel = max(float(((self.ys_pv[i].float() - self.ys[i].float()).abs().max()
+                             / self.ys[i].float().abs().max()).item())
+                      for i in range(len(names)))
+            out["per_variant_ab"] = {
+                "per_matrix_us": {nm: {"grouped": round(avg_us[f"{self.kind}_{nm}"], 2),
+                                       "per_variant": round(pv[nm], 2)} for nm in names},
+                "layer_grouped_us": round(total_us, 2),
+                "layer_per_variant_us": round(sum(pv.values()), 2),
+                "per_variant_over_grouped": round(sum(pv.values()) / total_us, 4),
+                "variant_calls_per_matrix": len(self.groups),
+                "max_abs_diff_over_max_abs": rel}
         if step_ms:
             # the same work over the measured one-pass steps (launch gaps and
             # the matrices' order included)
@@ -742,16 +795,55 @@ def cpu_baseline(w: ProjWorkload, budget_s: float):
 
 
 # ------------------------------------------------------------------ counters
-COUNTER_BLOCKS = ("compress", "decode_m1", "decode_m4", "decode_m16", "multi", "prefill",
-                  "reconstruct")
+COUNTER_WORKLOADS = ("proj_4096", "layer70b_multi", "layer70b_prefill")
 CALIB_BYTES = 256 * 2**20
-LIB_KERNELS = ("compress_rows_kernel", "compress_finalize_kernel", "linear_decode_kernel",
-               "linear_multi_kernel", "prefill_kernel", "prefill_pc_kernel", "reconstruct_kernel")
-# kernel name that every launch of a counter block must carry
-BLOCK_KERNEL = {"compress": "compress_rows_kernel", "decode_m1": "linear_decode_kernel",
-                "decode_m4": "linear_decode_kernel", "decode_m16": "linear_decode_kernel",
-                "multi": "linear_multi_kernel", "prefill": "prefill_",
-                "reconstruct": "reconstruct_kernel"}
+# kernel-name substring that every launch of a counter block must carry
+KERNEL_OF = {"compress": "compress_rows_kernel", "decode": "linear_decode_",
+             "multi": "linear_multi_", "prefill": "prefill_", "reconstruct": "reconstruct_kernel"}
+
+
+def layer_work_static(name: str):
+    """Per matrix of a layer workload: (label, algorithmic bytes per launch),
+    from the shapes and seeded variant ids alone (no GPU needed).  A mixed
+    decode launch reads W_base once and each distinct variant's signs and
+    alpha once; a prefill launch reads x, W_base, the signs and alpha and
+    writes y."""
+    wl = S.WORKLOADS[name]
+    m = wl.tokens[0]
+    out = []
+    for nm, d_out, d_in in wl.matrices:
+        n = d_out * d_in
+        alpha = 4 * (d_out if wl.alpha_mode == 1 else 1)
+        if name == "layer70b_prefill":
+            out.append((f"prefill_{nm}", 2 * n + n // 8 + alpha + 2 * m * d_in + 2 * m * d_out))
+        else:
+            ids = S.zipf_ids(m, wl.n_variants, wl.seed)
+            distinct = len(set(ids.tolist()))
+            out.append((f"multi_{nm}", 2 * n + distinct * (n // 8 + alpha) + 2 * m * d_in
+                        + 2 * m * d_out + 4 * m))
+    return out
+
+
+def counter_plan(workload: str):
+    """Blocks of a counter pass: [(block, kernel family, algorithmic bytes per
+    launch)], and how blocks group into one roofline unit per kernel family:
+    {family: (blocks, unit)}."""
+    if workload == "proj_4096":
+        sb = ProjWorkload.static_bytes()
+        blocks = [(b, b.split("_")[0], sb[b]) for b in
+                  ("compress", "decode_m1", "decode_m4", "decode_m16", "multi", "prefill",
+                   "reconstruct")]
+        groups = {"decode": (["decode_m1", "decode_m4", "decode_m16"],
+                             "one launch of each decode token count (M = 1, 4, 16), as the "
+                             "decode roofline's unit")}
+        for f in ("compress", "multi", "prefill", "reconstruct"):
+            groups[f] = ([f], "one launch")
+        return blocks, groups
+    fam = "prefill" if workload == "layer70b_prefill" else "multi"
+    blocks = [(b, fam, v) for b, v in layer_work_static(workload)]
+    return blocks, {fam: ([b for b, _, _ in blocks],
+                          "one pass of the layer's five linears (one launch each), as the "
+                          "layer roofline's unit")}
 
 
 def clock_pass(dev, n: int = 6):
@@ -775,18 +867,36 @@ def clock_pass(dev, n: int = 6):
     torch.cuda.synchronize()
 
 
-def counter_pass(w: ProjWorkload, n: int):
-    """n eager launches of each kernel of the step, block by block, each on its
-    own rotation copy; then n launches of the calibration kernel."""
-    run = {"compress": w.run_compress, "multi": w.run_multi, "prefill": w.run_prefill,
-           "reconstruct": w.run_reconstruct}
-    for m in w.decode_ms:
-        run[f"decode_m{m}"] = lambda r, m=m: w.run_decode(m, r)
-    for name in COUNTER_BLOCKS:
+SEPARATOR_KERNEL = "FillFunctor<unsigned char>"
+CALIB_KERNEL = "neg_kernel"
+
+
+def counter_pass(workload: str, dev, n: int):
+    """n eager calls of each block of the workload, block by block, each call
+    on its own rotation copy of the operands; then n launches of the
+    calibration kernel (a plain elementwise kernel reading and writing
+    CALIB_BYTES each).  A one-byte fill separates the blocks (a call may make
+    more than one launch), and one comes before the first."""
+    if workload == "proj_4096":
+        w = ProjWorkload(dev)
+        run = {"compress": w.run_compress, "multi": w.run_multi, "prefill": w.run_prefill,
+               "reconstruct": w.run_reconstruct}
+        for m in w.decode_ms:
+            run[f"decode_m{m}"] = lambda r, m=m: w.run_decode(m, r)
+    else:
+        w = LayerWorkload(workload, dev)
+        run = {f"{w.kind}_{nm}": (lambda r, i=i: w.run(i, r))
+               for i, (nm, _, _) in enumerate(w.wl.matrices)}
+    blocks, _ = counter_plan(workload)
+    sep = torch.empty(1, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    sep.fill_(0)
+    for b, (name, _, _) in enumerate(blocks):
         for r in range(n):
             run[name](r)
+        sep.fill_(b + 1)
         torch.cuda.synchronize()
-    src = torch.zeros(CALIB_BYTES // 2, dtype=torch.bfloat16, device=w.dev)
+    src = torch.zeros(CALIB_BYTES // 2, dtype=torch.bfloat16, device=dev)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     for _ in range(n):
@@ -794,82 +904,221 @@ def counter_pass(w: ProjWorkload, n: int):
     torch.cuda.synchronize()
 
 
-def _counter_rows(d: str, counter: str):
+def _counter_rows(d: str):
+    """(dispatch id, kernel name, counter, value) of every row of a --pmc run."""
     import csv
     rows = []
     for dirpath, _, files in os.walk(d):
         for f in files:
             if f.endswith("counter_collection.csv"):
                 for r in csv.DictReader(open(os.path.join(dirpath, f))):
-                    if r["Counter_Name"] == counter:
-                        rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"],
-                                     float(r["Counter_Value"])))
+                    rows.append((int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"],
+                                 float(r["Counter_Value"])))
     rows.sort()
     return rows
 
 
-def summarize_counters(fetch_dir: str, write_dir: str, n: int, w_bytes: dict):
-    """Per-launch HBM bytes of each kernel from the two counter runs."""
+def _split_blocks(d: str, workload: str, n: int):
+    """Per-dispatch counter values of a counter-pass run, cut into its blocks
+    at the separators and summed per call: ({block: [{counter: value} per
+    call]}, [calibration launches], calibration kernel name).  Raises when a
+    block holds a kernel of another family or a launch count that n calls
+    cannot make."""
+    blocks, _ = counter_plan(workload)
+    per = {}
+    names = {}
+    for did, kname, c, v in _counter_rows(d):
+        per.setdefault(did, {})
+        per[did][c] = per[did].get(c, 0.0) + v
+        names[did] = kname
+    ids = sorted(per)
+    seps = [i for i in ids if SEPARATOR_KERNEL in names[i]][-(len(blocks) + 1):]
+    if len(seps) != len(blocks) + 1:
+        raise SystemExit(f"{d}: expected {len(blocks) + 1} separators, found {len(seps)}")
+    calib = [i for i in ids if i > seps[-1]][-n:]
+    if len(calib) != n or any(CALIB_KERNEL not in names[i] for i in calib):
+        raise SystemExit(f"{d}: expected {n} calibration dispatches ({CALIB_KERNEL}) after "
+                         f"the last separator")
     out = {}
+    for b, (name, fam, _) in enumerate(blocks):
+        chunk = [i for i in ids if seps[b] < i < seps[b + 1]]
+        wrong = [names[i] for i in chunk if KERNEL_OF[fam] not in names[i]]
+        if wrong:
+            raise SystemExit(f"{d}: block {name} holds other kernels: {wrong[0][:80]}")
+        if not chunk or len(chunk) % n:
+            raise SystemExit(f"{d}: block {name} holds {len(chunk)} launches for {n} calls")
+        k = len(chunk) // n
+        counters = per[chunk[0]].keys()
+        out[name] = [{c: sum(per[i][c] for i in chunk[j * k:(j + 1) * k]) for c in counters}
+                     for j in range(n)]
+        out[name + "#kernel"] = sorted({_short_kernel(names[i]) for i in chunk})
+    return out, [per[i] for i in calib], names[calib[0]]
+
+
+def _short_kernel(name: str) -> str:
+    name = name.replace("void ", "").replace("bd::(anonymous namespace)::", "")
+    return name.split("(")[0]
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, workload: str, n: int):
+    """Per-launch HBM bytes of each block from the two counter runs, each
+    counter scaled by the calibration kernel's true bytes over its counted
+    bytes."""
+    blocks, _ = counter_plan(workload)
+    res = {name: {"algorithmic_bytes": v} for name, _, v in blocks}
     per = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        rows = _counter_rows(d, counter)
-        lib = [r for r in rows if any(k in r[1] for k in LIB_KERNELS)]
-        lib = lib[-n * len(COUNTER_BLOCKS):]
-        calib = [r for r in rows if r[0] > lib[-1][0]][-n:]
-        if len(lib) != n * len(COUNTER_BLOCKS) or len(calib) != n:
-            raise SystemExit(f"{counter}: expected {n} launches per block, found "
-                             f"{len(lib)} library and {len(calib)} calibration dispatches")
-        factor = CALIB_BYTES / (1024.0 * sum(v for _, _, v in calib) / n)
-        per[counter] = {"factor": factor, "calib_kernel": calib[0][1][:80]}
-        for b, name in enumerate(COUNTER_BLOCKS):
-            block = lib[b * n:(b + 1) * n]
-            wrong = [k for _, k, _ in block if BLOCK_KERNEL[name] not in k]
-            if wrong:
-                raise SystemExit(f"{counter}: block {name} holds other kernels: {wrong[0][:80]}")
-            vals = [v for _, _, v in block]
-            out.setdefault(name, {})[counter] = sum(vals) / n
-    res = {}
-    for name, c in out.items():
-        hbm = (c["FETCH_SIZE"] * 1024 * per["FETCH_SIZE"]["factor"]
-               + c["WRITE_SIZE"] * 1024 * per["WRITE_SIZE"]["factor"])
-        res[name] = {"fetch_kib": round(c["FETCH_SIZE"], 1), "write_kib": round(c["WRITE_SIZE"], 1),
-                     "hbm_bytes": round(hbm), "algorithmic_bytes": w_bytes[name]}
+        got, calib, ck = _split_blocks(d, workload, n)
+        factor = CALIB_BYTES / (1024.0 * sum(c[counter] for c in calib) / n)
+        per[counter] = {"factor": factor, "calib_kernel": ck[:80]}
+        for name, _, _ in blocks:
+            res[name][counter] = sum(c[counter] for c in got[name]) / n
+            res[name]["kernels"] = got[name + "#kernel"]
+    for name, r in res.items():
+        r["hbm_bytes"] = round(r["FETCH_SIZE"] * 1024 * per["FETCH_SIZE"]["factor"]
+                               + r["WRITE_SIZE"] * 1024 * per["WRITE_SIZE"]["factor"])
+        r["fetch_kib"] = round(r.pop("FETCH_SIZE"), 1)
+        r["write_kib"] = round(r.pop("WRITE_SIZE"), 1)
     return res, per
 
 
-def write_counter_profiles(res, per, n):
+def write_counter_profiles(res, per, workload: str, n: int):
     cmd = ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT_F -o run -- python -u "
-           f"bench.py --counter-pass --counter-launches {n}; the same with WRITE_SIZE into OUT_W; "
-           f"python bench.py --summarize-counters OUT_F OUT_W --counter-launches {n}")
-    groups = {"decode": ["decode_m1", "decode_m4", "decode_m16"], "compress": ["compress"],
-              "multi": ["multi"], "prefill": ["prefill"], "reconstruct": ["reconstruct"]}
-    for kernel, labels in groups.items():
-        rec = {"kernel": kernel, "workload": "proj_4096",
-               "sources_digest": sources_digest(KERNEL_SOURCES[kernel]),
+           f"bench.py --counter-pass --workload {workload} --counter-launches {n}; the same "
+           f"with WRITE_SIZE into OUT_W; python bench.py --summarize-counters OUT_F OUT_W "
+           f"--workload {workload} --counter-launches {n}")
+    _, groups = counter_plan(workload)
+    for fam, (labels, unit) in groups.items():
+        rec = {"kernel": fam, "workload": workload,
+               "sources_digest": sources_digest(KERNEL_SOURCES[fam]),
                "hbm_bytes_per_launch": sum(res[l]["hbm_bytes"] for l in labels),
                "algorithmic_bytes_per_launch": sum(res[l]["algorithmic_bytes"] for l in labels),
                "launches": {l: res[l] for l in labels},
                "calibration": {k: {"factor": round(v["factor"], 4), "kernel": v["calib_kernel"],
                                    "bytes": CALIB_BYTES} for k, v in per.items()},
-               "unit_note": ("one launch of each decode token count (M = 1, 4, 16), as the decode "
-                             "roofline's unit" if kernel == "decode" else "one launch"),
-               "command": cmd}
-        with open(os.path.join(PROFILES, f"{kernel}_proj_4096_pmc.json"), "w") as f:
+               "unit_note": unit, "command": cmd}
+        with open(os.path.join(PROFILES, f"{fam}_{workload}_pmc.json"), "w") as f:
             json.dump(rec, f, indent=1)
             f.write("\n")
-    lines = ["# HBM traffic per launch from rocprofv3 counters: bench.py, workload proj_4096", "",
-             "Commands (on one MI355X, from the repository root):", "", "    " + cmd, "",
+    lines = [f"# HBM traffic per launch from rocprofv3 counters: bench.py, workload {workload}",
+             "", "Commands (on one MI355X, from the repository root):", "", "    " + cmd, "",
              "FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by the ratio of true bytes "
              "to counter bytes measured on a plain elementwise kernel reading and writing 256 MiB "
              f"(FETCH x{per['FETCH_SIZE']['factor']:.3f}, WRITE x{per['WRITE_SIZE']['factor']:.3f}). "
-             f"Averages over {n} launches, each on its own weight copy.", "",
-             "| Launch | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes (scaled) | Algorithmic bytes "
-             "| Ratio |", "|---|---|---|---|---|---|"]
+             f"Averages over {n} calls, each on its own operand copy (a call may make more "
+             "than one launch: their counters are summed).", "",
+             "| Call | Kernels | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM bytes (scaled) "
+             "| Algorithmic bytes | Ratio |", "|---|---|---|---|---|---|---|"]
     for l, r in res.items():
-        lines.append(f"| {l} | {r['fetch_kib']:.0f} | {r['write_kib']:.0f} | {r['hbm_bytes']:,} | "
-                     f"{r['algorithmic_bytes']:,} | {r['hbm_bytes'] / r['algorithmic_bytes']:.3f} |")
-    with open(os.path.join(PROFILES, "counters_proj_4096.md"), "w") as f:
+        kname = ", ".join(f"`{k}`" for k in r["kernels"])
+        lines.append(f"| {l} | {kname} | {r['fetch_kib']:.0f} | {r['write_kib']:.0f} | "
+                     f"{r['hbm_bytes']:,} | {r['algorithmic_bytes']:,} | "
+                     f"{r['hbm_bytes'] / r['algorithmic_bytes']:.3f} |")
+    with open(os.path.join(PROFILES, f"counters_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+# Derived figures of a counter summary, each from counters of one run.
+# GRBM_GUI_ACTIVE sums the eight XCDs' busy cycles, so one eighth of it is the
+# dispatch's length in GPU clocks; the chip has 256 CUs of 4 SIMDs and one
+# texture addresser (TA) per CU.
+DERIVED = (
+    ("clocks", ("GRBM_GUI_ACTIVE",), lambda c: c["GRBM_GUI_ACTIVE"] / 8,
+     "GRBM_GUI_ACTIVE / 8", "{:,.0f}"),
+    ("MFMA pipe busy per SIMD", ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"),
+     lambda c: c["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * c["GRBM_GUI_ACTIVE"] / 8),
+     "SQ_VALU_MFMA_BUSY_CYCLES / (1024 x clocks)", "{:.1%}"),
+    ("VALU busy per SIMD", ("SQ_ACTIVE_INST_VALU", "GRBM_GUI_ACTIVE"),
+     lambda c: 4 * c["SQ_ACTIVE_INST_VALU"] / (1024 * c["GRBM_GUI_ACTIVE"] / 8),
+     "4 x SQ_ACTIVE_INST_VALU / (1024 x clocks)", "{:.1%}"),
+    ("waves waiting on anything", ("SQ_WAIT_ANY", "SQ_WAVE_CYCLES"),
+     lambda c: c["SQ_WAIT_ANY"] / c["SQ_WAVE_CYCLES"], "SQ_WAIT_ANY / SQ_WAVE_CYCLES", "{:.1%}"),
+    ("waves waiting to issue", ("SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES"),
+     lambda c: c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"], "SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES",
+     "{:.1%}"),
+    ("TA busy per CU", ("TA_TA_BUSY_sum", "GRBM_GUI_ACTIVE"),
+     lambda c: c["TA_TA_BUSY_sum"] / (256 * c["GRBM_GUI_ACTIVE"] / 8),
+     "TA_TA_BUSY_sum / (256 x clocks)", "{:.1%}"),
+    ("TA cycles per vector memory read", ("TA_TA_BUSY_sum", "SQ_INSTS_VMEM_RD"),
+     lambda c: c["TA_TA_BUSY_sum"] / c["SQ_INSTS_VMEM_RD"],
+     "TA_TA_BUSY_sum / SQ_INSTS_VMEM_RD", "{:.1f}"),
+    ("LDS bank conflicts per LDS cycle", ("SQ_LDS_BANK_CONFLICT", "SQ_ACTIVE_INST_LDS"),
+     lambda c: c["SQ_LDS_BANK_CONFLICT"] / c["SQ_ACTIVE_INST_LDS"],
+     "SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS", "{:.3f}"),
+)
+
+
+def summarize_pmc(dirs, workload: str, n: int):
+    """profiles/sq_counters_<workload>.md: per block, the average per dispatch
+    of every counter of the given --pmc runs of a counter pass, and the
+    derived figures whose counters one run holds."""
+    blocks, _ = counter_plan(workload)
+    runs = []
+    for d in dirs:
+        got, _, _ = _split_blocks(d, workload, n)
+        counters = sorted(next(iter(got[blocks[0][0]])).keys())
+        avg = {name: {c: sum(x[c] for x in got[name]) / n for c in counters}
+               for name, _, _ in blocks}
+        runs.append((d, counters, avg, got))
+    lines = [f"# Counters per dispatch: bench.py counter pass, workload {workload}", "",
+             "Commands (on one MI355X, from the repository root), one run per counter set:", ""]
+    for i, (_, counters, _, _) in enumerate(runs):
+        lines.append(f"    rocprofv3 --pmc {','.join(counters)} --output-format csv -d OUT_{i + 1} "
+                     f"-o run -- python -u bench.py --counter-pass --workload {workload} "
+                     f"--counter-launches {n}")
+    lines += ["", "    python bench.py --summarize-pmc " + " ".join(
+        f"OUT_{i + 1}" for i in range(len(runs))) + f" --workload {workload} "
+        f"--counter-launches {n}", "",
+        f"Averages over the {n} calls of each block (each on its own operand copy; the "
+        "launches of a call summed).", ""]
+    head = "| Counter | " + " | ".join(b for b, _, _ in blocks) + " |"
+    sep = "|---" * (len(blocks) + 1) + "|"
+    lines += ["## Raw counters", "", head, sep]
+    for ri, (_, counters, avg, _) in enumerate(runs):
+        for c in counters:
+            lines.append(f"| {c} (run {ri + 1}) | " + " | ".join(
+                f"{avg[b][c]:,.0f}" for b, _, _ in blocks) + " |")
+    lines += ["", "## Derived", "",
+              "GRBM_GUI_ACTIVE sums the eight XCDs' busy cycles: one eighth of it is the "
+              "dispatch's length in GPU clocks (clocks below). The chip has 256 CUs of 4 SIMDs "
+              "and one texture addresser per CU.", "", "| Figure (formula) | " +
+              " | ".join(b for b, _, _ in blocks) + " |", sep]
+    for label, need, fn, formula, fmt in DERIVED:
+        for ri, (_, counters, avg, _) in enumerate(runs):
+            if all(k in counters for k in need):
+                lines.append(f"| {label} ({formula}; run {ri + 1}) | " + " | ".join(
+                    fmt.format(fn(avg[b])) for b, _, _ in blocks) + " |")
+                break
+    with open(os.path.join(PROFILES, f"sq_counters_{workload}.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def summarize_trace(d: str, name: str, command: str):
+    """profiles/<name>_kernel_trace.md from the *_kernel_stats.csv of a
+    rocprofv3 --kernel-trace --stats run: calls and durations of the
+    library's kernels (and the calibration probes)."""
+    import csv
+    rows = []
+    for dirpath, _, files in os.walk(d):
+        for f in files:
+            if f.endswith("kernel_stats.csv"):
+                rows += list(csv.DictReader(open(os.path.join(dirpath, f))))
+    if not rows:
+        raise SystemExit(f"{d}: no kernel_stats.csv")
+    keep = [r for r in rows if "bd::" in r["Name"] or any(
+        k in r["Name"] for k in KERNEL_OF.values())]
+    lines = [f"# rocprofv3 kernel trace: {name}", "", "Command (one MI355X, repository root):", "",
+             "    " + command, "",
+             "Library kernels from the run's kernel statistics (every launch of the process: "
+             "set-up, eager runs, graph captures, timed steps and ranges; durations in "
+             "microseconds).", "", "| Kernel | Calls | Average | Min | Max | Total (ms) |",
+             "|---|---|---|---|---|---|"]
+    for r in sorted(keep, key=lambda r: -float(r["TotalDurationNs"])):
+        kname = _short_kernel(r["Name"])
+        lines.append(f"| `{kname}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                     f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.2f} |")
+    with open(os.path.join(PROFILES, f"{name}_kernel_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
@@ -1219,6 +1468,8 @@ def bench_layer(name, args, dev, ceil):
         w = StackWorkload(name, dev)
     else:
         w = LayerWorkload(name, dev)
+        if args.ab_per_variant and w.kind == "multi":
+            w.setup_per_variant()
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
     print(f"[bench] {name}: set up in {setup_s:.1f} s, distinct variants D={w.distinct}",
@@ -1339,10 +1590,21 @@ def main():
                     help="seconds of oracle work for the projection's cpu_baseline leg (half "
                          "that for each layer configuration; 0 skips them)")
     ap.add_argument("--counter-pass", action="store_true",
-                    help="eager launches for a rocprofv3 --pmc run (proj_4096), then exit")
+                    help="eager launches for a rocprofv3 --pmc run (--workload proj_4096, "
+                         "layer70b_multi or layer70b_prefill; default proj_4096), then exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="write profiles/*_proj_4096_pmc.json from two --pmc runs, then exit")
+                    help="write profiles/*_<workload>_pmc.json and counters_<workload>.md "
+                         "from a FETCH_SIZE and a WRITE_SIZE run of the counter pass, then exit")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="DIR",
+                    help="write profiles/sq_counters_<workload>.md from --pmc runs of the "
+                         "counter pass, then exit")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("DIR", "NAME", "COMMAND"),
+                    help="write profiles/NAME_kernel_trace.md from a --kernel-trace --stats "
+                         "run made by COMMAND, then exit")
     ap.add_argument("--counter-launches", type=int, default=8)
+    ap.add_argument("--ab-per-variant", action="store_true",
+                    help="layer70b_multi: also time the per-variant fused alternative (one "
+                         "single-variant fused call per variant present) on the same batch")
     ap.add_argument("--clock-pass", action="store_true",
                     help="six fused gate-shaped prefills then six library GEMMs, for a "
                          "rocprofv3 --pmc GRBM_GUI_ACTIVE run, then exit")
@@ -1352,11 +1614,22 @@ def main():
               "(the kernels would shard by output rows); run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    cw = "proj_4096" if args.workload == "default" else args.workload
+    if (args.counter_pass or args.summarize_counters or args.summarize_pmc) \
+            and cw not in COUNTER_WORKLOADS:
+        raise SystemExit(f"counter runs cover {', '.join(COUNTER_WORKLOADS)}")
     if args.summarize_counters:
-        res, per = summarize_counters(*args.summarize_counters, args.counter_launches,
-                                      ProjWorkload.static_bytes())
-        write_counter_profiles(res, per, args.counter_launches)
+        res, per = summarize_counters(*args.summarize_counters, cw, args.counter_launches)
+        write_counter_profiles(res, per, cw, args.counter_launches)
         print(json.dumps({"counters": res, "calibration": per}), flush=True)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc, cw, args.counter_launches)
+        print(f"[bench] wrote profiles/sq_counters_{cw}.md", flush=True)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        print(f"[bench] wrote profiles/{args.summarize_trace[1]}_kernel_trace.md", flush=True)
         return
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
@@ -1369,11 +1642,9 @@ def main():
         print("[bench] clock pass done", file=sys.stderr, flush=True)
         return
     if args.counter_pass:
-        w = ProjWorkload(dev)
-        torch.cuda.synchronize()
-        counter_pass(w, args.counter_launches)
-        print(f"[bench] counter pass done ({args.counter_launches} launches per kernel, "
-              f"D={w.distinct})", file=sys.stderr, flush=True)
+        counter_pass(cw, dev, args.counter_launches)
+        print(f"[bench] counter pass done ({cw}, {args.counter_launches} launches per block)",
+              file=sys.stderr, flush=True)
         return
     if args.workload == "default":
         run_default(args, dev)

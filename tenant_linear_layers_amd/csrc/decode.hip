@@ -299,6 +299,12 @@ __global__ __launch_bounds__(NW * kWave) void linear_decode_ring_kernel(const Sk
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u;
+      // The stage about to be refilled was read by the previous block: its
+      // LDS reads must be complete before the buffer loads may write it (a
+      // load to LDS is not ordered after earlier reads of the same wave), and
+      // the compiler must not move the loads above this point.
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_sched_barrier(0);
       // past the wave's last block the issue re-reads that block into a stage
       // nobody reads: every block issues the same number of loads
       issue(min(i + U - 1, nmine - 1), (u + U - 1) % U);
@@ -830,9 +836,10 @@ __device__ void build_pairs(PairGroups<NS>& G, const int32_t* ids, int M, int n_
 // sign words of its next block are requested before the current block is
 // multiplied.  The sign rows of the pairs' variants are looked up once per
 // batch, outside the loop over blocks.
-template <int MT, int NW, int KP, bool WLDS, int WPE>
+template <int MT, int NW, int KP, bool WLDS, int WPE, bool EARLY>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void
 linear_multi_pairs_kernel(const SkinnyArgs a) {
+  static_assert(!EARLY || (MT <= 2 && WLDS), "early staging keeps every tile's x in registers");
   constexpr int kXRows = MT * 16;
   constexpr int kXRowB = 256;                  // bytes per staged row (128 bf16)
   constexpr int kXWave = (kXRows + (WLDS ? 16 : 0)) * kXRowB;  // x rows, then 16 W_base rows
@@ -947,20 +954,98 @@ linear_multi_pairs_kernel(const SkinnyArgs a) {
         for (int q = 0; q < 4; ++q) wc[q] = bload128(wblk, wbytes, woff + 16 * q, 2 * k0);
       }
     };
-    auto load_s1 = [&](int i, int u) {
+    auto sign_word = [&](int i, int u) -> uint32_t {
       // dword sj/4 of the row's 16 sign bytes of block wv + NW*i; in a final
       // 64-wide block dwords 2 and 3 re-read the row's last 4 bytes (never
       // past the row)
       const uint32_t off = srow + min(((wv + NW * i) << 4) + sj, (d_in >> 3) - 4);
       const uint64_t b = ((uint64_t)__builtin_amdgcn_readlane(stab_hi, u) << 32) |
                          (uint32_t)__builtin_amdgcn_readlane(stab_lo, u);
-      sc[u] = *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(b + off);
+      return *reinterpret_cast<const __attribute__((address_space(1))) uint32_t*>(b + off);
     };
+    auto load_s1 = [&](int i, int u) { sc[u] = sign_word(i, u); };
     auto stage_x = [&](int i) {
       const int k0 = (wv + NW * i) << 7;
 #pragma unroll
       for (int j = 0; j < kDma; ++j) lds_bload16(a.x, xbytes, xoff[j], 2 * k0, xs + j * 1024);
     };
+    if constexpr (EARLY) {
+      // Every load of block i+1 is issued at the top of block i: its x once
+      // all tiles' x operands of block i are in registers, its sign words
+      // into sn, its W_base once this block's W operand is in registers.
+      // The sign words are moved into the operand layout at the end of the
+      // block.
+      uint32_t sn[KP];
+#pragma unroll
+      for (int u = 0; u < KP; ++u) sn[u] = 0u;
+      if (nmine > 0) {
+        stage_x(0);
+        if (batch == 0) stage_w(0);
+#pragma unroll
+        for (int u = 0; u < KP; ++u)
+          if ((builds >> (p0 + u)) & 1) sn[u] = sign_word(0, u);
+#pragma unroll
+        for (int u = 0; u < KP; ++u) sc[u] = __builtin_amdgcn_ds_bpermute(perm_src, sn[u]);
+      }
+      for (int i = 0; i < nmine; ++i) {
+        __builtin_amdgcn_s_waitcnt(0);  // x and W_base of block i staged
+        const bool more = i + 1 < nmine;
+        const int inext = more ? i + 1 : i;
+        if (half_tail && wv + NW * i == nblk - 1) {
+          // a final 64-wide block: zero columns 64..127 of every slot row
+          for (int e = lane; e < kXRows * 8; e += kWave) {
+            const int r = e >> 3;
+            const int cg = 8 + (e & 7);
+            *reinterpret_cast<u32x4*>(xs + r * kXRowB + ((cg ^ (r & 15)) << 4)) =
+                u32x4{0u, 0u, 0u, 0u};
+          }
+          __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        }
+        u32x4 xt[MT][4];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const char* src = xs + (16 * t + n) * kXRowB;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) xt[t][q] = *reinterpret_cast<const u32x4*>(src + foff[q]);
+        }
+        u32x4 wf[4];
+        if (batch == 0) {
+          const char* src = ws + n * kXRowB;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) wf[q] = *reinterpret_cast<const u32x4*>(src + foff[q]);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): both stages read
+        if (more) stage_x(i + 1);
+#pragma unroll
+        for (int u = 0; u < KP; ++u)
+          if ((builds >> (p0 + u)) & 1) sn[u] = sign_word(inext, u);
+        if (batch == 0) {
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) accw[t] = mfma16(xt[t][q], wf[q], accw[t]);
+          if (more) stage_w(inext);
+        }
+        Spread sz;
+#pragma unroll
+        for (int u = 0; u < KP; ++u) {
+          if (u < np) {
+            const int t = __builtin_amdgcn_readlane(pt_l, p0 + u);
+            if ((builds >> (p0 + u)) & 1) sz = spread_signs(sc[u]);
+            if (MT == 1 || t == 0) {
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[u] = mfma16(xt[0][q], step_signs(sz, q), acc[u]);
+            } else {
+#pragma unroll
+              for (int q = 0; q < 4; ++q)
+                acc[u] = mfma16(xt[MT - 1][q], step_signs(sz, q), acc[u]);
+            }
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < KP; ++u) sc[u] = __builtin_amdgcn_ds_bpermute(perm_src, sn[u]);
+      }
+    } else {
     if (nmine > 0) {
       stage_x(0);
       if (batch == 0) stage_w(0);
@@ -996,9 +1081,9 @@ linear_multi_pairs_kernel(const SkinnyArgs a) {
       // merge).
       const int inext = more ? i + 1 : i;
       // this block's sign words into the operand layout
+      // (every slot: a slot that loaded nothing permutes a stale word it never reads)
 #pragma unroll
-      for (int u = 0; u < KP; ++u)
-        if ((builds >> (p0 + u)) & 1) sc[u] = __builtin_amdgcn_ds_bpermute(perm_src, sc[u]);
+      for (int u = 0; u < KP; ++u) sc[u] = __builtin_amdgcn_ds_bpermute(perm_src, sc[u]);
       int tcur = -1;
       if (batch == 0) {
         u32x4 wf[4];
@@ -1050,6 +1135,7 @@ linear_multi_pairs_kernel(const SkinnyArgs a) {
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this block's LDS reads are done
         stage_x(i + 1);
       }
+    }
     }
 
     // Sign sums of the batch's pairs: add the waves' partials in a fixed
@@ -1167,10 +1253,10 @@ hipError_t launch_multi(const SkinnyArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MT, int NW, int KP, bool WLDS, int WPE>
+template <int MT, int NW, int KP, bool WLDS, int WPE, bool EARLY>
 hipError_t launch_multi_pairs(const SkinnyArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((linear_multi_pairs_kernel<MT, NW, KP, WLDS, WPE>), dim3((a.d_out + 15) / 16),
-                     dim3(NW * kWave), 0, stream, a);
+  hipLaunchKernelGGL((linear_multi_pairs_kernel<MT, NW, KP, WLDS, WPE, EARLY>),
+                     dim3((a.d_out + 15) / 16), dim3(NW * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1212,14 +1298,19 @@ hipError_t launch_linear_multi(const SkinnyArgs& a, hipStream_t stream) {
   // enough 16-row groups to fill the CUs that way (at least 1.5 per CU);
   // eight otherwise (measured: 28672 x 8192 at 32 tokens 246 against 265 us,
   // 8192 x 8192 76 us; 4096 x 4096 at 16 tokens 25.0 against 21.8 us).
+  // Early staging (every load of the next block issued at the top of the
+  // current one) for one token tile: 28672 x 8192 at 16 tokens 165 -> 157
+  // us.  At two tiles it needs 32 more registers a lane: with three
+  // workgroups per CU they spill (472 us), with two it is no faster (246
+  // against 242 us).
   const bool wide = (a.d_out + 15) / 16 >= 384;
   if (a.M <= 16)
-    return wide ? launch_multi_pairs<1, 4, 12, true, 3>(a, stream)
-                : launch_multi_pairs<1, 8, 12, true, 2>(a, stream);
+    return wide ? launch_multi_pairs<1, 4, 12, true, 3, true>(a, stream)
+                : launch_multi_pairs<1, 8, 12, true, 2, true>(a, stream);
   if (a.M <= 32)
-    return wide ? launch_multi_pairs<2, 4, 12, true, 3>(a, stream)
-                : launch_multi_pairs<2, 8, 12, true, 2>(a, stream);
-  return launch_multi_pairs<4, 8, 20, false, 2>(a, stream);
+    return wide ? launch_multi_pairs<2, 4, 12, true, 3, false>(a, stream)
+                : launch_multi_pairs<2, 8, 12, true, 2, false>(a, stream);
+  return launch_multi_pairs<4, 8, 20, false, 2, false>(a, stream);
 }
 
 }  // namespace bd

@@ -508,6 +508,34 @@ def test_layer70b_decode_full_size():
                            f"layer70b_decode {name} M={m}")
 
 
+@pytest.mark.parametrize("shape", [(10240, 8192), (8192, 8192)])
+def test_decode_small_m_back_to_back_full_output(shape):
+    """Few-token decode (M = 1, 3, 6, 8: the kernels that keep two blocks of
+    W_base and x in flight per wave) of four variants of one base, launched
+    back to back with x hot in the cache, as a per-variant grouping of a
+    mixed batch runs them.  Every output is compared with the oracle (row
+    chunks of the float64 product).  A refill of a stage whose last reads
+    were still in flight once corrupted a few outputs in each such run."""
+    d_out, d_in = shape
+    g = S.generator(d_out + 3, DEV)
+    wb = S.draw_base(d_out, d_in, 0.015, g, DEV)
+    variants = []
+    for b in (2e-4, 5e-4, 1e-3, 2e-3):
+        wf = S.draw_finetuned(wb, b, g)
+        variants.append(T.compress(wf, wb, 1))
+        del wf
+    x = S.draw_activations(8, d_in, g, DEV)
+    for m in (1, 3, 6, 8):
+        ys = [T.linear(x[:m], wb, p, a, 1) for p, a in variants]
+        torch.cuda.synchronize()
+        for v, ((p, a), y) in enumerate(zip(variants, ys)):
+            for r0 in range(0, d_out, 2048):
+                rows = np.arange(r0, min(r0 + 2048, d_out))
+                ref = oracle_y(x[:m], wb, p, a, 1, rows=rows)
+                assert_y_close(y[:, r0:r0 + len(rows)], ref,
+                               f"{d_out}x{d_in} M={m} variant {v} rows {r0}..")
+
+
 def _progress(msg):
     import sys
     sys.__stderr__.write(f"  [stack70b] {msg}\n")
