@@ -1583,7 +1583,7 @@ def main():
     ap.add_argument("--workload", default="default",
                     choices=["default", "proj_4096", "layer70b_prefill", "layer70b_multi",
                              "layer70b_decode", "stack70b_multi", "serve_layer70b",
-                             "monosoup_4096"])
+                             "monosoup_4096", "ceilings"])
     ap.add_argument("--configs", default=",".join(DEFAULT_CONFIGS),
                     help="configurations of the default line (comma-separated)")
     ap.add_argument("--cpu-budget", type=float, default=10.0,
@@ -1648,6 +1648,14 @@ def main():
         return
     if args.workload == "default":
         run_default(args, dev)
+        return
+    if args.workload == "ceilings":
+        # the measured ceilings alone (stream read of HBM, bf16 MFMA), as the
+        # default line reports them beside the published peaks
+        ceil = measure_ceilings(dev)
+        print(json.dumps({"ceilings": ceil, "published": {"hbm_gbs": HBM_PEAK_GBS,
+                                                         "bf16_tflops": BF16_PEAK_TFLOPS}}),
+              flush=True)
         return
     print(f"[bench] setting up {args.workload}", file=sys.stderr, flush=True)
     if args.workload == "serve_layer70b":
