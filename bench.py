@@ -1086,8 +1086,13 @@ def summarize_pmc(dirs, workload: str, n: int):
     for label, need, fn, formula, fmt in DERIVED:
         for ri, (_, counters, avg, _) in enumerate(runs):
             if all(k in counters for k in need):
+                def cell(c):
+                    try:
+                        return fmt.format(fn(c))
+                    except ZeroDivisionError:
+                        return "—"
                 lines.append(f"| {label} ({formula}; run {ri + 1}) | " + " | ".join(
-                    fmt.format(fn(avg[b])) for b, _, _ in blocks) + " |")
+                    cell(avg[b]) for b, _, _ in blocks) + " |")
                 break
     with open(os.path.join(PROFILES, f"sq_counters_{workload}.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
