@@ -486,7 +486,8 @@ def test_layer70b_multi_full_size():
 
 def test_layer70b_decode_full_size():
     """One variant of a 70B-shaped layer (per-row alpha) through the decode
-    kernel at M = 1, 4, 16, as the layer decode benchmark runs it: every
+    kernels at M = 1, 4, 16, as the layer decode benchmark runs it, and at
+    M = 32 and 64 (the pairs kernel with every token on variant 0): every
     compression bit-exact on sampled rows, every output on sampled rows."""
     wl = S.WORKLOADS["layer70b_decode"]
     g = S.generator(wl.seed, DEV)
@@ -498,10 +499,10 @@ def test_layer70b_decode_full_size():
         packs.append(p)
         alphas.append(a)
         del wf
-    xs = S.draw_layer_inputs(wl, max(wl.tokens), g, DEV)
+    xs = S.draw_layer_inputs(wl, 64, g, DEV)
     for i, (name, d_out, d_in) in enumerate(wl.matrices):
         rows = _sample_rows(d_out, 48, 600 + i)
-        for m in wl.tokens:
+        for m in tuple(wl.tokens) + (32, 64):
             y = T.linear(xs[i][:m], bases[i], packs[i], alphas[i], 1)
             ref = oracle_y(xs[i][:m], bases[i], packs[i], alphas[i], 1, rows=rows)
             assert_y_close(y[:, torch.as_tensor(rows, device=DEV)], ref,
