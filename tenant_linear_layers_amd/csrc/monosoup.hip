@@ -22,21 +22,39 @@
 // rounded up to 8, 16 or 32; columns past the rank start as zeros and stay
 // zero (their Cholesky pivots are dropped).
 //
-// Kernels: mul (Y = Delta X: 8 rows per wave (4 at width 32), lanes across d_in, a
-// butterfly sum per output), tmul (partial Z = Delta^T Y over row chunks,
-// lanes across d_in) and its fixed-order reduction, gram (partial A^T A over
-// row chunks), chol (sum of the partials and the Cholesky factor with
-// dropped pivots, one workgroup), scale (A <- A U^-1 by substitution, one row
-// per thread), merge (W_base + mean of Q_i Z_i^T, rounded to bf16, LDS
-// tiles).
+// CholeskyQR of A is Q = A U^+ with U the Cholesky factor of A^T A and U^+
+// the inverse on the kept pivots (zero rows and columns for dropped ones).
+// The products are linear, so Delta (A U^+) = (Delta A) U^+: the scaling of
+// one basis is applied to the next product's output rows instead of being a
+// pass of its own, and the stored A is the unscaled product.
+//
+// Kernels, two per product:
+//   mul / tmul   Y = Delta X and Z = Delta^T Y on the matrix cores
+//                (v_mfma_f32_16x16x4_f32), Delta formed in registers from
+//                16-byte loads of both matrices; four waves per workgroup
+//                split the contraction and add through LDS; the workgroups
+//                along the contraction write partial sums.  One extra
+//                workgroup meanwhile factors the Gram matrix of the
+//                previous product (its partials summed in order, Cholesky
+//                with dropped pivots, U^+), which only the next epilogue
+//                needs.
+//   epi          sums the partials in order, multiplies by the previous
+//                U^+, writes the rows and a Gram partial per 64 rows.  The
+//                same kernel in place scales a basis (with or without its
+//                Gram partials).
+//   factor       the Gram factorisation on its own, where no product follows.
+//   merge        W_base + (1/k) sum_i Q_i Z_i^T, an fp32 matrix-core product
+//                with K = k R, rounded to bf16 through an LDS tile.
+#include <algorithm>
+
 #include "common.h"
 #include "internal.h"
 
 namespace bd {
 namespace {
 
-constexpr int kTmulChunks = 64;   // row chunks of the Delta^T Y partials
-constexpr int kGramChunks = 64;   // row chunks of the Gram partials
+constexpr int kWaves = 4;     // waves per workgroup of the products
+constexpr int kEpiRows = 64;  // rows per workgroup of the epilogue
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
@@ -50,193 +68,402 @@ __device__ __forceinline__ void delta8(const u32x4& a, const u32x4& b, float (&d
   }
 }
 
-// Y[o][j] = sum_c Delta[o][c] X[c][j]; X [d_in][R], Y [d_out][R].  A wave
-// owns RW rows, which share every read of X; one wave per workgroup.
-template <int R, int RW>
-__global__ __launch_bounds__(64) void ms_mul_kernel(const uint16_t* __restrict__ wf,
-                                                    const uint16_t* __restrict__ wb, int d_out,
-                                                    int d_in, const float* __restrict__ X,
-                                                    float* __restrict__ Y) {
-  const int lane = threadIdx.x & 63;
-  const int o0 = blockIdx.x * RW;
-  float acc[RW][R];
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// A Gram factorisation for the extra workgroup of a product kernel (none when
+// Gp is null): Mout = U^+ from the nb partials at Gp.
+struct FactorJob {
+  const float* Gp;
+  int nb;
+  float* Mout;
+};
+
+// Workgroups along the contraction of mul: about 512 workgroups in all, each
+// wave at least one 32-column block, at most 32.
+inline int ms_mul_slices(int64_t d_out, int64_t d_in) {
+  const int64_t groups = (d_out + 63) / 64;
+  int64_t ks = (512 + groups - 1) / groups;
+  const int64_t most = d_in / 32 / kWaves;
+  ks = ks > most ? most : ks;
+  ks = ks > 32 ? 32 : ks;
+  return (int)(ks < 1 ? 1 : ks);
+}
+
+// Row chunks of tmul: about 512 workgroups, at least 32 rows each, at most 32.
+inline int ms_tmul_chunks(int64_t d_out, int64_t d_in) {
+  const int64_t groups = (d_in + 127) / 128;
+  int64_t kt = (512 + groups - 1) / groups;
+  const int64_t most = (d_out + 31) / 32;
+  kt = kt > most ? most : kt;
+  kt = kt > 32 ? 32 : kt;
+  return (int)(kt < 1 ? 1 : kt);
+}
+
+// LDS floats that gram_factor needs.
+template <int R>
+constexpr int factor_smem() {
+  return 1024 + 2 * R * R + 4;
+}
+
+// G = the sum of the nb Gram partials Gp[0 .. nb-1] in order, its Cholesky
+// factor U with dropped pivots (a pivot at or below 1e-6 of the largest
+// diagonal of G: its row of U is zero) and Mout = U^+, the upper-triangular
+// matrix with z = x U^+ solving z U = x on the kept indices (z zero on the
+// dropped ones).  One workgroup of 256 threads; sm: factor_smem<R>() floats
+// of LDS, 16-byte aligned.
+template <int R>
+__device__ void gram_factor(const float* __restrict__ Gp, int nb, float* __restrict__ Mout,
+                            float* sm) {
+  float4* S4 = reinterpret_cast<float4*>(sm);
+  float(*G)[R] = reinterpret_cast<float(*)[R]>(sm + 1024);
+  float(*U)[R] = reinterpret_cast<float(*)[R]>(sm + 1024 + R * R);
+  float& piv = sm[1024 + 2 * R * R];
+  const int t = threadIdx.x;
+  // G = sum of the partials in workgroup order: thread t adds float4 q of
+  // partials h, h + H, ... (q = t % F, h = t / F); then the H sums in h order
+  constexpr int F = R * R / 4;
+  constexpr int H = 256 / F;
+  {
+    const int q = t % F, h = t / F;
+    const float* src = Gp + 4 * q;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    int b = h;
+    // eight loads in flight, then their sums in order
+    for (; b + 7 * H < nb; b += 8 * H) {
+      float4 v[8];
 #pragma unroll
-  for (int i = 0; i < RW; ++i)
+      for (int u = 0; u < 8; ++u)
+        v[u] = *reinterpret_cast<const float4*>(src + (size_t)(b + u * H) * R * R);
 #pragma unroll
-    for (int j = 0; j < R; ++j) acc[i][j] = 0.f;
-  for (int c0 = lane * 8; c0 < d_in; c0 += 512) {
-    float d[RW][8];
-#pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      const size_t base = (size_t)min(o0 + i, d_out - 1) * d_in + c0;
-      delta8(ld128(wf + base), ld128(wb + base), d[i]);
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float* xr = X + (size_t)(c0 + e) * R;
-#pragma unroll
-      for (int j4 = 0; j4 < R / 4; ++j4) {
-        const float4 x = *reinterpret_cast<const float4*>(xr + 4 * j4);
-#pragma unroll
-        for (int i = 0; i < RW; ++i) {
-          acc[i][4 * j4] += d[i][e] * x.x;
-          acc[i][4 * j4 + 1] += d[i][e] * x.y;
-          acc[i][4 * j4 + 2] += d[i][e] * x.z;
-          acc[i][4 * j4 + 3] += d[i][e] * x.w;
-        }
+      for (int u = 0; u < 8; ++u) {
+        s.x += v[u].x;
+        s.y += v[u].y;
+        s.z += v[u].z;
+        s.w += v[u].w;
       }
     }
-  }
-#pragma unroll
-  for (int i = 0; i < RW; ++i)
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      float v = acc[i][j];
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-      acc[i][j] = v;
+    for (; b < nb; b += H) {
+      const float4 v = *reinterpret_cast<const float4*>(src + (size_t)b * R * R);
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
     }
-  if (lane == 0) {
-#pragma unroll
-    for (int i = 0; i < RW; ++i) {
-      if (o0 + i >= d_out) continue;
-#pragma unroll
-      for (int j = 0; j < R; ++j) Y[(size_t)(o0 + i) * R + j] = acc[i][j];
-    }
+    S4[t] = s;
   }
-}
-
-// Zp[p][c][j] = sum over rows o of chunk p of Delta[o][c] Y[o][j]; one wave
-// per (128-column block, chunk), two columns per lane.
-template <int R>
-__global__ __launch_bounds__(64) void ms_tmul_kernel(const uint16_t* __restrict__ wf,
-                                                     const uint16_t* __restrict__ wb, int d_out,
-                                                     int d_in, const float* __restrict__ Y,
-                                                     float* __restrict__ Zp) {
-  const int lane = threadIdx.x;
-  const int c = blockIdx.x * 128 + 2 * lane;
-  const bool live = c < d_in;
-  const int cc = live ? c : d_in - 2;
-  const int p = blockIdx.y;
-  const int rows = (d_out + kTmulChunks - 1) / kTmulChunks;
-  const int r0 = p * rows;
-  const int r1 = min(r0 + rows, d_out);
-  float acc[2][R];
-#pragma unroll
-  for (int h = 0; h < 2; ++h)
-#pragma unroll
-    for (int j = 0; j < R; ++j) acc[h][j] = 0.f;
-#pragma unroll 4
-  for (int o = r0; o < r1; ++o) {
-    const size_t base = (size_t)o * d_in + cc;
-    const uint32_t a = ld32(wf + base);
-    const uint32_t b = ld32(wb + base);
-    const float d0 = bf16_lo(a) - bf16_lo(b);
-    const float d1 = bf16_hi(a) - bf16_hi(b);
-    const float* yr = Y + (size_t)o * R;
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const float y = yr[j];
-      acc[0][j] += d0 * y;
-      acc[1][j] += d1 * y;
-    }
-  }
-  if (live) {
-    float* z = Zp + ((size_t)p * d_in + c) * R;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int j4 = 0; j4 < R / 4; ++j4)
-        *reinterpret_cast<float4*>(z + h * R + 4 * j4) =
-            make_float4(acc[h][4 * j4], acc[h][4 * j4 + 1], acc[h][4 * j4 + 2], acc[h][4 * j4 + 3]);
-  }
-}
-
-// Z[i] = sum_p Zp[p][i] in chunk order (n = d_in * R values).
-__global__ __launch_bounds__(256) void ms_reduce_kernel(const float* __restrict__ Zp, int64_t n,
-                                                        float* __restrict__ Z) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  float s = 0.f;
-#pragma unroll 16
-  for (int p = 0; p < kTmulChunks; ++p) s += Zp[(int64_t)p * n + i];
-  Z[i] = s;
-}
-
-// Gp[p][a][b] = sum over rows of chunk p of A[row][a] A[row][b]; A [n][R].
-template <int R>
-__global__ __launch_bounds__(R * R) void ms_gram_kernel(const float* __restrict__ A, int n,
-                                                        float* __restrict__ Gp) {
-  const int a = threadIdx.x / R;
-  const int b = threadIdx.x % R;
-  const int p = blockIdx.x;
-  const int rows = (n + kGramChunks - 1) / kGramChunks;
-  const int r0 = p * rows;
-  const int r1 = min(r0 + rows, n);
-  float s = 0.f;
-#pragma unroll 8
-  for (int o = r0; o < r1; ++o) s += A[(size_t)o * R + a] * A[(size_t)o * R + b];
-  Gp[((size_t)p * R + a) * R + b] = s;
-}
-
-// G = sum_p Gp[p] (chunk order) and its upper Cholesky factor U (G = U^T U),
-// written to Uf [R][R].  Thread (a, b) keeps G[a][b] (b >= a) in a register
-// and the factorisation runs one pivot per step: the step's row of U from the
-// updated row of G, then the trailing update.  A pivot at or below 1e-6 of
-// the largest diagonal of G is dropped: its row of U is zero, its diagonal
-// 0 marks it for the substitution.
-template <int R>
-__global__ __launch_bounds__(R * R) void ms_chol_kernel(const float* __restrict__ Gp,
-                                                        float* __restrict__ Uf) {
-  __shared__ float U[R][R];
-  __shared__ float diag[R];
-  __shared__ float piv;
-  const int a = threadIdx.x / R;
-  const int b = threadIdx.x % R;
-  float g = 0.f;
-#pragma unroll
-  for (int p = 0; p < kGramChunks; ++p) g += Gp[((size_t)p * R + a) * R + b];
-  U[a][b] = 0.f;
-  if (a == b) diag[a] = g;
   __syncthreads();
+  if (t < F) {
+    float4 s = S4[t];
+    for (int h = 1; h < H; ++h) {
+      const float4 v = S4[h * F + t];
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    float* gr = &G[0][0] + 4 * t;
+    gr[0] = s.x;
+    gr[1] = s.y;
+    gr[2] = s.z;
+    gr[3] = s.w;
+  }
+  __syncthreads();
+  // Cholesky with dropped pivots: thread t keeps G entries t, t + 256, ...
+  constexpr int NE = (R * R + 255) / 256;
+  float gv[NE];
+#pragma unroll
+  for (int u = 0; u < NE; ++u) {
+    const int e = t + 256 * u;
+    gv[u] = e < R * R ? G[e / R][e % R] : 0.f;
+    if (e < R * R) U[e / R][e % R] = 0.f;
+  }
   float gmax = 0.f;
-  for (int k = 0; k < R; ++k) gmax = fmaxf(gmax, diag[k]);
+  for (int kk = 0; kk < R; ++kk) gmax = fmaxf(gmax, G[kk][kk]);
   const float thr = 1e-6f * gmax;
-  for (int k = 0; k < R; ++k) {
-    if (a == k && b == k) piv = g;
+  __syncthreads();
+  for (int kk = 0; kk < R; ++kk) {
+#pragma unroll
+    for (int u = 0; u < NE; ++u)
+      if (t + 256 * u == kk * R + kk) piv = gv[u];
     __syncthreads();
     const float pk = piv;
     const bool keep = gmax > 0.f && pk > thr;
-    if (a == k && b >= k) U[k][b] = keep ? g / sqrtf(pk) : 0.f;
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+      const int e = t + 256 * u, a = e / R, b = e % R;
+      if (e < R * R && a == kk && b >= kk) U[kk][b] = keep ? gv[u] / sqrtf(pk) : 0.f;
+    }
     __syncthreads();
-    if (a > k && b >= a) g -= U[k][a] * U[k][b];
+#pragma unroll
+    for (int u = 0; u < NE; ++u) {
+      const int e = t + 256 * u, a = e / R, b = e % R;
+      if (e < R * R && a > kk && b >= a) gv[u] -= U[kk][a] * U[kk][b];
+    }
   }
-  Uf[a * R + b] = U[a][b];
+  // row m of U^+ is the substitution of the unit vector e_m (thread m)
+  if (t < R) {
+    float z[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      float v = j == t ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < j; ++m) v -= z[m] * U[m][j];
+      const float ujj = U[j][j];
+      z[j] = ujj > 0.f ? v / ujj : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < R; ++j) Mout[t * R + j] = z[j];
+  }
 }
 
-// A[row][:] <- A[row][:] U^-1 on the kept indices, by forward substitution
-// (z U = x, z_j = 0 where U[j][j] = 0); one row per thread.
+// Yp[ks][o][j] = sum over the workgroup's columns c of Delta[o][c] X[c][j];
+// X [d_in][R].  A workgroup owns 64 rows (four 16-row tiles) and the 32-wide
+// column blocks 4 ks + w, 4 ks + w + 4 KS, ... for wave w.  Lane (n, g)
+// holds columns 8g .. 8g+7 of a block for row n of each tile (one 16-byte
+// load of each bf16 matrix) and X's rows 8g .. 8g+7 of the block for column
+// n of each 16-column tile; product s takes the block's columns s, 8+s,
+// 16+s, 24+s.  The waves' sums are added through LDS in wave order.
 template <int R>
-__global__ __launch_bounds__(256) void ms_scale_kernel(float* __restrict__ A, int n,
-                                                       const float* __restrict__ Uf) {
-  __shared__ float M[R * R];
-  for (int t = threadIdx.x; t < R * R; t += 256) M[t] = Uf[t];
-  __syncthreads();
-  const int row = blockIdx.x * 256 + threadIdx.x;
-  if (row >= n) return;
-  float z[R];
+__global__ __launch_bounds__(256) void ms_mul_kernel(const uint16_t* __restrict__ wf,
+                                                     const uint16_t* __restrict__ wb, int d_out,
+                                                     int d_in, int KS, const float* __restrict__ X,
+                                                     float* __restrict__ Yp, FactorJob fj) {
+  constexpr int NC = (R + 15) / 16;  // 16-column tiles of X and Y
+  constexpr int E = 4 * NC * 4;      // accumulator floats per lane
+  constexpr int NS = std::max(kWaves * E * 64, factor_smem<R>());
+  __shared__ __attribute__((aligned(16))) float sm[NS];
+  if (blockIdx.x == gridDim.x - 1 && fj.Gp) {
+    if (blockIdx.y == 0) gram_factor<R>(fj.Gp, fj.nb, fj.Mout, sm);
+    return;
+  }
+  float(*red)[E][64] = reinterpret_cast<float(*)[E][64]>(sm);
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int row0 = blockIdx.x * 64;
+  const int ks = blockIdx.y;
+  const int nblk = d_in >> 5;
+  size_t rbase[4];
 #pragma unroll
-  for (int j = 0; j < R; ++j) z[j] = A[(size_t)row * R + j];
+  for (int t = 0; t < 4; ++t) rbase[t] = (size_t)min(row0 + 16 * t + n, d_out - 1) * d_in + 8 * g;
+  f32x4 acc[4][NC];
 #pragma unroll
-  for (int j = 0; j < R; ++j) {
-    float v = z[j];
+  for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int m = 0; m < j; ++m) v -= z[m] * M[m * R + j];
-    const float ujj = M[j * R + j];
-    z[j] = ujj > 0.f ? v / ujj : 0.f;
+    for (int ct = 0; ct < NC; ++ct) acc[t][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int kb = ks * kWaves + w; kb < nblk; kb += KS * kWaves) {
+    const int c0 = kb << 5;
+    float d[4][8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) delta8(ld128(wf + rbase[t] + c0), ld128(wb + rbase[t] + c0), d[t]);
+    float xv[NC][8];
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) {
+      const int j = 16 * ct + n;
+      const float* xc = X + (size_t)(c0 + 8 * g) * R + min(j, R - 1);
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const float v = xc[(size_t)s * R];
+        xv[ct][s] = j < R ? v : 0.f;
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) acc[t][ct] = mfma_f32(d[t][s], xv[ct][s], acc[t][ct]);
   }
 #pragma unroll
-  for (int j = 0; j < R; ++j) A[(size_t)row * R + j] = z[j];
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[w][(t * NC + ct) * 4 + v][lane] = acc[t][ct][v];
+  __syncthreads();
+  // wave w adds the waves' sums of groups (t, ct) = w, w + 4, ...; the
+  // 16x16 output layout puts rows 4g .. 4g+3 of column n in lane (n, g)
+  for (int q = w; q < 4 * NC; q += kWaves) {
+    const int t = q / NC, ct = q % NC;
+    const int j = 16 * ct + n;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int idx = q * 4 + v;
+      const float sum =
+          ((red[0][idx][lane] + red[1][idx][lane]) + red[2][idx][lane]) + red[3][idx][lane];
+      const int row = row0 + 16 * t + 4 * g + v;
+      if (row < d_out && j < R) Yp[((size_t)ks * d_out + row) * R + j] = sum;
+    }
+  }
+}
+
+// Zp[p][c][j] = sum over rows o of chunk p of Delta[o][c] Y[o][j], as
+// Z^T = Y^T Delta.  A workgroup owns 128 columns and one row chunk; wave w
+// takes the 8-row steps w, w + 4, ... of the chunk.  Per 4-row step lane
+// (n, g) holds Y[o+g][16ct+n] (operand A) and columns 8n .. 8n+7 of row o+g
+// (one 16-byte load of each bf16 matrix); product e takes column 8n+e of
+// every lane, so accumulator (e, ct) of lane (n, g) ends with
+// Z[8n+e][16ct+4g+v], v = 0..3.  The waves' sums are added through LDS.
+template <int R>
+__global__ __launch_bounds__(256) void ms_tmul_kernel(const uint16_t* __restrict__ wf,
+                                                      const uint16_t* __restrict__ wb, int d_out,
+                                                      int d_in, int KT, const float* __restrict__ Y,
+                                                      float* __restrict__ Zp, FactorJob fj) {
+  constexpr int NC = (R + 15) / 16;
+  constexpr int E = 8 * NC * 4;
+  constexpr int NS = std::max(kWaves * E * 64, factor_smem<R>());
+  __shared__ __attribute__((aligned(16))) float sm[NS];
+  if (blockIdx.x == gridDim.x - 1 && fj.Gp) {
+    if (blockIdx.y == 0) gram_factor<R>(fj.Gp, fj.nb, fj.Mout, sm);
+    return;
+  }
+  float(*red)[E][64] = reinterpret_cast<float(*)[E][64]>(sm);
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int c = blockIdx.x * 128 + 8 * n;
+  const bool live = c < d_in;
+  const int cc = live ? c : 0;
+  const int p = blockIdx.y;
+  const int rows = ((d_out + KT - 1) / KT + 31) & ~31;
+  const int r0 = p * rows;
+  const int r1 = min(r0 + rows, d_out);
+  f32x4 acc[8][NC];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct) acc[e][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // two 4-row steps per pass with their loads first (the products are
+  // convergent operations, which the compiler does not unroll by a runtime
+  // trip count)
+  for (int o0 = r0 + 8 * w; o0 < r1; o0 += 8 * kWaves) {
+    float d[2][8], y[2][NC];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int o = o0 + 4 * h + g;
+      const int oc = min(o, d_out - 1);
+      const size_t base = (size_t)oc * d_in + cc;
+      delta8(ld128(wf + base), ld128(wb + base), d[h]);
+#pragma unroll
+      for (int ct = 0; ct < NC; ++ct) {
+        const int j = 16 * ct + n;
+        const float v = Y[(size_t)oc * R + min(j, R - 1)];
+        y[h][ct] = o < r1 && j < R ? v : 0.f;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+#pragma unroll
+        for (int ct = 0; ct < NC; ++ct) acc[e][ct] = mfma_f32(y[h][ct], d[h][e], acc[e][ct]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+#pragma unroll
+    for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[w][(e * NC + ct) * 4 + v][lane] = acc[e][ct][v];
+  __syncthreads();
+  if (!live) return;
+  for (int q = w; q < 8 * NC; q += kWaves) {
+    const int e = q / NC, ct = q % NC;
+    const int j = 16 * ct + 4 * g;
+    float s[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int idx = q * 4 + v;
+      s[v] = ((red[0][idx][lane] + red[1][idx][lane]) + red[2][idx][lane]) + red[3][idx][lane];
+    }
+    if (j < R)
+      *reinterpret_cast<float4*>(Zp + ((size_t)p * d_in + c + e) * R + j) =
+          make_float4(s[0], s[1], s[2], s[3]);
+  }
+}
+
+// The epilogue of a product, and the in-place scaling of a basis:
+//   A[row] = (sum_p P[p][row]) Min        (Min = identity when null)
+// over 64-row tiles, one per workgroup; with Gp, each workgroup also writes
+// the Gram partial of its rows, A_tile^T A_tile, to Gp[workgroup].  P may
+// alias A (parts = 1): every workgroup reads its whole tile before writing.
+template <int R>
+__global__ __launch_bounds__(256) void ms_epi_kernel(const float* P, int parts, int n,
+                                                     const float* __restrict__ Min, float* A,
+                                                     float* __restrict__ Gp) {
+  constexpr int RB = kEpiRows;
+  constexpr int Q4 = R / 4;    // float4 per row
+  constexpr int V4 = RB * Q4;  // float4 per tile
+  __shared__ float T[RB][R + 1];
+  __shared__ float Zs[RB][R + 1];
+  __shared__ float Ms[R][R];
+  const int t = threadIdx.x;
+  const int row0 = blockIdx.x * RB;
+  const size_t plane = (size_t)n * R;
+  for (int f = t; f < V4; f += 256) {
+    const int r = f / Q4, j = 4 * (f % Q4);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row0 + r < n) {
+      const float* src = P + (size_t)(row0 + r) * R + j;
+#pragma unroll 4
+      for (int p = 0; p < parts; ++p) {
+        const float4 v = *reinterpret_cast<const float4*>(src + p * plane);
+        s.x += v.x;
+        s.y += v.y;
+        s.z += v.z;
+        s.w += v.w;
+      }
+    }
+    T[r][j] = s.x;
+    T[r][j + 1] = s.y;
+    T[r][j + 2] = s.z;
+    T[r][j + 3] = s.w;
+  }
+  if (Min)
+    for (int e = t; e < R * R; e += 256) Ms[e / R][e % R] = Min[e];
+  __syncthreads();
+  for (int f = t; f < V4; f += 256) {
+    const int r = f / Q4, j = 4 * (f % Q4);
+    float z[4];
+    if (Min) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) z[u] = 0.f;
+#pragma unroll
+      for (int m = 0; m < R; ++m) {
+        const float x = T[r][m];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) z[u] += x * Ms[m][j + u];
+      }
+    } else {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) z[u] = T[r][j + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) Zs[r][j + u] = z[u];
+    if (row0 + r < n)
+      *reinterpret_cast<float4*>(A + (size_t)(row0 + r) * R + j) =
+          make_float4(z[0], z[1], z[2], z[3]);
+  }
+  if (!Gp) return;
+  __syncthreads();
+  for (int e = t; e < R * R; e += 256) {
+    const int a = e / R, b = e % R;
+    float s = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < RB; ++r) s += Zs[r][a] * Zs[r][b];
+    Gp[(size_t)blockIdx.x * R * R + e] = s;
+  }
+}
+
+// The Gram factorisation where no product kernel follows to host it.
+template <int R>
+__global__ __launch_bounds__(256) void ms_factor_kernel(const float* __restrict__ Gp, int nb,
+                                                        float* __restrict__ Mout) {
+  __shared__ __attribute__((aligned(16))) float sm[factor_smem<R>()];
+  gram_factor<R>(Gp, nb, Mout, sm);
 }
 
 // Omega [d_in][rank] into X [d_in][R], zero columns past the rank.
@@ -249,105 +476,170 @@ __global__ __launch_bounds__(256) void ms_pad_kernel(const float* __restrict__ o
   X[i] = j < rank ? omega[(size_t)c * rank + j] : 0.f;
 }
 
-// out[o][c] = bf16(W_base[o][c] + (1/k) sum_i sum_j Y_i[o][j] Z_i[c][j]);
-// tau (optional) the float32 mean.  A workgroup owns 16 rows x 128 columns;
-// thread t takes row t/16 and columns 8*(t%16) .. +7; each checkpoint's Y
-// rows and Z columns of the tile go through LDS.
+// out[o][c] = bf16(W_base[o][c] + (1/k) sum_i sum_j Q_i[o][j] Z_i[c][j]);
+// tau (optional) the float32 mean.  A workgroup owns 64 rows x 128 columns,
+// wave w the 32 x 64 quarter (w / 2, w % 2).  Per 16-wide block of j, lane
+// (n, g) loads Q[row n][4g .. 4g+3] of each 16-row tile (operand A) and
+// Z[column n][4g .. 4g+3] of each 16-column tile (operand B); product v
+// takes j = 4g + v.  The sums go through LDS so that each thread adds 8
+// consecutive columns of a row to W_base with 16-byte accesses.
 template <int R>
 __global__ __launch_bounds__(256) void ms_merge_kernel(const uint16_t* __restrict__ wb, int d_out,
-                                                       int d_in, int k, const float* __restrict__ Y,
+                                                       int d_in, int k, const float* __restrict__ Q,
                                                        const float* __restrict__ Z,
                                                        uint16_t* __restrict__ out,
                                                        float* __restrict__ tau) {
-  __shared__ float Ys[16][R];
-  __shared__ __attribute__((aligned(16))) float Zs[R][128];  // transposed: a thread's 8
-                                                              // columns are 32 contiguous bytes
+  constexpr int KB = (R + 15) / 16;
+  __shared__ __attribute__((aligned(16))) float C[64][128 + 4];
   const int t = threadIdx.x;
-  const int o0 = blockIdx.y * 16;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+  const int o0 = blockIdx.y * 64;
   const int c0 = blockIdx.x * 128;
-  const int lr = t >> 4;
-  const int lc = (t & 15) * 8;
-  float acc[8];
+  const int wr = o0 + 32 * (w >> 1);
+  const int wc = c0 + 64 * (w & 1);
+  f32x4 acc[2][4];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int i = 0; i < k; ++i) {
-    const float* Yi = Y + (size_t)i * d_out * R;
+    const float* Qi = Q + (size_t)i * d_out * R;
     const float* Zi = Z + (size_t)i * d_in * R;
-    __syncthreads();
-    for (int u = t; u < 16 * R; u += 256) {
-      const int r = u / R, j = u % R;
-      Ys[r][j] = Yi[(size_t)min(o0 + r, d_out - 1) * R + j];
-    }
-    for (int u = t; u < 128 * R; u += 256) {
-      const int cc = u / R, j = u % R;
-      Zs[j][cc] = Zi[(size_t)min(c0 + cc, d_in - 1) * R + j];
-    }
-    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < R; ++j) {
-      const float y = Ys[lr][j];
-      const float4 z0 = *reinterpret_cast<const float4*>(&Zs[j][lc]);
-      const float4 z1 = *reinterpret_cast<const float4*>(&Zs[j][lc + 4]);
-      acc[0] += y * z0.x;
-      acc[1] += y * z0.y;
-      acc[2] += y * z0.z;
-      acc[3] += y * z0.w;
-      acc[4] += y * z1.x;
-      acc[5] += y * z1.y;
-      acc[6] += y * z1.z;
-      acc[7] += y * z1.w;
+    for (int kb = 0; kb < KB; ++kb) {
+      const int kk = 16 * kb + 4 * g;
+      const bool in = kk < R;
+      const int kc = in ? kk : 0;
+      f32x4 a[2], b[4];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const f32x4 v =
+            *reinterpret_cast<const f32x4*>(Qi + (size_t)min(wr + 16 * u + n, d_out - 1) * R + kc);
+        a[u] = in ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 v =
+            *reinterpret_cast<const f32x4*>(Zi + (size_t)min(wc + 16 * u + n, d_in - 1) * R + kc);
+        b[u] = in ? v : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) acc[ra][cb] = mfma_f32(a[ra][v], b[cb][v], acc[ra][cb]);
     }
   }
-  const int o = o0 + lr;
-  const int c = c0 + lc;
-  if (o >= d_out || c >= d_in) return;
+#pragma unroll
+  for (int ra = 0; ra < 2; ++ra)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        C[32 * (w >> 1) + 16 * ra + 4 * g + v][64 * (w & 1) + 16 * cb + n] = acc[ra][cb][v];
+  __syncthreads();
   const float invk = 1.f / (float)k;
-  const size_t base = (size_t)o * d_in + c;
-  const u32x4 w = ld128(wb + base);
-  u32x4 r;
 #pragma unroll
-  for (int h = 0; h < 4; ++h) {
-    const float t0 = acc[2 * h] * invk;
-    const float t1 = acc[2 * h + 1] * invk;
-    r[h] = (uint32_t)f32_to_bf16_bits(bf16_lo(w[h]) + t0) |
-           ((uint32_t)f32_to_bf16_bits(bf16_hi(w[h]) + t1) << 16);
-    if (tau) {
-      tau[base + 2 * h] = t0;
-      tau[base + 2 * h + 1] = t1;
+  for (int s = 0; s < 4; ++s) {
+    const int seg = t + 256 * s;
+    const int r = seg >> 4;
+    const int cs = (seg & 15) * 8;
+    const int o = o0 + r;
+    const int c = c0 + cs;
+    if (o >= d_out || c >= d_in) continue;
+    const size_t base = (size_t)o * d_in + c;
+    const u32x4 wv = ld128(wb + base);
+    const float4 m0 = *reinterpret_cast<const float4*>(&C[r][cs]);
+    const float4 m1 = *reinterpret_cast<const float4*>(&C[r][cs + 4]);
+    const float m[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    u32x4 res;
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float t0 = m[2 * h] * invk;
+      const float t1 = m[2 * h + 1] * invk;
+      res[h] = (uint32_t)f32_to_bf16_bits(bf16_lo(wv[h]) + t0) |
+               ((uint32_t)f32_to_bf16_bits(bf16_hi(wv[h]) + t1) << 16);
+      if (tau) {
+        tau[base + 2 * h] = t0;
+        tau[base + 2 * h + 1] = t1;
+      }
     }
+    *reinterpret_cast<u32x4*>(out + base) = res;
   }
-  *reinterpret_cast<u32x4*>(out + base) = r;
 }
 
+// Workgroups of the epilogue over n rows.
+inline int64_t epi_groups(int64_t n) { return (n + kEpiRows - 1) / kEpiRows; }
+
+// Workspace in floats: Y, Z (k planes each), X0, the products' partial
+// planes, the Gram partials, the R x R inverse.
+struct Layout {
+  int64_t y, z, x0, part, gp, m, total;
+  Layout(int64_t d_out, int64_t d_in, int k, int64_t R) {
+    const int64_t parts = std::max((int64_t)ms_mul_slices(d_out, d_in) * d_out,
+                                   (int64_t)ms_tmul_chunks(d_out, d_in) * d_in);
+    y = 0;
+    z = y + k * d_out * R;
+    x0 = z + k * d_in * R;
+    part = x0 + d_in * R;
+    gp = part + parts * R;
+    m = gp + std::max(epi_groups(d_out), epi_groups(d_in)) * R * R;
+    total = m + R * R;
+  }
+};
+
+// One checkpoint's products.  Each epilogue with Gram partials leaves them
+// in Gp for `pending` rows; the next product kernel (or a factor kernel)
+// turns them into M = U^+, which the epilogue after it applies.
 template <int R>
 struct Plan {
-  int d_out, d_in, k;
-  float *Y, *Z, *X0, *Zp, *Gp, *Uf;
+  int d_out, d_in;
+  float *Part, *Gp, *M;
+  int64_t pending = 0;  // rows whose Gram partials wait in Gp (0: none)
   hipStream_t s;
 
-  // passes = 2 (CholeskyQR2) for the final basis; inside the iteration one
-  // pass is enough, since every step re-orthonormalises what it multiplies.
-  hipError_t orth(float* A, int n, int passes) const {
-    for (int pass = 0; pass < passes; ++pass) {
-      hipLaunchKernelGGL(ms_gram_kernel<R>, dim3(kGramChunks), dim3(R * R), 0, s, A, n, Gp);
-      hipLaunchKernelGGL(ms_chol_kernel<R>, dim3(1), dim3(R * R), 0, s, Gp, Uf);
-      hipLaunchKernelGGL(ms_scale_kernel<R>, dim3((n + 255) / 256), dim3(256), 0, s, A, n, Uf);
-    }
+  FactorJob job() {
+    FactorJob fj{pending ? Gp : nullptr, (int)epi_groups(pending), M};
+    pending = 0;
+    return fj;
+  }
+  // A [n][R] = (sum of `parts` partial planes) Min, with Gram partials
+  hipError_t epi(const float* P, int parts, int n, const float* Min, float* A, bool gram) {
+    hipLaunchKernelGGL(ms_epi_kernel<R>, dim3((unsigned)epi_groups(n)), dim3(256), 0, s, P, parts,
+                       n, Min, A, gram ? Gp : nullptr);
+    if (gram) pending = n;
     return hipGetLastError();
   }
-  hipError_t mul(const uint16_t* wf, const uint16_t* wb, const float* X, float* Yo) const {
-    constexpr int RW = R <= 16 ? 8 : 4;
-    hipLaunchKernelGGL((ms_mul_kernel<R, RW>), dim3((d_out + RW - 1) / RW), dim3(64), 0, s, wf, wb,
-                       d_out, d_in, X, Yo);
+  hipError_t factor() {
+    const FactorJob fj = job();
+    if (fj.Gp) hipLaunchKernelGGL(ms_factor_kernel<R>, dim3(1), dim3(256), 0, s, fj.Gp, fj.nb, M);
     return hipGetLastError();
   }
-  hipError_t tmul(const uint16_t* wf, const uint16_t* wb, const float* Yi, float* Zo) const {
-    hipLaunchKernelGGL(ms_tmul_kernel<R>, dim3((d_in + 127) / 128, kTmulChunks), dim3(64), 0, s,
-                       wf, wb, d_out, d_in, Yi, Zp);
-    const int64_t n = (int64_t)d_in * R;
-    hipLaunchKernelGGL(ms_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, Zp,
-                       n, Zo);
-    return hipGetLastError();
+  // Y = (Delta X) M with the pending factorisation (or X's own rows when
+  // none is pending), Gram partials of Y
+  hipError_t mul(const uint16_t* wf, const uint16_t* wb, const float* X, float* Y) {
+    const int ks = ms_mul_slices(d_out, d_in);
+    const FactorJob fj = job();
+    const int gx = (d_out + 63) / 64 + (fj.Gp ? 1 : 0);
+    hipLaunchKernelGGL(ms_mul_kernel<R>, dim3(gx, ks), dim3(256), 0, s, wf, wb, d_out, d_in, ks, X,
+                       Part, fj);
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : epi(Part, ks, d_out, fj.Gp ? M : nullptr, Y, true);
+  }
+  // Z = (Delta^T Y) M with the pending factorisation, Gram partials of Z
+  // when asked
+  hipError_t tmul(const uint16_t* wf, const uint16_t* wb, const float* Y, float* Z, bool gram) {
+    const int kt = ms_tmul_chunks(d_out, d_in);
+    const FactorJob fj = job();
+    const int gx = (d_in + 127) / 128 + (fj.Gp ? 1 : 0);
+    hipLaunchKernelGGL(ms_tmul_kernel<R>, dim3(gx, kt), dim3(256), 0, s, wf, wb, d_out, d_in, kt, Y,
+                       Part, fj);
+    const hipError_t e = hipGetLastError();
+    return e != hipSuccess ? e : epi(Part, kt, d_in, fj.Gp ? M : nullptr, Z, gram);
   }
 };
 
@@ -355,38 +647,38 @@ template <int R>
 hipError_t run_monosoup(const uint16_t* const* w_ft, int k, const uint16_t* w_base, int d_out,
                         int d_in, int rank, int q, const float* omega, uint16_t* out, float* tau,
                         char* ws, hipStream_t s) {
-  Plan<R> P;
-  P.d_out = d_out;
-  P.d_in = d_in;
-  P.k = k;
-  P.s = s;
-  const size_t nY = (size_t)k * d_out * R, nZ = (size_t)k * d_in * R;
+  const Layout L(d_out, d_in, k, R);
   float* f = reinterpret_cast<float*>(ws);
-  P.Y = f;
-  P.Z = P.Y + nY;
-  P.X0 = P.Z + nZ;
-  P.Zp = P.X0 + (size_t)d_in * R;
-  P.Gp = P.Zp + (size_t)kTmulChunks * d_in * R;
-  P.Uf = P.Gp + (size_t)kGramChunks * R * R;
+  float* const X0 = f + L.x0;
   hipLaunchKernelGGL(ms_pad_kernel, dim3((unsigned)(((size_t)d_in * R + 255) / 256)), dim3(256), 0,
-                     s, omega, d_in, rank, R, P.X0);
+                     s, omega, d_in, rank, R, X0);
   hipError_t e = hipGetLastError();
   for (int i = 0; i < k && e == hipSuccess; ++i) {
-    float* Yi = P.Y + (size_t)i * d_out * R;
-    float* Zi = P.Z + (size_t)i * d_in * R;
-    e = P.mul(w_ft[i], w_base, P.X0, Yi);
-    if (e == hipSuccess) e = P.orth(Yi, d_out, q == 0 ? 2 : 1);
+    Plan<R> P;
+    P.d_out = d_out;
+    P.d_in = d_in;
+    P.s = s;
+    P.Part = f + L.part;
+    P.Gp = f + L.gp;
+    P.M = f + L.m;
+    float* Yi = f + L.y + (size_t)i * d_out * R;
+    float* Zi = f + L.z + (size_t)i * d_in * R;
+    // Y and Z are stored unscaled; their bases are Y U_Y^+ and Z U_Z^+
+    e = P.mul(w_ft[i], w_base, X0, Yi);
     for (int it = 0; it < q && e == hipSuccess; ++it) {
-      e = P.tmul(w_ft[i], w_base, Yi, Zi);
-      if (e == hipSuccess) e = P.orth(Zi, d_in, 1);
+      e = P.tmul(w_ft[i], w_base, Yi, Zi, true);
       if (e == hipSuccess) e = P.mul(w_ft[i], w_base, Zi, Yi);
-      if (e == hipSuccess) e = P.orth(Yi, d_out, it == q - 1 ? 2 : 1);
     }
-    if (e == hipSuccess) e = P.tmul(w_ft[i], w_base, Yi, Zi);
+    // the final basis: a second CholeskyQR pass on the explicit Y U_Y^+,
+    // then Z = Delta^T Q and Q itself
+    if (e == hipSuccess) e = P.factor();
+    if (e == hipSuccess) e = P.epi(Yi, 1, d_out, P.M, Yi, true);
+    if (e == hipSuccess) e = P.tmul(w_ft[i], w_base, Yi, Zi, false);
+    if (e == hipSuccess) e = P.epi(Yi, 1, d_out, P.M, Yi, false);
   }
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(ms_merge_kernel<R>, dim3((d_in + 127) / 128, (d_out + 15) / 16), dim3(256),
-                     0, s, w_base, d_out, d_in, k, P.Y, P.Z, out, tau);
+  hipLaunchKernelGGL(ms_merge_kernel<R>, dim3((d_in + 127) / 128, (d_out + 63) / 64), dim3(256),
+                     0, s, w_base, d_out, d_in, k, f + L.y, f + L.z, out, tau);
   return hipGetLastError();
 }
 
@@ -395,9 +687,7 @@ hipError_t run_monosoup(const uint16_t* const* w_ft, int k, const uint16_t* w_ba
 int monosoup_width(int rank) { return rank <= 8 ? 8 : (rank <= 16 ? 16 : 32); }
 
 size_t monosoup_workspace_bytes(int64_t d_out, int64_t d_in, int k, int rank) {
-  const int64_t R = monosoup_width(rank);
-  return 4u * (size_t)(k * d_out * R + k * d_in * R + d_in * R + (int64_t)kTmulChunks * d_in * R +
-                       (int64_t)kGramChunks * R * R + R * R);
+  return 4u * (size_t)Layout(d_out, d_in, k, monosoup_width(rank)).total;
 }
 
 hipError_t launch_monosoup(const uint16_t* const* w_ft, int k, const uint16_t* w_base, int d_out,
