@@ -78,6 +78,43 @@ def test_monosoup_ranks_and_iterations(rank, q):
     check(wb, wf, omega, rank, q)
 
 
+def _iteration_subspace_tau(dl, omega, q):
+    """float64 projection of each task vector onto the span of
+    (Delta Delta^T)^q Delta Omega: the subspace q steps of orthogonal
+    iteration reach from Omega, whatever orthonormalisation runs between the
+    steps (re-orthonormalised here by numpy's QR only to keep the numbers in
+    range).  Their mean."""
+    out = 0.0
+    for d in dl:
+        k = np.linalg.qr(d @ omega)[0]
+        for _ in range(q):
+            k = np.linalg.qr(d @ np.linalg.qr(d.T @ k)[0])[0]
+        out = out + k @ (k.T @ d)
+    return out / len(dl)
+
+
+@pytest.mark.parametrize("q", [0, 1, 2])
+def test_monosoup_iteration_subspace_few_steps(q):
+    """With zero to two power iterations the subspace has not converged to
+    the top singular one (the exact-truncation tests need four), so this
+    checks what the iteration computes: tau_i is Delta_i projected onto the
+    span of (Delta_i Delta_i^T)^q Delta_i Omega.  q = 0 runs the factorisation
+    on its own before the second CholeskyQR pass."""
+    rank = 8
+    wb, wf, omega = checkpoints(256, 384, 2, rank, seed=40 + q)
+    merged, tau = T.monosoup_merge(wf, wb, rank, q, omega, want_tau=True)
+    torch.cuda.synchronize()
+    base = bf16_bits_to_f32(bits16(wb)).astype(np.float64)
+    dl = [bf16_bits_to_f32(bits16(w)).astype(np.float64) - base for w in wf]
+    ref = _iteration_subspace_tau(dl, omega.cpu().numpy().astype(np.float64), q)
+    t = tau.cpu().numpy().astype(np.float64)
+    rel = np.linalg.norm(t - ref) / np.linalg.norm(ref)
+    assert rel <= 1e-4, f"q={q}: tau_mean rel_fro {rel:.2e}"
+    # the few-step subspace is not the top one: the exact truncation differs
+    _, t_svd = M.merge([bits16(w) for w in wf], bits16(wb), rank)
+    assert np.linalg.norm(t - t_svd) / np.linalg.norm(t_svd) > 10 * rel or q > 0
+
+
 def test_monosoup_checkpoint_equal_to_base():
     """A task vector of zero has no directions: its truncation is zero, and a
     merge of the base with itself returns the base bit for bit."""
