@@ -37,3 +37,4 @@ from .bitdelta import (  # noqa: F401
     reconstruct,
     status_string,
 )
+from .deltafile import delta_blob, load_delta, read_delta_header, save_delta  # noqa: F401

@@ -110,6 +110,41 @@ def test_cache_loads_and_policy_match_oracle():
             assert torch.equal(slots[s][:n].cpu(), blobs[v]), v
 
 
+def test_cache_from_delta_files(tmp_path):
+    """Variants written to delta files and read back into page-locked blobs
+    (tenant_linear_layers_amd.deltafile) serve the cache exactly as the blobs
+    they were written from: the blob built from the device tensors equals
+    the test's own, the read-back blob equals it byte for byte, and every
+    linear through a slot loaded from it equals the direct call."""
+    shapes = [(192, 512), (320, 1024)]
+    mode = T.ALPHA_PER_ROW
+    V = 3
+    bases, packs, alphas, blobs = make_variants(shapes, V, mode, 61)
+    loaded = []
+    for v in range(V):
+        built = T.delta_blob(list(zip(packs[v], alphas[v])), shapes, mode)
+        assert torch.equal(built, blobs[v]), v
+        path = tmp_path / f"variant{v}.bdlt"
+        T.save_delta(path, built, shapes, mode)
+        blob, shp, m = T.load_delta(path)
+        assert shp == shapes and m == mode and blob.is_pinned()
+        assert torch.equal(blob, blobs[v]), v
+        loaded.append(blob)
+    cache, slots = make_cache(V, 2, 0, 0, loaded)
+    copy = torch.cuda.Stream()
+    g = S.generator(62)
+    xs = [S.draw_activations(4, d_in, g).to(DEV) for _, d_in in shapes]
+    for v in [2, 0, 1, 2, 1]:
+        act, slot, _ = cache.acquire(v, copy)
+        assert act != T.CACHE_FULL and slot is not None
+        for i, (p, a) in enumerate(T.delta_views(slot, shapes, mode)):
+            y = T.linear(xs[i], bases[i], p, a, mode)
+            y_direct = T.linear(xs[i], bases[i], packs[v][i], alphas[v][i], mode)
+            assert torch.equal(y.view(torch.int16), y_direct.view(torch.int16)), (v, i)
+        cache.release(v)
+    torch.cuda.synchronize()
+
+
 def test_cache_mixed_batches_without_synchronisation():
     """Batches hold several variants at once and nothing waits on the host:
     loads overlap earlier batches' kernels; each mixed-variant output equals
