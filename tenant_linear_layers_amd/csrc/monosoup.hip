@@ -218,11 +218,22 @@ __device__ void gram_factor(const float* __restrict__ Gp, int nb, float* __restr
   }
 }
 
+// Position of 16-byte chunk c of a staged 64-byte row r: the operand reads
+// of 16 consecutive rows at one chunk hit distinct banks whether the LDS
+// serves 8 or 16 lanes of a 16-byte read per cycle.
+__device__ __forceinline__ int ms_swz(int r, int c) {
+  return c ^ (((r >> 2) & 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 1));
+}
+
 // Yp[ks][o][j] = sum over the workgroup's columns c of Delta[o][c] X[c][j];
 // X [d_in][R].  A workgroup owns 64 rows (four 16-row tiles) and the 32-wide
-// column blocks 4 ks + w, 4 ks + w + 4 KS, ... for wave w.  Lane (n, g)
-// holds columns 8g .. 8g+7 of a block for row n of each tile (one 16-byte
-// load of each bf16 matrix) and X's rows 8g .. 8g+7 of the block for column
+// column blocks 4 ks + w, 4 ks + w + 4 KS, ... for wave w.  Each wave stages
+// its block of both bf16 matrices (64 rows x 64 bytes each) by buffer loads
+// to LDS, four lanes per row (every quad of lanes one contiguous 64-byte
+// piece, which the address unit serves about four times faster than loads
+// in the operand layout), one block ahead in a ring of two stages; X's rows
+// of the block go to registers with it.  Lane (n, g) then reads columns
+// 8g .. 8g+7 of row n of each tile and holds X's rows 8g .. 8g+7 for column
 // n of each 16-column tile; product s takes the block's columns s, 8+s,
 // 16+s, 24+s.  The waves' sums are added through LDS in wave order.
 template <int R>
@@ -230,53 +241,111 @@ __global__ __launch_bounds__(256) void ms_mul_kernel(const uint16_t* __restrict_
                                                      const uint16_t* __restrict__ wb, int d_out,
                                                      int d_in, int KS, const float* __restrict__ X,
                                                      float* __restrict__ Yp, FactorJob fj) {
-  constexpr int NC = (R + 15) / 16;  // 16-column tiles of X and Y
-  constexpr int E = 4 * NC * 4;      // accumulator floats per lane
-  constexpr int NS = std::max(kWaves * E * 64, factor_smem<R>());
-  __shared__ __attribute__((aligned(16))) float sm[NS];
+  constexpr int NC = (R + 15) / 16;         // 16-column tiles of X and Y
+  constexpr int E = 4 * NC * 4;             // accumulator floats per lane
+  constexpr int kWaveStage = 2 * 64 * 64;   // a wave's block of both matrices
+  constexpr int kStage = kWaves * kWaveStage;
+  constexpr int kLoads = 8 + 8 * NC;        // vector loads per block
+  static_assert(kWaves * E * 64 * 4 <= kStage && factor_smem<R>() * 4 <= kStage,
+                "the reduction and the factorisation fit in the first stage");
+  static_assert(kLoads < 64, "vmcnt holds 6 bits");
+  // one array per stage: the compiler's wait insertion tells separate LDS
+  // arrays apart, so reads of one stage do not wait for loads into the other
+  __shared__ __attribute__((aligned(16))) char st0[kStage];
+  __shared__ __attribute__((aligned(16))) char st1[kStage];
+  float* sm = reinterpret_cast<float*>(st0);
   if (blockIdx.x == gridDim.x - 1 && fj.Gp) {
     if (blockIdx.y == 0) gram_factor<R>(fj.Gp, fj.nb, fj.Mout, sm);
     return;
   }
-  float(*red)[E][64] = reinterpret_cast<float(*)[E][64]>(sm);
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform per wave
   const int n = lane & 15;
   const int g = lane >> 4;
   const int row0 = blockIdx.x * 64;
   const int ks = blockIdx.y;
   const int nblk = d_in >> 5;
-  size_t rbase[4];
+  // rows past d_out lie beyond the buffers and read as zero
+  const int nbytes = min(64, d_out - row0) * d_in * 2;
+  const uint16_t* fblk = wf + (size_t)row0 * d_in;
+  const uint16_t* bblk = wb + (size_t)row0 * d_in;
+  // staging instruction j: rows 16j .. 16j+15, lane l row 16j + l/4 at
+  // position l%4 (global chunk ms_swz(row, l%4)); operand reads of tile t:
+  // row 16t + n, chunk g
+  int voff[4], roff[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) rbase[t] = (size_t)min(row0 + 16 * t + n, d_out - 1) * d_in + 8 * g;
+  for (int j = 0; j < 4; ++j) {
+    const int r = 16 * j + (lane >> 2);
+    voff[j] = r * d_in * 2 + (ms_swz(r, lane & 3) << 4);
+    const int rr = 16 * j + n;
+    roff[j] = rr * 64 + (ms_swz(rr, g) << 4);
+  }
+  const int kb0 = ks * kWaves + w;
+  const int kstep = KS * kWaves;
+  const int nmine = kb0 < nblk ? (nblk - 1 - kb0) / kstep + 1 : 0;
+
   f32x4 acc[4][NC];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) acc[t][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int kb = ks * kWaves + w; kb < nblk; kb += KS * kWaves) {
-    const int c0 = kb << 5;
-    float d[4][8];
+  float xv[2][NC][8];
+  auto issue = [&](int i, int su) {
+    const int c0 = (kb0 + i * kstep) << 5;
+    char* st = (su == 0 ? st0 : st1) + w * kWaveStage;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) delta8(ld128(wf + rbase[t] + c0), ld128(wb + rbase[t] + c0), d[t]);
-    float xv[NC][8];
+    for (int j = 0; j < 4; ++j) lds_bload16(fblk, nbytes, voff[j], c0 * 2, st + j * 1024);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) lds_bload16(bblk, nbytes, voff[j], c0 * 2, st + 4096 + j * 1024);
 #pragma unroll
     for (int ct = 0; ct < NC; ++ct) {
-      const int j = 16 * ct + n;
-      const float* xc = X + (size_t)(c0 + 8 * g) * R + min(j, R - 1);
+      const float* xc = X + (size_t)(c0 + 8 * g) * R + min(16 * ct + n, R - 1);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const float v = xc[(size_t)s * R];
-        xv[ct][s] = j < R ? v : 0.f;
-      }
+      for (int s = 0; s < 8; ++s) xv[su][ct][s] = xc[(size_t)s * R];
     }
+  };
+  if (nmine > 0) issue(0, 0);
+  for (int i0 = 0; i0 < nmine; i0 += 2) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
+    for (int su = 0; su < 2; ++su) {
+      const int i = i0 + su;
+      // the stage about to be refilled was read by the previous block: its
+      // LDS reads complete before the buffer loads may write it, and the
+      // loads stay below this point
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      __builtin_amdgcn_sched_barrier(0);
+      // past the wave's last block the issue re-reads that block into the
+      // stage nobody reads: every block issues the same number of loads
+      issue(min(i + 1, nmine - 1), su ^ 1);
+      __builtin_amdgcn_sched_barrier(0);  // the next block's loads stay together, here
+      __builtin_amdgcn_s_waitcnt((kLoads & 15) | ((kLoads >> 4) << 14) | (0x7 << 4) |
+                                 (0xF << 8));  // vmcnt only: block i is in
+      // No branch on i: past the wave's last block X is taken as zero (the
+      // stage holds a re-read of that block), which adds nothing; with a
+      // branch the compiler moves the next block's loads into it.
+      const bool live = i < nmine;
+      const char* st = (su == 0 ? st0 : st1) + w * kWaveStage;
+      float d[4][8];
 #pragma unroll
       for (int t = 0; t < 4; ++t)
+        delta8(*reinterpret_cast<const u32x4*>(st + roff[t]),
+               *reinterpret_cast<const u32x4*>(st + 4096 + roff[t]), d[t]);
+      float xm[NC][8];
 #pragma unroll
-        for (int ct = 0; ct < NC; ++ct) acc[t][ct] = mfma_f32(d[t][s], xv[ct][s], acc[t][ct]);
+      for (int ct = 0; ct < NC; ++ct)
+#pragma unroll
+        for (int s = 0; s < 8; ++s) xm[ct][s] = live && 16 * ct + n < R ? xv[su][ct][s] : 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int ct = 0; ct < NC; ++ct) acc[t][ct] = mfma_f32(d[t][s], xm[ct][s], acc[t][ct]);
+    }
   }
+  __builtin_amdgcn_s_waitcnt(0);  // the last re-reads have landed
+  __syncthreads();                // the first stage becomes the reduction area
+  float(*red)[E][64] = reinterpret_cast<float(*)[E][64]>(sm);
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
