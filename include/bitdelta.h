@@ -387,8 +387,9 @@ int bitdelta_router_pending(bitdelta_router* router, int32_t* n);
  *
  *   w_ft         HOST array of k device pointers, bf16 [d_out, d_in] each
  *   k            1 .. BITDELTA_MONOSOUP_MAX_CHECKPOINTS
- *   w_base       device, bf16 [d_out, d_in]; d_out at most 1048560 (the
- *                general shape rules of this header apply otherwise)
+ *   w_base       device, bf16 [d_out, d_in]; d_out at most 4194240 and d_in
+ *                at most 16777152 (the general shape rules of this header
+ *                apply otherwise)
  *   rank         1 .. min(BITDELTA_MONOSOUP_MAX_RANK, d_out, d_in)
  *   power_iters  0 .. BITDELTA_MONOSOUP_MAX_POWER_ITERS
  *   omega        device, float32 [d_in, rank], the caller's Gaussian start

@@ -16,9 +16,12 @@ namespace {
 
 constexpr int64_t kInt32Max = 2147483647;
 constexpr int64_t kMaxElems = int64_t(1) << 40;
-// The MonoSoup merge kernel's grid takes 16 rows per workgroup in its y
+// The MonoSoup merge kernel's grid takes 64 rows per workgroup in its y
 // dimension (at most 65535 workgroups).
-constexpr int64_t kMonosoupMaxRows = 65535 * 16;
+constexpr int64_t kMonosoupMaxRows = 65535 * 64;
+// The product Delta X addresses a workgroup's 64 rows of each matrix with
+// 32-bit buffer offsets: 64 d_in bf16 values must stay below 2 GiB.
+constexpr int64_t kMonosoupMaxCols = (int64_t(1) << 24) - 64;
 
 bool shape_ok(int64_t d_out, int64_t d_in) {
   return d_out >= 1 && d_in >= 64 && d_in % 64 == 0 && d_out <= kInt32Max && d_in <= kInt32Max &&
@@ -303,7 +306,7 @@ BD_EXPORT size_t bitdelta_monosoup_workspace_size(int64_t d_out, int64_t d_in, i
                                                   int32_t rank) {
   if (!shape_ok(d_out, d_in) || k < 1 || k > BITDELTA_MONOSOUP_MAX_CHECKPOINTS || rank < 1 ||
       rank > BITDELTA_MONOSOUP_MAX_RANK || rank > d_out || rank > d_in ||
-      d_out > kMonosoupMaxRows)
+      d_out > kMonosoupMaxRows || d_in > kMonosoupMaxCols)
     return 0;
   return bd::monosoup_workspace_bytes(d_out, d_in, k, rank);
 }
@@ -317,7 +320,7 @@ BD_EXPORT int bitdelta_monosoup_merge(const uint16_t* const* w_ft, int32_t k,
   if (!shape_ok(d_out, d_in) || k < 1 || k > BITDELTA_MONOSOUP_MAX_CHECKPOINTS || rank < 1 ||
       rank > BITDELTA_MONOSOUP_MAX_RANK || rank > d_out || rank > d_in || power_iters < 0 ||
       power_iters > BITDELTA_MONOSOUP_MAX_POWER_ITERS || d_out * d_in >= kMaxElems / 4 ||
-      d_out > kMonosoupMaxRows)
+      d_out > kMonosoupMaxRows || d_in > kMonosoupMaxCols)
     return BITDELTA_ERR_SHAPE;
   for (int i = 0; i < k; ++i)
     if (!w_ft[i]) return BITDELTA_ERR_NULL;

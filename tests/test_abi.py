@@ -156,7 +156,10 @@ def test_monosoup_argument_checks():
                                          ctypes.c_void_p(tau), ctypes.c_void_p(wsp), wsb, None)
     assert call(rank=0) == 2 and call(rank=33) == 2 and call(k=0) == 2 and call(k=65) == 2
     assert call(q=-1) == 2 and call(q=65) == 2 and call(d_in=100) == 2 and call(d_out=4, rank=8) == 2
-    assert call(d_out=65535 * 16 + 1, d_in=64) == 2     # past the merge grid's rows
+    assert call(d_out=65535 * 64 + 1, d_in=64) == 2     # past the merge grid's rows
+    assert call(d_out=64, d_in=1 << 24) == 2             # past the product's 32-bit offsets
+    assert T.monosoup_workspace_size(64, 1 << 24, 2, 8) == 0
+    assert T.monosoup_workspace_size(64, (1 << 24) - 64, 2, 8) > 0
     assert call(omega=0) == 1 and call(out=0) == 1 and call(wsp=0) == 1
     assert call(out=D + 8) == 3 and call(omega=C + 2) == 3
     assert call(wsb=ws - 1) == 6
