@@ -35,6 +35,7 @@ from .bitdelta import ALPHA_PER_MATRIX, ALPHA_PER_ROW, delta_layout, delta_views
 
 MAGIC = b"BDLT"
 VERSION = 1
+MAX_MATRICES = 1 << 16  # bounds the header a reader accepts (about 1 MiB)
 _FIXED = struct.Struct("<4sIIIIIQII")
 _SHAPE = struct.Struct("<QQ")
 _ALIGN = 256
@@ -78,6 +79,8 @@ def delta_blob(pieces, shapes, alpha_mode: int, pin_memory: bool = True) -> torc
     [(packed, alpha), ...] (int64 [d_out, d_in/64] and float32 tensors, on
     any device), page-locked unless pin_memory is False."""
     shapes = _check_shapes(shapes, alpha_mode)
+    if len(shapes) > MAX_MATRICES:
+        raise ValueError(f"at most {MAX_MATRICES} matrices per delta")
     if len(pieces) != len(shapes):
         raise ValueError(f"{len(pieces)} (packed, alpha) pairs for {len(shapes)} shapes")
     _, total = delta_layout(shapes, alpha_mode)
@@ -99,6 +102,8 @@ def save_delta(path, blob: torch.Tensor, shapes, alpha_mode: int) -> int:
     """Write one variant's delta (a uint8 blob in delta_layout order, host or
     device) to path; returns the file's size in bytes."""
     shapes = _check_shapes(shapes, alpha_mode)
+    if len(shapes) > MAX_MATRICES:
+        raise ValueError(f"at most {MAX_MATRICES} matrices per delta")
     _, total = delta_layout(shapes, alpha_mode)
     if blob.dtype != torch.uint8 or blob.dim() != 1 or blob.numel() != total:
         raise ValueError(f"the blob must be a 1-D uint8 tensor of {total} bytes for these shapes")
@@ -123,7 +128,10 @@ def read_delta_header(path):
             raise ValueError(f"{path}: not a delta file (magic {magic!r})")
         if version != VERSION:
             raise ValueError(f"{path}: delta file version {version}, this reader knows {VERSION}")
-        if align != _ALIGN or hsize % align or hsize < _FIXED.size + n * _SHAPE.size:
+        if not 1 <= n <= MAX_MATRICES:
+            raise ValueError(f"{path}: {n} matrices in the header (1 .. {MAX_MATRICES})")
+        need = -(-(_FIXED.size + n * _SHAPE.size) // _ALIGN) * _ALIGN
+        if align != _ALIGN or hsize != need:
             raise ValueError(f"{path}: header size {hsize} or alignment {align} is invalid")
         rest = f.read(hsize - _FIXED.size)
         if len(rest) < hsize - _FIXED.size:

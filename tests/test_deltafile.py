@@ -106,6 +106,22 @@ def test_damaged_header_is_refused(tmp_path, offset, match):
         T.load_delta(path, pin_memory=False)
 
 
+def test_oversized_header_fields_are_refused_before_reading(tmp_path):
+    """A header announcing a huge matrix count or header size is refused
+    from its fixed fields, before anything that size is read."""
+    path, raw = _saved(tmp_path)
+    big = bytearray(raw)
+    struct.pack_into("<I", big, 12, 1 << 30)          # matrices
+    _write(path, big)
+    with pytest.raises(ValueError, match="matrices in the header"):
+        T.load_delta(path, pin_memory=False)
+    big = bytearray(raw)
+    struct.pack_into("<I", big, 20, (1 << 31) - 256)  # header bytes
+    _write(path, big)
+    with pytest.raises(ValueError, match="header size"):
+        T.load_delta(path, pin_memory=False)
+
+
 def test_truncated_files_are_refused(tmp_path):
     path, raw = _saved(tmp_path)
     for cut in (10, 100, len(raw) - 1):
