@@ -33,9 +33,9 @@
  *   GPU work is enqueued on it asynchronously.  The returned status reports
  *   argument checks (done on the host before anything is enqueued) and
  *   launch errors only.
- * - Shapes: d_out >= 1, d_in >= 64 and d_in % 64 == 0, M >= 1.  d_out,
- *   d_in and M must each fit in a signed 32-bit int, and d_out*d_in below
- *   2^40.
+ * - Shapes: d_out >= 1, d_in >= 64 and d_in % 64 == 0, M >= 1.  d_out and
+ *   M must each fit in a signed 32-bit int, d_in is at most 2^30, and
+ *   d_out*d_in is below 2^40.
  * - Alignment: x, w_ft, w_base, packed and y must be 16-byte aligned.
  * - Outputs must not overlap inputs (checked: BITDELTA_ERR_OVERLAP).
  * - Data errors are encoded in values, never reported by status: a scope
@@ -136,8 +136,9 @@ int bitdelta_compress_noalloc(const uint16_t* w_ft, const uint16_t* w_base, int6
  * rounded to bf16 (nearest even).  M <= 64 runs the decode-shaped kernel
  * (base and sign products on the matrix cores, one pass over W_base and the
  * packed signs); larger M runs the prefill GEMM, which rebuilds bf16 tiles of
- * W_eff in LDS; its 32-bit buffer offsets limit it to d_in <= 4194240
- * (BITDELTA_ERR_SHAPE beyond that when M > 64).
+ * W_eff in LDS.  Both address their tiles with 32-bit buffer offsets, which
+ * limits d_in to 16777152 when M <= 64 and to 4194240 when M > 64
+ * (BITDELTA_ERR_SHAPE beyond).
  *
  *   x       device, bf16 [M, d_in]
  *   w_base  device, bf16 [d_out, d_in]
@@ -160,7 +161,8 @@ int bitdelta_linear(const uint16_t* x, int64_t M, const uint16_t* w_base,
  * tokens and each distinct variant's packed signs once.  An id outside
  * [-1, n_variants) makes that token's output row NaN (nothing out of bounds
  * is read).  Tokens are processed in groups of 64 (one pass over the weights
- * per group).
+ * per group).  d_in is at most 16777152 (the decode-shaped kernel's 32-bit
+ * buffer offsets; BITDELTA_ERR_SHAPE beyond).
  *
  *   x            device, bf16 [M, d_in]
  *   variant_ids  device, int32 [M]

@@ -23,8 +23,12 @@ constexpr int64_t kMonosoupMaxRows = 65535 * 64;
 // 32-bit buffer offsets: 64 d_in bf16 values must stay below 2 GiB.
 constexpr int64_t kMonosoupMaxCols = (int64_t(1) << 24) - 64;
 
+// Row lengths up to 2^30 keep every per-row element and chunk index of the
+// kernels (a row's chunks of 512 elements, rounded up) inside a 32-bit int.
+constexpr int64_t kMaxDin = int64_t(1) << 30;
+
 bool shape_ok(int64_t d_out, int64_t d_in) {
-  return d_out >= 1 && d_in >= 64 && d_in % 64 == 0 && d_out <= kInt32Max && d_in <= kInt32Max &&
+  return d_out >= 1 && d_in >= 64 && d_in % 64 == 0 && d_out <= kInt32Max && d_in <= kMaxDin &&
          d_out * d_in < kMaxElems;
 }
 
@@ -189,7 +193,8 @@ BD_EXPORT int bitdelta_linear(const uint16_t* x, int64_t M, const uint16_t* w_ba
                               int64_t d_out, int64_t d_in, uint16_t* y, void* stream) {
   if (!x || !w_base || !packed || !alpha || !y) return BITDELTA_ERR_NULL;
   if (!shape_ok(d_out, d_in) || M < 1 || M > kInt32Max || M * d_in >= kMaxElems ||
-      M * d_out >= kMaxElems || (M > bd::kMaxSkinnyTokens && d_in > bd::kPrefillMaxDin))
+      M * d_out >= kMaxElems ||
+      d_in > (M > bd::kMaxSkinnyTokens ? bd::kPrefillMaxDin : bd::kSkinnyMaxDin))
     return BITDELTA_ERR_SHAPE;
   if (alpha_mode != BITDELTA_ALPHA_PER_MATRIX && alpha_mode != BITDELTA_ALPHA_PER_ROW)
     return BITDELTA_ERR_MODE;
@@ -233,7 +238,7 @@ BD_EXPORT int bitdelta_linear_multi(const uint16_t* x, int64_t M, const int32_t*
                                     void* stream) {
   if (!x || !variant_ids || !w_base || !packed || !alpha || !y) return BITDELTA_ERR_NULL;
   if (!shape_ok(d_out, d_in) || M < 1 || M > kInt32Max || M * d_in >= kMaxElems ||
-      M * d_out >= kMaxElems)
+      M * d_out >= kMaxElems || d_in > bd::kSkinnyMaxDin)
     return BITDELTA_ERR_SHAPE;
   if (alpha_mode != BITDELTA_ALPHA_PER_MATRIX && alpha_mode != BITDELTA_ALPHA_PER_ROW)
     return BITDELTA_ERR_MODE;

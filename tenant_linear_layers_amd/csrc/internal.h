@@ -8,6 +8,10 @@ namespace bd {
 
 constexpr int kMaxVariants = 64;   // equals BITDELTA_MAX_VARIANTS
 constexpr int kMaxSkinnyTokens = 64;
+// The decode-shaped kernels address a workgroup's 16 rows of W_base and the
+// token rows of x (at most 64) with 32-bit buffer offsets: 64 * d_in * 2
+// bytes must stay below 2^31.
+constexpr int64_t kSkinnyMaxDin = (int64_t(1) << 24) - 64;
 // The prefill GEMM addresses one tile's rows of W_base (up to 256 rows) with
 // 32-bit buffer offsets: 256 * d_in * 2 bytes must stay below 2^31.
 constexpr int64_t kPrefillMaxTileBytes = 2147483647;

@@ -82,6 +82,8 @@ def test_compress_argument_errors():
     assert _c(f(A, B, 0, 64, 1, C, D, None, 0, None)) == 2       # d_out
     assert _c(f(A, B, 4, 0, 1, C, D, None, 0, None)) == 2
     assert _c(f(A, B, 1 << 31, 64, 1, C, D, None, 0, None)) == 2
+    assert _c(f(A, B, 8, (1 << 30) + 64, 1, C, D, None, 0, None)) == 2   # row length cap
+    assert _c(f(A, B, 8, 1 << 30, 7, C, D, None, 0, None)) == 4          # passes the shape check
     assert _c(f(A, B, 4, 64, 2, C, D, None, 0, None)) == 4       # mode
     assert _c(f(A + 2, B, 4, 64, 1, C, D, None, 0, None)) == 3   # alignment
     assert _c(f(A, B, 4, 64, 0, C, D, None, 0, None)) == 6       # no workspace
@@ -104,6 +106,10 @@ def test_linear_argument_errors():
     assert _c(f(A, 65, B, C, D, 1, 8, big, E, None)) == 2
     assert _c(f(A, 65, B, C, D, 7, 8, 4194240, E, None)) == 4    # passes the shape check
     assert _c(f(A, 64, B, C, D, 7, 8, big, E, None)) == 4
+    # The decode-shaped path (M <= 64) addresses 16 weight rows and up to 64
+    # token rows with 32-bit offsets: d_in above 16777152 is rejected there.
+    assert _c(f(A, 1, B, C, D, 1, 8, 16777152 + 64, E, None)) == 2
+    assert _c(f(A, 64, B, C, D, 7, 8, 16777152, E, None)) == 4   # passes the shape check
 
 
 def test_multi_argument_errors():
@@ -120,6 +126,8 @@ def test_multi_argument_errors():
     assert _c(f(A, 4, B + 2, E, 2, pa, aa, 1, 8, 64, E + 65536, None)) == 3
     assert _c(f(A, 4, B, E, 2, pa, aa, 3, 8, 64, E + 65536, None)) == 4
     assert _c(f(A, 4, B, E, 2, pa, aa, 1, 8, 32, E + 65536, None)) == 2
+    assert _c(f(A, 4, B, E, 2, pa, aa, 1, 8, 16777152 + 64, E + (1 << 30), None)) == 2
+    assert _c(f(A, 4, B, E, 2, pa, aa, 3, 8, 16777152, E + (1 << 30), None)) == 4
     assert _c(f(A, 4, B, E, 2, pa, aa, 1, 8, 64, A, None)) == 9
 
 
