@@ -91,10 +91,11 @@ __device__ __forceinline__ int blocks_of_wave(int wv, int nblk, int NW) {
 }
 
 // Sum the NW waves' partial accumulators (LDS, fixed order) and store y.
+// rowof(c) is the output row of the workgroup's column c (0..15);
 // out(slot, o, sw, ss, m) returns the output value and sets its token m.
-template <int MT, int NW, class Out>
+template <int MT, int NW, class RowOf, class Out>
 __device__ __forceinline__ void reduce_and_store(float* red, const f32x4 (&accw)[MT],
-                                                 const f32x4 (&accs)[MT], int row0, int M,
+                                                 const f32x4 (&accs)[MT], RowOf rowof, int M,
                                                  int d_out, uint16_t* y, Out out) {
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x >> 6;
@@ -119,7 +120,7 @@ __device__ __forceinline__ void reduce_and_store(float* red, const f32x4 (&accw)
     }
     // MFMA 16x16 output layout: lane l holds rows 4*(l/16)+v of column l%16.
     const int slot = 16 * t + 4 * (l >> 4) + v;
-    const int o = row0 + (l & 15);
+    const int o = rowof(l & 15);
     if (slot < M && o < d_out) {
       int m;
       const float yv = out(slot, o, sw, ss, m);
@@ -201,7 +202,7 @@ __global__ __launch_bounds__(NW * kWave) void linear_decode_kernel(const SkinnyA
 
   const float* alpha = a.alpha[0];
   const int per_row = a.per_row;
-  reduce_and_store<MT, NW>(red, accw, accs, row0, M, a.d_out, a.y,
+  reduce_and_store<MT, NW>(red, accw, accs, [&](int c) { return row0 + c; }, M, a.d_out, a.y,
                            [&](int slot, int o, float sw, float ss, int& m) {
                              m = slot;
                              return sw + (per_row ? alpha[o] : alpha[0]) * ss;
@@ -223,7 +224,19 @@ __global__ __launch_bounds__(NW * kWave) void linear_decode_kernel(const SkinnyA
 // multiplied, with a constant count of loads per block, so one vmcnt wait
 // finds block i complete.  XD: 4-row x staging instructions per 16-token tile
 // (tokens past M re-read the last token; their outputs are never stored).
-template <int XD, int NW, int U>
+//
+// IL (interleaved rows): workgroup b of G takes four chunks of 4 rows, chunk
+// k being rows 4(b + G k) .. 4(b + G k) + 3, instead of rows 16b .. 16b+15,
+// and each wave starts at block b mod (its block count) of its range.
+// Every row is still taken by exactly one workgroup and one lane column;
+// rows past d_out (in the last chunks) read as zero from W_base, re-read the
+// last row's signs and are not stored.  W_base is then addressed through one
+// resource over the whole matrix, so this needs (d_out + 16) * d_in * 2 <
+// 2^31.
+// Measured on 4096 x 4096, 8192 x 8192, 10240 x 8192 and 28672 x 8192: 2-7%
+// faster at 1 to 16 tokens; on 8192 x 28672 it was 1-3% slower, so it is
+// used for d_in up to 8192.
+template <int XD, int NW, int U, bool IL>
 __global__ __launch_bounds__(NW * kWave) void linear_decode_ring_kernel(const SkinnyArgs a) {
   constexpr int kXR = 4 * XD;                    // staged x rows
   constexpr int kStage = (16 + kXR) * 256;       // W_base rows, then x rows
@@ -245,23 +258,29 @@ __global__ __launch_bounds__(NW * kWave) void linear_decode_ring_kernel(const Sk
   // DMA sources, byte offsets at the first block: W_base rows 4j..4j+3 and
   // x rows 4j..4j+3 per instruction, lane (lane/16, c = lane%16) fetching
   // chunk c ^ row.
-  const uint16_t* wblk = a.w + (size_t)row0 * d_in;
-  const int wbytes = nrows * d_in * 2;
+  // Row of the workgroup's column c (0..15).  G (the grid) from d_out, not
+  // gridDim: reading the dispatch packet would delay the first loads.
+  const int G = (a.d_out + 15) >> 4;
+  auto rowof = [&](int c) { return IL ? 4 * (blockIdx.x + G * (c >> 2)) + (c & 3) : row0 + c; };
+  // W_base through one resource: the workgroup's rows, or with IL the whole
+  // matrix (below 2^31 bytes; columns past d_out then read as zero).
+  const uint16_t* wsrc = IL ? a.w : a.w + (size_t)row0 * d_in;
+  const int wbytes = IL ? a.d_out * d_in * 2 : nrows * d_in * 2;
   const int xbytes = M * d_in * 2;
   int wdoff[4], xdoff[XD];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int r = 4 * j + (lane >> 4);
-    wdoff[j] = min(r, nrows - 1) * d_in * 2 + (((lane & 15) ^ r) << 4);
+    wdoff[j] = (IL ? rowof(r) : min(r, nrows - 1)) * d_in * 2 + (((lane & 15) ^ r) << 4);
   }
 #pragma unroll
   for (int j = 0; j < XD; ++j) {
     const int r = 4 * j + (lane >> 4);
     xdoff[j] = min(r, M - 1) * d_in * 2 + (((lane & 15) ^ r) << 4);
   }
-  // Sign words: lane 4r + j loads dword j of row r's 16 bytes of the block.
-  const uint8_t* sblk = reinterpret_cast<const uint8_t*>(a.packed[0]) + (size_t)row0 * (d_in >> 3);
-  const uint32_t srow = min(lane >> 2, nrows - 1) * (d_in >> 3);
+  // Sign words: lane 4r + j loads dword j of column r's 16 bytes of the block.
+  const uint8_t* sblk = reinterpret_cast<const uint8_t*>(a.packed[0]) + (IL ? 0 : (size_t)row0 * (d_in >> 3));
+  const uint32_t srow = (IL ? min(rowof(lane >> 2), a.d_out - 1) : min(lane >> 2, nrows - 1)) * (d_in >> 3);
   const int sj = (lane & 3) << 2;
   const int perm_src = ((n << 2) + g) << 2;
   // Operand reads: W row n, x row min(n, kXR - 1), chunk 4g + q.
@@ -277,12 +296,16 @@ __global__ __launch_bounds__(NW * kWave) void linear_decode_ring_kernel(const Sk
   const int nmine = blocks_of_wave(wv, nblk, NW);
   const bool half_tail = (d_in & 127) != 0;
 
+  // Block of the wave's i-th step (IL: rotated by the workgroup index).
+  const int rot = IL && nmine > 0 ? (int)(blockIdx.x % (unsigned)nmine) : 0;
+  auto blk = [&](int i) { return wv + NW * (i + rot < nmine ? i + rot : i + rot - nmine); };
+
   uint32_t sreg[U];
   auto issue = [&](int i, int u) {
-    const int k0 = (wv + NW * i) << 7;
+    const int k0 = blk(i) << 7;
     char* st = ring + u * kStage;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) lds_bload16(wblk, wbytes, wdoff[j], 2 * k0, st + j * 1024);
+    for (int j = 0; j < 4; ++j) lds_bload16(wsrc, wbytes, wdoff[j], 2 * k0, st + j * 1024);
 #pragma unroll
     for (int j = 0; j < XD; ++j) lds_bload16(a.x, xbytes, xdoff[j], 2 * k0, st + (16 + 4 * j) * 256);
     const uint32_t off = srow + min((k0 >> 3) + sj, (d_in >> 3) - 4);
@@ -312,7 +335,7 @@ __global__ __launch_bounds__(NW * kWave) void linear_decode_ring_kernel(const Sk
                                  (0x7 << 4) | (0xF << 8));  // vmcnt only
       if (i < nmine) {  // uniform
         char* st = ring + u * kStage;
-        if (half_tail && wv + NW * i == nblk - 1) {
+        if (half_tail && blk(i) == nblk - 1) {
           // a final 64-wide block: zero x's columns 64..127 (read from other bytes)
           for (int e = lane; e < kXR * 8; e += kWave) {
             const int r = e >> 3;
@@ -341,7 +364,7 @@ __global__ __launch_bounds__(NW * kWave) void linear_decode_ring_kernel(const Sk
   const f32x4 aw[1] = {accw}, as[1] = {accs};
   const float* alpha = a.alpha[0];
   const int per_row = a.per_row;
-  reduce_and_store<1, NW>(red, aw, as, row0, M, a.d_out, a.y,
+  reduce_and_store<1, NW>(red, aw, as, rowof, M, a.d_out, a.y,
                           [&](int slot, int o, float sw, float ss, int& m) {
                             m = slot;
                             return sw + (per_row ? alpha[o] : alpha[0]) * ss;
@@ -1237,8 +1260,13 @@ bool decode_use_valu() { return env_is("BITDELTA_DECODE_KERNEL", "valu"); }
 
 template <int XD, int NW, int U>
 hipError_t launch_decode_ring(const SkinnyArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((linear_decode_ring_kernel<XD, NW, U>), dim3((a.d_out + 15) / 16),
-                     dim3(NW * kWave), 0, stream, a);
+  // interleaved rows reach d_out + 14: their offsets stay below 2^31
+  if (a.d_in <= 8192 && ((int64_t)a.d_out + 16) * a.d_in * 2 < (int64_t(1) << 31))
+    hipLaunchKernelGGL((linear_decode_ring_kernel<XD, NW, U, true>), dim3((a.d_out + 15) / 16),
+                       dim3(NW * kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL((linear_decode_ring_kernel<XD, NW, U, false>), dim3((a.d_out + 15) / 16),
+                       dim3(NW * kWave), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -181,6 +181,24 @@ def test_linear_decode_ragged(shape, m):
     assert_y_close(y, oracle_y(x, wb, packed, alpha, mode), f"decode {shape} M={m}")
 
 
+@pytest.mark.parametrize("shape", [(1000, 512), (4100, 256), (33, 8192), (48, 8256), (20, 64)])
+@pytest.mark.parametrize("m", [1, 4, 16])
+def test_linear_decode_interleaved_rows(shape, m):
+    """Up to 16 tokens with d_in <= 8192 a workgroup takes four chunks of 4
+    rows spread over the matrix (chunks past d_out partly or wholly empty)
+    and starts each wave at a rotated block; 8256 takes contiguous rows.
+    Every output is compared, starting from a NaN-filled y."""
+    d_out, d_in = shape
+    wb, wf = S.small_pair(d_out, d_in, 0.02, 1e-3, seed=d_out + m)
+    x = S.draw_activations(m, d_in, S.generator(7 * m))
+    wb, wf, x = to_dev(wb, wf, x)
+    for mode in (0, 1):
+        packed, alpha = T.compress(wf, wb, mode)
+        y = torch.full((m, d_out), float("nan"), dtype=torch.bfloat16, device=DEV)
+        T.linear(x, wb, packed, alpha, mode, y=y)
+        assert_y_close(y, oracle_y(x, wb, packed, alpha, mode), f"decode {shape} M={m} mode {mode}")
+
+
 @pytest.mark.parametrize("shape", [(130, 192), (257, 640), (128, 64)])
 @pytest.mark.parametrize("m", [65, 100, 256, 300, 513])
 def test_linear_prefill_ragged(shape, m):
