@@ -70,6 +70,38 @@ def test_host_rounding_matches_oracle():
     assert float(Fraction(s, 4096 << 48)) == 2.0 ** -12
 
 
+def test_host_rounding_near_float_midpoints():
+    """The rounding takes a double-precision quotient unless it lies within a
+    few of its last places of a point halfway between two floats, where it
+    falls back to long division.  Sums placed exactly on such midpoints and
+    then moved by k units of the quotient's last place (k = -20..20, both
+    sides of the fallback window) must still round as the oracle's long
+    division does; so must random sums over row lengths like d_in."""
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        n = int(rng.integers(1, 1 << 24))
+        m = int(rng.integers(1 << 23, 1 << 24))          # 24-bit significand
+        s_mid = (2 * m + 1) * n                            # S/n = m + 1/2
+        s_mid <<= int(rng.integers(0, max(1, 63 - s_mid.bit_length())))
+        unit = max(1, s_mid >> 52)                         # about one unit of q's last place
+        for k in range(-20, 21):
+            s = s_mid + k * unit
+            if s <= 0:
+                continue
+            want = O.rne_ratio_to_f32_bits(s, n << 48)
+            assert T.ratio_to_f32_bits(s, n) == want, (s, n, k)
+    # exact halfway quotients (q = S/n exactly, taken without the long division)
+    for n in (64, 4096, 8192, 28672, 3 << 20):
+        for _ in range(200):
+            m = int(rng.integers(1 << 23, 1 << 24))
+            s = ((2 * m + 1) * n) << int(rng.integers(0, 12))
+            assert T.ratio_to_f32_bits(s, n) == O.rne_ratio_to_f32_bits(s, n << 48), (s, n)
+    for _ in range(6000):
+        n = int(rng.choice([64, 192, 4096, 8192, 28672, 1 << 20]))
+        s = int(rng.integers(1, 1 << 63))
+        assert T.ratio_to_f32_bits(s, n) == O.rne_ratio_to_f32_bits(s, n << 48), (s, n)
+
+
 def _c(status):
     return int(status)
 
