@@ -254,7 +254,9 @@ __global__ __launch_bounds__(256) void ms_mul_kernel(const uint16_t* __restrict_
   __shared__ __attribute__((aligned(16))) char st0[kStage];
   __shared__ __attribute__((aligned(16))) char st1[kStage];
   float* sm = reinterpret_cast<float*>(st0);
-  if (blockIdx.x == gridDim.x - 1 && fj.Gp) {
+  // the extra workgroup after the row groups (its index from d_out, not
+  // gridDim: a read of the dispatch packet would delay every first load)
+  if (blockIdx.x == (unsigned)((d_out + 63) >> 6) && fj.Gp) {
     if (blockIdx.y == 0) gram_factor<R>(fj.Gp, fj.nb, fj.Mout, sm);
     return;
   }
@@ -385,7 +387,7 @@ __global__ __launch_bounds__(256) void ms_tmul_kernel(const uint16_t* __restrict
   constexpr int E = 8 * NC * 4;
   constexpr int NS = std::max(kWaves * E * 64, factor_smem<R>());
   __shared__ __attribute__((aligned(16))) float sm[NS];
-  if (blockIdx.x == gridDim.x - 1 && fj.Gp) {
+  if (blockIdx.x == (unsigned)((d_in + 127) >> 7) && fj.Gp) {  // the extra workgroup
     if (blockIdx.y == 0) gram_factor<R>(fj.Gp, fj.nb, fj.Mout, sm);
     return;
   }
