@@ -788,10 +788,10 @@ struct PairGroups {
 };
 
 template <int NS>
-__device__ void build_pairs(PairGroups<NS>& G, const int32_t* ids, int M, int n_variants) {
+__device__ void build_pairs(PairGroups<NS>& G, int vt, int M, int n_variants) {
   const int t = threadIdx.x;
   if (t < M) {
-    const int v = ids != nullptr ? ids[t] : 0;  // no ids: every token uses variant 0
+    const int v = vt;  // thread t's token's variant id (0 for a batch without ids)
     // order: variants 0..V-1, then base-only tokens, then invalid ids
     G.key[t] = (v >= 0 && v < n_variants) ? v : (v == -1 ? n_variants : n_variants + 1);
   }
@@ -859,7 +859,14 @@ __device__ void build_pairs(PairGroups<NS>& G, const int32_t* ids, int M, int n_
 // sign words of its next block are requested before the current block is
 // multiplied.  The sign rows of the pairs' variants are looked up once per
 // batch, outside the loop over blocks.
-template <int MT, int NW, int KP, bool WLDS, int WPE, bool EARLY>
+//
+// EW (early weights, for batches with variant ids): the first block of
+// W_base does not depend on the grouping, so it is requested into registers
+// before the sort (after the token ids, so that waiting for the ids does not
+// wait for it) and written to its LDS stage after.  A batch without ids
+// sorts at once, and there the wait for these loads before x is requested
+// cost 2-3%.
+template <int MT, int NW, int KP, bool WLDS, int WPE, bool EARLY, bool EW>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(WPE))) void
 linear_multi_pairs_kernel(const SkinnyArgs a) {
   static_assert(!EARLY || (MT <= 2 && WLDS), "early staging keeps every tile's x in registers");
@@ -887,7 +894,39 @@ linear_multi_pairs_kernel(const SkinnyArgs a) {
   char* ws = xs + kXRows * kXRowB;  // the wave's 16 rows of W_base for one block
   float* red = reinterpret_cast<float*>(smem);
 
-  build_pairs(G, a.ids, M, a.n_variants);
+  // Token ids first (no branch around the load, so that the compiler counts
+  // the loads issued after it exactly).
+  const int vt = a.ids != nullptr ? a.ids[min((int)threadIdx.x, M - 1)] : 0;
+  const int row0 = blockIdx.x * 16;
+  const int nrows = min(16, a.d_out - row0);
+  const uint16_t* wblk = a.w + (size_t)row0 * d_in;
+  const int wbytes = nrows * d_in * 2;
+  // W_base staging (WLDS), like x: instruction j writes rows 4j..4j+3 of
+  // the block, lane (lane/16, c = lane%16) fetching chunk c ^ row of its row
+  // (rows past d_out re-read the last row).  Byte offsets at the first
+  // block.  Without WLDS the lane loads its own 64 bytes in operand layout.
+  const int woff = (min(n, nrows - 1) * d_in + (g << 5)) * 2;  // + 2*k0 per block
+  int wdoff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * j + (lane >> 4);
+    wdoff[j] = min(r, nrows - 1) * d_in * 2 + (((lane & 15) ^ r) << 4);
+  }
+  const int nblk = (d_in + 127) >> 7;
+  const int nmine = blocks_of_wave(wv, nblk, NW);
+  u32x4 w0[4];
+  if (EW) {
+    // the first block of W_base (a wave with no blocks reads zeros past d_in)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w0[j] = WLDS ? bload128(wblk, wbytes, wdoff[j], 2 * (wv << 7))
+                   : bload128(wblk, wbytes, woff + 16 * j, 2 * (wv << 7));
+  }
+  build_pairs(G, vt, M, a.n_variants);
+  if (EW && WLDS) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(ws + j * 1024 + (lane << 4)) = w0[j];
+  }
   const int npair = G.npair;
   const int nbatch = max((npair + KP - 1) / KP, 1);  // one pass at least, for the base
   // Pair and variant tables, lane p holding entry p.
@@ -911,21 +950,6 @@ linear_multi_pairs_kernel(const SkinnyArgs a) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) foff[q] = (((4 * g + q) ^ n) << 4);
 
-  const int row0 = blockIdx.x * 16;
-  const int nrows = min(16, a.d_out - row0);
-  const uint16_t* wblk = a.w + (size_t)row0 * d_in;
-  const int wbytes = nrows * d_in * 2;
-  // W_base staging (WLDS), like x: instruction j writes rows 4j..4j+3 of
-  // the block, lane (lane/16, c = lane%16) fetching chunk c ^ row of its row
-  // (rows past d_out re-read the last row).  Byte offsets at the first
-  // block.  Without WLDS the lane loads its own 64 bytes in operand layout.
-  const int woff = (min(n, nrows - 1) * d_in + (g << 5)) * 2;  // + 2*k0 per block
-  int wdoff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 4 * j + (lane >> 4);
-    wdoff[j] = min(r, nrows - 1) * d_in * 2 + (((lane & 15) ^ r) << 4);
-  }
   // Sign words are loaded with four lanes per row (lane 4r + j reads dword
   // j of row r's 16 bytes of the block: every quad of lanes reads one
   // contiguous piece, which the address unit serves four times faster than
@@ -936,8 +960,6 @@ linear_multi_pairs_kernel(const SkinnyArgs a) {
   const int perm_src = ((n << 2) + g) << 2;            // byte address of the source lane
   const size_t prow = (size_t)row0 * (d_in >> 3);      // this workgroup's rows in a packed matrix
 
-  const int nblk = (d_in + 127) >> 7;
-  const int nmine = blocks_of_wave(wv, nblk, NW);
   const bool half_tail = (d_in & 127) != 0;
 
   f32x4 accw[MT];
@@ -967,6 +989,10 @@ linear_multi_pairs_kernel(const SkinnyArgs a) {
 
     uint32_t sc[KP];
     u32x4 wc[4];
+    if (EW && !WLDS && batch == 0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) wc[q] = w0[q];
+    }
     auto stage_w = [&](int i) {
       const int k0 = (wv + NW * i) << 7;
       if (WLDS) {
@@ -1003,7 +1029,7 @@ linear_multi_pairs_kernel(const SkinnyArgs a) {
       for (int u = 0; u < KP; ++u) sn[u] = 0u;
       if (nmine > 0) {
         stage_x(0);
-        if (batch == 0) stage_w(0);
+        if (batch == 0 && !EW) stage_w(0);
 #pragma unroll
         for (int u = 0; u < KP; ++u)
           if ((builds >> (p0 + u)) & 1) sn[u] = sign_word(0, u);
@@ -1071,7 +1097,7 @@ linear_multi_pairs_kernel(const SkinnyArgs a) {
     } else {
     if (nmine > 0) {
       stage_x(0);
-      if (batch == 0) stage_w(0);
+      if (batch == 0 && !EW) stage_w(0);
 #pragma unroll
       for (int u = 0; u < KP; ++u)
         if ((builds >> (p0 + u)) & 1) load_s1(0, u);
@@ -1283,8 +1309,12 @@ hipError_t launch_multi(const SkinnyArgs& a, hipStream_t stream) {
 
 template <int MT, int NW, int KP, bool WLDS, int WPE, bool EARLY>
 hipError_t launch_multi_pairs(const SkinnyArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((linear_multi_pairs_kernel<MT, NW, KP, WLDS, WPE, EARLY>),
-                     dim3((a.d_out + 15) / 16), dim3(NW * kWave), 0, stream, a);
+  if (a.ids != nullptr)
+    hipLaunchKernelGGL((linear_multi_pairs_kernel<MT, NW, KP, WLDS, WPE, EARLY, true>),
+                       dim3((a.d_out + 15) / 16), dim3(NW * kWave), 0, stream, a);
+  else
+    hipLaunchKernelGGL((linear_multi_pairs_kernel<MT, NW, KP, WLDS, WPE, EARLY, false>),
+                       dim3((a.d_out + 15) / 16), dim3(NW * kWave), 0, stream, a);
   return hipGetLastError();
 }
 
