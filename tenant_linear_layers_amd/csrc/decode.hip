@@ -85,6 +85,22 @@ __device__ __forceinline__ u32x4 quad(const uint32_t (&s)[16], int q) {
   return v;
 }
 
+// Sign words in the operand layout from a coalesced load.  The quad of lanes
+// 4r..4r+3 reads row r's 16 bytes (4 sign words) of a block; lane 4r + j
+// takes dword sign_quad_dword(4r + j), i.e. dword j for r < 8 and dword
+// (j + 2) mod 4 for r >= 8 (the row's two halves swapped).  Lane n + 16g
+// then takes dword g of row n from lane sign_perm_src(n, g) by one
+// ds_bpermute.  With plain dword j at lane 4r + j, the 32 lanes of each half
+// of the wave read source lanes that pair up 32 apart, a two-way bank
+// conflict on every permute (measured: one conflict cycle per active LDS
+// cycle); with the halves of rows 8..15 swapped they cover all 32 banks.
+__device__ __forceinline__ int sign_quad_dword(int lane) {
+  return ((lane & 3) + ((lane >> 5) << 1)) & 3;
+}
+__device__ __forceinline__ int sign_perm_src(int n, int g) {
+  return (n << 2) + ((g + ((n >> 3) << 1)) & 3);
+}
+
 // Number of a wave's blocks when NW waves take nblk blocks round-robin.
 __device__ __forceinline__ int blocks_of_wave(int wv, int nblk, int NW) {
   return wv < nblk ? (nblk - 1 - wv) / NW + 1 : 0;
@@ -278,11 +294,12 @@ __global__ __launch_bounds__(NW * kWave) void linear_decode_ring_kernel(const Sk
     const int r = 4 * j + (lane >> 4);
     xdoff[j] = min(r, M - 1) * d_in * 2 + (((lane & 15) ^ r) << 4);
   }
-  // Sign words: lane 4r + j loads dword j of column r's 16 bytes of the block.
+  // Sign words: the quad of lanes 4r..4r+3 loads column r's 16 bytes of the
+  // block (halves swapped for r >= 8, see sign_quad_dword).
   const uint8_t* sblk = reinterpret_cast<const uint8_t*>(a.packed[0]) + (IL ? 0 : (size_t)row0 * (d_in >> 3));
   const uint32_t srow = (IL ? min(rowof(lane >> 2), a.d_out - 1) : min(lane >> 2, nrows - 1)) * (d_in >> 3);
-  const int sj = (lane & 3) << 2;
-  const int perm_src = ((n << 2) + g) << 2;
+  const int sj = sign_quad_dword(lane) << 2;
+  const int perm_src = sign_perm_src(n, g) << 2;
   // Operand reads: W row n, x row min(n, kXR - 1), chunk 4g + q.
   const int xr = min(n, kXR - 1);
   int wro[4], xro[4];
@@ -950,14 +967,14 @@ linear_multi_pairs_kernel(const SkinnyArgs a) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) foff[q] = (((4 * g + q) ^ n) << 4);
 
-  // Sign words are loaded with four lanes per row (lane 4r + j reads dword
-  // j of row r's 16 bytes of the block: every quad of lanes reads one
-  // contiguous piece, which the address unit serves four times faster than
-  // the operand layout), then moved to the operand layout (lane n + 16g
-  // holds dword g of row n) by one cross-lane permute.
+  // Sign words are loaded with four lanes per row (the quad of lanes
+  // 4r..4r+3 reads row r's 16 bytes of the block: every quad of lanes reads
+  // one contiguous piece, which the address unit serves four times faster
+  // than the operand layout), then moved to the operand layout (lane n + 16g
+  // holds dword g of row n) by one cross-lane permute (sign_quad_dword).
   const uint32_t srow = min(lane >> 2, nrows - 1) * (d_in >> 3);
-  const int sj = (lane & 3) << 2;
-  const int perm_src = ((n << 2) + g) << 2;            // byte address of the source lane
+  const int sj = sign_quad_dword(lane) << 2;
+  const int perm_src = sign_perm_src(n, g) << 2;       // byte address of the source lane
   const size_t prow = (size_t)row0 * (d_in >> 3);      // this workgroup's rows in a packed matrix
 
   const bool half_tail = (d_in & 127) != 0;
