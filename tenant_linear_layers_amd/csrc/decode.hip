@@ -1370,10 +1370,20 @@ hipError_t launch_linear_skinny(const SkinnyArgs& a, hipStream_t stream) {
   }
   // Ring stages: two up to 8 tokens (80 and 96 KB of LDS per workgroup),
   // one for 16 (64 KB: two workgroups per CU), measured on 4096 x 4096,
-  // 28672 x 8192 and 8192 x 28672.
+  // 28672 x 8192 and 8192 x 28672.  Up to 8 tokens, four waves per workgroup
+  // (half the LDS, twice the blocks per wave) where the row groups number
+  // 256..320: 4096 x 4096 at 1 / 4 / 8 tokens 8.72 / 8.87 / 9.25 -> 8.49 /
+  // 8.57 / 8.70 us, 5120 x 4096 12.6 -> 12.1 us, 4096 x 8192 14.55 -> 14.2
+  // us.  With 128 or fewer groups (2048 rows: 6.7 -> 7.1 us) and with 512 or
+  // 640 (8192, 10240 rows: 2-4% slower) eight waves stay faster; at 384
+  // (6144 rows) it went either way (-1.8% with d_in 4096, +1.3% with 8192).
   if (!decode_use_old() && a.M <= 16) {
-    if (a.M <= 4) return launch_decode_ring<1, 8, 2>(a, stream);
-    if (a.M <= 8) return launch_decode_ring<2, 8, 2>(a, stream);
+    const int groups = (a.d_out + 15) / 16;
+    const bool four = groups >= 256 && groups <= 320;
+    if (a.M <= 4)
+      return four ? launch_decode_ring<1, 4, 2>(a, stream) : launch_decode_ring<1, 8, 2>(a, stream);
+    if (a.M <= 8)
+      return four ? launch_decode_ring<2, 4, 2>(a, stream) : launch_decode_ring<2, 8, 2>(a, stream);
     return launch_decode_ring<4, 8, 1>(a, stream);
   }
   // Beyond 16 tokens the pairs kernel with every token on variant 0 (no
