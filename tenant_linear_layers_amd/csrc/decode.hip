@@ -1369,14 +1369,14 @@ hipError_t launch_linear_skinny(const SkinnyArgs& a, hipStream_t stream) {
     return launch_decode_valu<4, 4, 4>(a, stream);
   }
   // Two ring stages; up to 8 tokens eight waves (80 and 96 KB of LDS per
-  // workgroup), measured on 4096 x 4096, 28672 x 8192 and 8192 x 28672,
-  // except that four waves per workgroup
-  // (half the LDS, twice the blocks per wave) run where the row groups
-  // number 256..320: 4096 x 4096 at 1 / 4 / 8 tokens 8.72 / 8.87 / 9.25 -> 8.49 /
-  // 8.57 / 8.70 us, 5120 x 4096 12.6 -> 12.1 us, 4096 x 8192 14.55 -> 14.2
-  // us.  With 128 or fewer groups (2048 rows: 6.7 -> 7.1 us) and with 512 or
-  // 640 (8192, 10240 rows: 2-4% slower) eight waves stay faster; at 384
-  // (6144 rows) it went either way (-1.8% with d_in 4096, +1.3% with 8192).
+  // workgroup, measured on 4096 x 4096, 28672 x 8192 and 8192 x 28672),
+  // but four (half the LDS, twice the blocks per wave) where the row groups
+  // number 256..320: 4096 x 4096 at 1 / 4 / 8 tokens 8.72 / 8.87 / 9.25 ->
+  // 8.49 / 8.57 / 8.70 us, 5120 x 4096 12.6 -> 12.1 us, 4096 x 8192 14.55
+  // -> 14.2 us.  With 128 or fewer groups (2048 rows: 6.7 -> 7.1 us) and
+  // with 512 or 640 (8192, 10240 rows: 2-4% slower) eight waves stay
+  // faster; at 384 (6144 rows) it went either way (-1.8% with d_in 4096,
+  // +1.3% with 8192).
   if (!decode_use_old() && a.M <= 16) {
     const int groups = (a.d_out + 15) / 16;
     const bool four = groups >= 256 && groups <= 320;
