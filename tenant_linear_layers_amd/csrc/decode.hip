@@ -1359,6 +1359,13 @@ hipError_t launch_multi_tiles(const SkinnyArgs& a, hipStream_t stream) {
   if (a.M <= 32)
     return wide ? launch_multi_pairs<2, 4, 12, true, 3, false>(a, stream)
                 : launch_multi_pairs<2, 8, 12, true, 2, false>(a, stream);
+  // Up to 64 tokens: two workgroups of four waves per CU (75.5 KB of LDS
+  // each, 16 pairs per batch) where there are at least 320 row groups, else
+  // one of eight waves.  Four waves: 28672 x 8192 at 64 tokens 380 -> 340
+  // us, at 48 tokens 356 -> 316 us, 8192 x 8192 113 -> 105 us, 5120 and
+  // 6144 x 4096 68 -> 58 us, 8192 x 28672 363 -> 357 us; with 256 row
+  // groups (4096 x 4096) it was 22% slower (one workgroup, four waves a CU).
+  if ((a.d_out + 15) / 16 >= 320) return launch_multi_pairs<4, 4, 16, false, 2, false>(a, stream);
   return launch_multi_pairs<4, 8, 20, false, 2, false>(a, stream);
 }
 
