@@ -411,11 +411,11 @@ def test_multi_more_distinct_variants_than_prefetched(shape):
 
 
 @pytest.mark.parametrize("shape", [(12345, 192), (24600, 128)])
-@pytest.mark.parametrize("m", [20, 32])
+@pytest.mark.parametrize("m", [20, 32, 50, 64])
 def test_multi_many_row_groups_full_output(shape, m):
     """More 16-row groups than the GPU holds at once (772 and 1538, the last
     one ragged), with a base-only token: y starts as NaN and every output is
-    compared."""
+    compared.  From 33 tokens these take the four-wave workgroups."""
     mode = m % 2
     wb, packs, alphas = _variants(*shape, 9, seed=95 + m, mode=mode)
     ids = S.zipf_ids(m, 9, seed=96 + m)
