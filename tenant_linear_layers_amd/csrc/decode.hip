@@ -1343,16 +1343,17 @@ bool multi_use_windows() { return env_is("BITDELTA_MULTI_KERNEL", "windows"); }
 
 // The (tile, variant) pairs kernel for a batch of M tokens.
 hipError_t launch_multi_tiles(const SkinnyArgs& a, hipStream_t stream) {
-  // Four waves per workgroup (three workgroups per CU) where there are
-  // enough 16-row groups to fill the CUs that way (at least 1.5 per CU);
-  // eight otherwise (measured: 28672 x 8192 at 32 tokens 246 against 265 us,
-  // 8192 x 8192 76 us; 4096 x 4096 at 16 tokens 25.0 against 21.8 us).
+  // Four waves per workgroup (three workgroups per CU) where there are at
+  // least 320 groups of 16 rows; eight otherwise (measured: 28672 x 8192 at
+  // 32 tokens 246 against 265 us, 8192 x 8192 76 us, 5120 x 4096 at 16 and
+  // 32 tokens 26.9 and 38.6 against 31.0 and 44.6 us; with 256 groups, 4096
+  // x 4096 at 16 tokens, 25.0 against 21.8 us).
   // Early staging (every load of the next block issued at the top of the
   // current one) for one token tile: 28672 x 8192 at 16 tokens 165 -> 157
   // us.  At two tiles it needs 32 more registers a lane: with three
   // workgroups per CU they spill (472 us), with two it is no faster (246
   // against 242 us).
-  const bool wide = (a.d_out + 15) / 16 >= 384;
+  const bool wide = (a.d_out + 15) / 16 >= 320;
   if (a.M <= 16)
     return wide ? launch_multi_pairs<1, 4, 12, true, 3, true>(a, stream)
                 : launch_multi_pairs<1, 8, 12, true, 2, true>(a, stream);
