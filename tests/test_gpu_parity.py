@@ -199,6 +199,23 @@ def test_linear_decode_interleaved_rows(shape, m):
         assert_y_close(y, oracle_y(x, wb, packed, alpha, mode), f"decode {shape} M={m} mode {mode}")
 
 
+@pytest.mark.parametrize("shape", [(4100, 4032), (5120, 64), (4096, 1088), (4096, 4096)])
+@pytest.mark.parametrize("m", [1, 2, 3, 4])
+def test_linear_decode_four_wave_rows(shape, m):
+    """Up to 4 tokens on 256..320 groups of 16 rows (four-wave workgroups):
+    ragged and 64-wide final blocks, a single block of d_in, and every token
+    count up to 4.  Every output is compared, starting from a NaN-filled y."""
+    d_out, d_in = shape
+    wb, wf = S.small_pair(d_out, d_in, 0.02, 1e-3, seed=d_in + m)
+    x = S.draw_activations(m, d_in, S.generator(11 * m))
+    wb, wf, x = to_dev(wb, wf, x)
+    for mode in (0, 1):
+        packed, alpha = T.compress(wf, wb, mode)
+        y = torch.full((m, d_out), float("nan"), dtype=torch.bfloat16, device=DEV)
+        T.linear(x, wb, packed, alpha, mode, y=y)
+        assert_y_close(y, oracle_y(x, wb, packed, alpha, mode), f"decode {shape} M={m} mode {mode}")
+
+
 @pytest.mark.parametrize("shape", [(130, 192), (257, 640), (128, 64)])
 @pytest.mark.parametrize("m", [65, 100, 256, 300, 513])
 def test_linear_prefill_ragged(shape, m):
