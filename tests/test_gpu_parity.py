@@ -444,6 +444,24 @@ def test_multi_many_row_groups_full_output(shape, m):
     assert_y_close(y, _multi_ref(x, idt, wb, packs, alphas, mode), f"multi rounds {shape} M={m}")
 
 
+@pytest.mark.parametrize("shape", [(300, 320), (5200, 192)])
+@pytest.mark.parametrize("m", [16, 32, 64])
+def test_multi_every_token_its_own_variant_of_64(shape, m):
+    """The largest variant table (64 entries): every token on a variant of
+    its own, so each 16-token tile holds 16 pairs and the pairs take several
+    batches; 325 row groups take the four-wave workgroups, 19 the eight-wave
+    ones, and 192 ends in a 64-wide block.  Every output is compared,
+    starting from a NaN-filled y."""
+    mode = m % 2
+    wb, packs, alphas = _variants(*shape, 64, seed=40 + m, mode=mode)
+    ids = np.random.default_rng(41 + m).permutation(64)[:m].astype(np.int32)
+    x = S.draw_activations(m, shape[1], S.generator(42 + m)).to(DEV)
+    idt = torch.from_numpy(ids).to(DEV)
+    y = torch.full((m, shape[0]), float("nan"), dtype=torch.bfloat16, device=DEV)
+    T.linear_multi(x, idt, wb, packs, alphas, mode, y=y)
+    assert_y_close(y, _multi_ref(x, idt, wb, packs, alphas, mode), f"multi 64 variants {shape} M={m}")
+
+
 def _pattern_ids(kind, m):
     """Variant-id patterns that exercise how a batch is cut into (16-token
     tile, variant) pairs."""
