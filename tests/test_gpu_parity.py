@@ -216,6 +216,40 @@ def test_linear_decode_four_wave_rows(shape, m):
         assert_y_close(y, oracle_y(x, wb, packed, alpha, mode), f"decode {shape} M={m} mode {mode}")
 
 
+@pytest.mark.parametrize("m", [1, 16, 64])
+def test_linear_decode_longest_rows(m):
+    """d_in = 16777152, the longest row the decode-shaped path (up to 64
+    tokens) accepts: its 32-bit x offsets come within 8 KB of 2^31 at 64
+    tokens (x is 2 GiB), and the weight rows take the contiguous-row form.
+    The first, a middle and the last row against the oracle."""
+    d_out, d_in = 17, 16777152
+    mode = m % 2
+    wb, wf = S.small_pair(d_out, d_in, 0.02, 1e-3, seed=60 + m, device=DEV)
+    packed, alpha = T.compress(wf, wb, mode)
+    del wf
+    x = S.draw_activations(m, d_in, S.generator(61 + m, DEV), DEV)
+    y = T.linear(x, wb, packed, alpha, mode)
+    rows = [0, 9, 16]
+    assert_y_close(y[:, rows], oracle_y(x, wb, packed, alpha, mode, rows=rows),
+                   f"decode d_in={d_in} M={m}")
+
+
+def test_linear_prefill_longest_rows():
+    """d_in = 4194240, the longest row the prefill path (more than 64
+    tokens) accepts: a 256-row weight tile and a 256-token x tile then span
+    2^31 - 32 KB with 32-bit offsets.  300 rows (a full 256-row tile and a
+    ragged one), 65 tokens; sampled rows of both tiles against the oracle."""
+    d_out, d_in, m = 300, 4194240, 65
+    wb, wf = S.small_pair(d_out, d_in, 0.02, 1e-3, seed=62, device=DEV)
+    packed, alpha = T.compress(wf, wb, 0)
+    del wf
+    x = S.draw_activations(m, d_in, S.generator(63, DEV), DEV)
+    y = T.linear(x, wb, packed, alpha, 0)
+    rows = [0, 255, 256, 299]
+    assert_y_close(y[:, rows], oracle_y(x, wb, packed, alpha, 0, rows=rows),
+                   f"prefill d_in={d_in} M={m}")
+
+
 @pytest.mark.parametrize("shape", [(130, 192), (257, 640), (128, 64)])
 @pytest.mark.parametrize("m", [65, 100, 256, 300, 513])
 def test_linear_prefill_ragged(shape, m):
