@@ -496,6 +496,30 @@ def test_multi_every_token_its_own_variant_of_64(shape, m):
     assert_y_close(y, _multi_ref(x, idt, wb, packs, alphas, mode), f"multi 64 variants {shape} M={m}")
 
 
+def test_multi_longest_rows():
+    """A mixed batch at d_in = 16777152, the longest row bitdelta_linear_multi
+    accepts: 64 tokens over 3 variants and base-only tokens, x of 2 GiB.
+    The first, a middle and the last row against the oracle."""
+    d_out, d_in, m = 17, 16777152, 64
+    g = S.generator(64, DEV)
+    wb = S.draw_base(d_out, d_in, 0.02, g, DEV)
+    packs, alphas = [], []
+    for v in range(3):
+        wf = S.draw_finetuned(wb, 2e-4 * (v + 1), g)
+        p, a = T.compress(wf, wb, 1)
+        del wf
+        packs.append(p)
+        alphas.append(a)
+    ids = np.random.default_rng(65).integers(-1, 3, size=m).astype(np.int32)
+    x = S.draw_activations(m, d_in, S.generator(66, DEV), DEV)
+    idt = torch.from_numpy(ids).to(DEV)
+    y = T.linear_multi(x, idt, wb, packs, alphas, 1)
+    rows = torch.as_tensor([0, 9, 16], device=DEV)
+    ref = O.linear_multi(bits16(x), ids, bits16(wb[rows]), [packed_u64(p[rows]) for p in packs],
+                         [a[rows].cpu().numpy() for a in alphas], 1)
+    assert_y_close(y[:, rows], ref, f"multi d_in={d_in} M={m}")
+
+
 def _pattern_ids(kind, m):
     """Variant-id patterns that exercise how a batch is cut into (16-token
     tile, variant) pairs."""
