@@ -1264,8 +1264,29 @@ def measure_ceilings(dev):
     res["bf16_mfma_tflops"] = round(bestm[0], 1)
     res["bf16_mfma_workgroups"] = bestm[1]
     res["bf16_mfma_implied_ghz"] = round(2.4 * bestm[0] / BF16_PEAK_TFLOPS, 3)
+    # The single-variant decode's loads on the 4096 x 4096 projection without
+    # its arithmetic, in six patterns (bitdelta_probe_decode_loads), over 12
+    # matrix copies in turn; microseconds per launch.
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(17)
+    ws = [torch.randn(4096, 4096, generator=gen, device=dev).to(torch.bfloat16) for _ in range(12)]
+    ss = [torch.randint(0, 2 ** 31 - 1, (1 << 19,), generator=gen, device=dev, dtype=torch.int32)
+          for _ in range(12)]
+    xv = torch.randn(4096, generator=gen, device=dev).to(torch.bfloat16)
+    orders = {}
+    for mode, name in enumerate(DECODE_LOAD_PATTERNS):
+        g = capture(lambda mode=mode: [T.probe_decode_loads(ws[c % 12], ss[c % 12], xv, mode, sink)
+                                       for c in range(24)])
+        orders[name] = round(median(time_replays(g, 20)) / 24 * 1e3, 3)
+    res["decode_loads_us"] = orders
+    del ws, ss
     torch.cuda.synchronize()
     return res
+
+
+# bitdelta_probe_decode_loads modes 0..5 (include/bitdelta.h)
+DECODE_LOAD_PATTERNS = ("contiguous", "blocks_consecutive_rows", "blocks_interleaved_rows",
+                        "interleaved_to_lds", "interleaved_with_signs", "ring_loads")
 
 
 # ------------------------------------------------------------------ timing

@@ -435,6 +435,24 @@ int bitdelta_probe_stream_read(const void* src, size_t bytes, int32_t workgroups
                                void* stream);
 int bitdelta_probe_mfma_bf16(int32_t workgroups, int32_t iters, float* sink, void* stream);
 
+/* bitdelta_probe_decode_loads issues the single-variant decode's loads on a
+ * 4096 x 4096 bf16 matrix without its arithmetic, so that the time of the
+ * load pattern alone can be set beside the kernel's: 256 workgroups of 4
+ * waves, 16 rows each, the 128-element blocks of a row round-robin over the
+ * waves, two blocks of loads in flight per wave.  mode 0: contiguous 32 KB
+ * per wave; 1: blocks of 16 consecutive rows x 256 bytes; 2: the same with
+ * the rows interleaved as the decode kernel takes them; 3: mode 2 by buffer
+ * loads to LDS; 4: mode 2 plus each block's sign words; 5: mode 3 plus the
+ * sign words plus 1 KB of x per block.  w: 32 MiB (16-byte aligned),
+ * signs: 2 MiB (4-byte aligned), x: 8 KiB (16-byte aligned), all read only
+ * and all device memory owned by the caller; sink: 1024 bytes of device
+ * memory that a chosen xor of the data would be written to (it never is
+ * for data of real weights; the caller owns it).  Returns
+ * BITDELTA_ERR_NULL, _MODE (mode outside 0..5), _ALIGN, _OVERLAP (sink
+ * inside an input) or _HIP; computes nothing of the method. */
+int bitdelta_probe_decode_loads(const void* w, const void* signs, const void* x, int32_t mode,
+                                uint32_t* sink, void* stream);
+
 /* Human-readable text of a status code (static storage, never NULL). */
 const char* bitdelta_status_string(int status);
 

@@ -30,6 +30,7 @@ from .bitdelta import (  # noqa: F401
     linear_multi,
     monosoup_merge,
     monosoup_workspace_size,
+    probe_decode_loads,
     probe_mfma_bf16,
     probe_stream_read,
     Router,

@@ -66,6 +66,7 @@ EXPORTS = (
     "bitdelta_monosoup_merge",
     "bitdelta_probe_stream_read",
     "bitdelta_probe_mfma_bf16",
+    "bitdelta_probe_decode_loads",
 )
 
 MONOSOUP_MAX_RANK = 32
@@ -152,6 +153,8 @@ def lib() -> ctypes.CDLL:
     L.bitdelta_probe_stream_read.restype = i32
     L.bitdelta_probe_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp]
     L.bitdelta_probe_mfma_bf16.restype = i32
+    L.bitdelta_probe_decode_loads.argtypes = [vp, vp, vp, ctypes.c_int32, vp, vp]
+    L.bitdelta_probe_decode_loads.restype = i32
     _lib = L
     return L
 
@@ -591,3 +594,23 @@ def probe_mfma_bf16(workgroups: int, iters: int, sink: torch.Tensor, stream=None
         st = lib().bitdelta_probe_mfma_bf16(workgroups, iters, _ptr(sink), _stream(stream))
     _check(st, "bitdelta_probe_mfma_bf16")
     return 1048576 * workgroups * iters
+
+
+def probe_decode_loads(w: torch.Tensor, signs: torch.Tensor, x: torch.Tensor, mode: int,
+                       sink: torch.Tensor, stream=None):
+    """The single-variant decode's loads on a 4096 x 4096 bf16 matrix without
+    its arithmetic (mode 0..5, see include/bitdelta.h); w: [4096, 4096] bf16,
+    signs: at least 2 MiB, x: at least 8 KiB, sink: at least 1024 bytes, all
+    contiguous device tensors."""
+    for t in (w, signs, x, sink):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("all arguments must be contiguous device tensors")
+    if w.dtype != torch.bfloat16 or tuple(w.shape) != (4096, 4096):
+        raise ValueError("w must be a [4096, 4096] bf16 tensor")
+    nb = lambda t: t.numel() * t.element_size()
+    if nb(signs) < (1 << 21) or nb(x) < 8192 or nb(sink) < 1024:
+        raise ValueError("signs, x and sink must hold 2 MiB, 8 KiB and 1 KiB")
+    with _on(w.device):
+        st = lib().bitdelta_probe_decode_loads(_ptr(w), _ptr(signs), _ptr(x), mode, _ptr(sink),
+                                               _stream(stream))
+    _check(st, "bitdelta_probe_decode_loads")

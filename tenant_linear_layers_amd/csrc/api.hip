@@ -370,6 +370,22 @@ BD_EXPORT int bitdelta_probe_stream_read(const void* src, size_t bytes, int32_t 
                                          static_cast<hipStream_t>(stream)));
 }
 
+BD_EXPORT int bitdelta_probe_decode_loads(const void* w, const void* signs, const void* x,
+                                          int32_t mode, uint32_t* sink, void* stream) {
+  if (!w || !signs || !x || !sink) return BITDELTA_ERR_NULL;
+  if (mode < 0 || mode > 5) return BITDELTA_ERR_MODE;
+  if (!aligned16(w) || !aligned16(x) || (reinterpret_cast<uintptr_t>(signs) & 3u) ||
+      (reinterpret_cast<uintptr_t>(sink) & 3u))
+    return BITDELTA_ERR_ALIGN;
+  if (overlap(sink, 1024, w, size_t(4096) * 8192) || overlap(sink, 1024, signs, size_t(1) << 21) ||
+      overlap(sink, 1024, x, 8192))
+    return BITDELTA_ERR_OVERLAP;
+  const int dev = check_device();
+  if (dev != BITDELTA_OK) return dev;
+  return status_of(bd::launch_probe_decode_loads(w, signs, x, mode, sink,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 BD_EXPORT int bitdelta_probe_mfma_bf16(int32_t workgroups, int32_t iters, float* sink,
                                        void* stream) {
   if (!sink) return BITDELTA_ERR_NULL;

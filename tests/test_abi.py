@@ -222,6 +222,18 @@ def test_probe_argument_checks():
     assert g(8, 16, vp(0), None) == 1
     assert g(0, 16, vp(B), None) == 2 and g(8, 0, vp(B), None) == 2
     assert g(8, (1 << 24) + 1, vp(B), None) == 2 and g(8, 16, vp(B + 1), None) == 3
+    h = L.bitdelta_probe_decode_loads
+    far = 0x10000000                                        # 32 MiB clear of A..E
+    assert h(vp(0), vp(C), vp(D), 0, vp(B), None) == 1
+    assert h(vp(far), vp(C), vp(D), 0, vp(0), None) == 1
+    assert h(vp(far), vp(C), vp(D), 6, vp(B), None) == 4 and h(vp(far), vp(C), vp(D), -1, vp(B), None) == 4
+    assert h(vp(far + 8), vp(C), vp(D), 0, vp(B), None) == 3
+    assert h(vp(far), vp(C + 2), vp(D), 0, vp(B), None) == 3
+    assert h(vp(far), vp(C), vp(D + 8), 0, vp(B), None) == 3
+    assert h(vp(far), vp(C), vp(D), 0, vp(B + 2), None) == 3
+    assert h(vp(far), vp(C), vp(D), 0, vp(far + 4096), None) == 9   # sink inside w
+    assert h(vp(far), vp(C), vp(D), 0, vp(C + 512), None) == 9      # inside the signs
+    assert h(vp(far), vp(C), vp(D), 0, vp(D + 256), None) == 9      # inside x
 
 
 def test_compress_noalloc_argument_checks():

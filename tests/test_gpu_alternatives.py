@@ -72,3 +72,23 @@ def test_multi_windows_kernel(env, m):
     ref = O.linear_multi(bits16(x), ids, bits16(wb), [packed_u64(p) for p in packs],
                          [a.cpu().numpy() for a in alphas], 1)
     assert_y_close(y, ref, f"windows multi M={m}")
+
+
+def test_probe_decode_loads_every_mode():
+    """The calibration probe of the decode's loads (it computes nothing of the
+    method): every load pattern runs on a 4096 x 4096 matrix, twice, and
+    leaves the sink alone on ordinary data; a wrong shape is refused by the
+    binding before any call."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3)
+    w = torch.randn(4096, 4096, generator=g, device=DEV).to(torch.bfloat16)
+    signs = torch.randint(0, 2 ** 31 - 1, (1 << 19,), generator=g, device=DEV, dtype=torch.int32)
+    x = torch.randn(4096, generator=g, device=DEV).to(torch.bfloat16)
+    sink = torch.zeros(256, dtype=torch.int32, device=DEV)
+    for mode in range(6):
+        for _ in range(2):
+            T.probe_decode_loads(w, signs, x, mode, sink)
+    torch.cuda.synchronize()
+    assert int(sink.abs().sum()) == 0
+    with pytest.raises(ValueError):
+        T.probe_decode_loads(w[:2048], signs, x, 0, sink)
