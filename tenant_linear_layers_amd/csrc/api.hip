@@ -8,6 +8,7 @@
 #include "bitdelta.h"
 #include "common.h"
 #include "internal.h"
+#include "probe.h"
 #include "scale_round.h"
 
 #define BD_EXPORT extern "C" __attribute__((visibility("default")))

@@ -63,8 +63,5 @@ hipError_t launch_monosoup(const uint16_t* const* w_ft, int k, const uint16_t* w
 hipError_t launch_probe_read(const void* src, size_t bytes, int workgroups, uint32_t* sink,
                              hipStream_t stream);
 hipError_t launch_probe_mfma(int workgroups, int iters, float* sink, hipStream_t stream);
-// The single-variant decode's loads on a 4096 x 4096 bf16 matrix, modes 0..5.
-hipError_t launch_probe_decode_loads(const void* w, const void* signs, const void* x, int mode,
-                                     uint32_t* sink, hipStream_t stream);
 
 }  // namespace bd

@@ -4,6 +4,7 @@
 // against these measured ceilings beside the published peaks.
 #include "common.h"
 #include "internal.h"
+#include "probe.h"
 
 namespace bd {
 namespace {
